@@ -1,0 +1,263 @@
+"""Benchmark: prefill tokens/s of the 3:1 linear:sparse SALA layer group at 256K tokens on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+A step is one pass of the hot path over one batch of synthetic input with
+everything already resident in HBM:
+  3 x linear prefill  (B=1, H=32, N=262144, d=128, chunk 128, slope decay)
+  1 x sparse select   (Hq=32, Hkv=2, block 64, top-64 + 1 initial + 2 local)
+  1 x sparse prefill  (attention over the selected blocks)
+all on one stream.  value = 262144 tokens / step time.
+
+The JSON line also carries:
+  roofline      the dominant kernel (block-sparse attention, MFMA-bound):
+                algorithmic flops 4*d*Hq*sum_t |A(t)| per launch / its average
+                duration from HIP events on its stream over the timed steps
+  cpu_baseline  the float64 oracle timed on the host on a bounded sample of the
+                same workload, scaled to tokens/s of the whole group
+  decode        the 1M-context decode step (3 linear decode + select over 16384
+                pooled blocks + attention over 67 blocks, B=4) against HBM peak
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tokens", type=int, default=262144)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def sparse_flops(idx, N, d, G, block=64):
+    """4 * d * sum over query rows of |A(t)|, from the actual selection (host)."""
+    import numpy as np
+    ix = idx.cpu().numpy()
+    B, Hkv, NQB, _ = ix.shape
+    total = 0
+    for i in range(NQB):
+        t0, t1 = i * block, min((i + 1) * block, N)
+        rows = t1 - t0
+        sel = ix[:, :, i, :]
+        valid = (sel >= 0) & (sel <= i)
+        n_full = (valid & (sel < i)).sum(axis=-1)            # blocks wholly before the query block
+        has_diag = (valid & (sel == i)).any(axis=-1)
+        per_bh = n_full * block * rows + has_diag * (rows * (rows + 1) // 2)
+        total += int(per_bh.sum())
+    return 4.0 * d * G * total
+
+
+def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
+    """Time the oracle on a bounded sample of the group and scale to tokens/s."""
+    cores = len(os.sched_getaffinity(0))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, str(cores))
+    import numpy as np
+    import torch
+    from oracle import linear as OL
+    from oracle import sparse as OS
+    torch.set_num_threads(cores)
+
+    N = lin_inputs[0]["q"].shape[2]
+    H = lin_inputs[0]["q"].shape[1]
+    # linear: chunked form on one head over a sample of tokens (cost is linear in tokens)
+    n_lin = 8192
+    x = lin_inputs[0]
+    q = x["q"][0, 0, :n_lin].double().cpu().numpy()
+    k = x["k"][0, 0, :n_lin].double().cpu().numpy()
+    v = x["v"][0, 0, :n_lin].double().cpu().numpy()
+    lam = float(x["decay"][0])
+    t0 = time.perf_counter()
+    OL.linear_attention_chunked(q, k, v, lam, 128)
+    t_lin_tok_head = (time.perf_counter() - t0) / n_lin
+
+    # sparse: rows of query blocks deep in the sequence (67 blocks each), one KV group
+    sq, sk, sv = sp_inputs["q"], sp_inputs["k"], sp_inputs["v"]
+    Hq, Hkv, d = sq.shape[1], sk.shape[1], sq.shape[3]
+    G = Hq // Hkv
+    kbar = OS.pool_blocks(sk[0, 0].double().cpu().numpy(), 64)
+    nb = kbar.shape[0]
+    ix = idx.cpu().numpy()
+    sample_blocks = list(range(nb - 1, max(66, nb - 1 - 8), -1))
+    t0 = time.perf_counter()
+    for i in sample_blocks:  # selection: pooled query, scores against all blocks, top-k
+        qb = sq[0, :G, i * 64:(i + 1) * 64].double().cpu().numpy().reshape(-1, d).mean(axis=0)
+        s = (kbar @ qb) / math.sqrt(d)
+        OS.select_row(s, i, N, 64, 64, 1, 2)
+    t_sel_row = (time.perf_counter() - t0) / len(sample_blocks)
+    kv_k = sk.double().cpu().numpy() if False else None  # (full K/V stay on the GPU; rows gather their blocks)
+    rows = [(0, h, i * 64 + r) for i in sample_blocks[:2] for h in range(2) for r in (0, 31, 63)]
+    kb = {}
+    t0 = time.perf_counter()
+    for (b, h, t) in rows:
+        i = t // 64
+        blocks = [int(j) for j in ix[0, h // G, i] if j >= 0]
+        toks = np.concatenate([np.arange(j * 64, min((j + 1) * 64, N)) for j in blocks])
+        toks = toks[toks <= t]
+        kk = sk[0, h // G, toks].double().cpu().numpy()
+        vv = sv[0, h // G, toks].double().cpu().numpy()
+        logit = (kk @ sq[0, h, t].double().cpu().numpy()) / math.sqrt(d)
+        logit -= logit.max()
+        p = np.exp(logit)
+        (p / p.sum()) @ vv
+    t_att_row = (time.perf_counter() - t0) / len(rows)
+    del kb, kv_k
+    nqb = (N + 63) // 64
+    total = 3 * H * N * t_lin_tok_head + Hkv * nqb * t_sel_row + Hq * N * t_att_row
+    return {"value": N / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 oracle on the host: chunked linear form over {n_lin} tokens of one head "
+                       f"({t_lin_tok_head * 1e6:.2f} us/token/head); selection of {len(sample_blocks)} query blocks "
+                       f"at the end of the 256K context ({t_sel_row * 1e3:.1f} ms/row); restricted softmax for "
+                       f"{len(rows)} query rows of 67 blocks ({t_att_row * 1e3:.2f} ms/row); scaled to 3 linear "
+                       f"layers x 32 heads x N + 2 x 4096 selection rows + 32 x N attention rows")}
+
+
+def bench_decode(torch, sala, I, reps=20):
+    lin, sp = I.workload5_decode("cuda")
+    for x in lin:
+        x["decay"] = x["decay"].cuda()
+        x["o"] = torch.empty_like(x["q"])
+    L = sp["L"]
+    q = sp["q"]
+    q4 = q[:, :, None].contiguous()
+    idx, kp = sala.sparse_select(q4, sp["k_cache"])  # pooled cache built once, outside the timed region
+    ws_sel = torch.empty(sala.workspace_bytes("sparse_select", dtype=1, B=4, Hq=32, Hkv=2, d=128, Nq=1, L=L,
+                                              block=64, topk=64, n_init=1, n_local=2), dtype=torch.uint8,
+                         device="cuda")
+    ws_att = torch.empty(sala.workspace_bytes("sparse_decode", dtype=1, B=4, Hq=32, Hkv=2, L=L, d=128, block=64,
+                                              n_sel=67), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step():
+        for x in lin:
+            sala.linear_decode(x["q"], x["k"], x["v"], x["state"], x["decay"], out=x["o"])
+        sala.sparse_select(q4, None, k_pooled=kp, L=L, idx_out=idx, workspace=ws_sel)
+        sala.sparse_decode(q, sp["k_cache"], sp["v_cache"], idx[:, :, 0], L=L, out=o, workspace=ws_att)
+
+    for _ in range(3):
+        step()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)  # evict L2 and MALL
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        step()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) * 1000.0)
+    times.sort()
+    us = times[len(times) // 2]
+    nbytes = 3 * (2 * 4 * 32 * 128 * 128 * 4) + 4 * 2 * 16384 * 128 * 4 + 4 * 2 * 67 * 64 * 128 * 2 * 2
+    return {"workload": "decode step at L=1048576, B=4: 3 linear decode (H=32, d=128 fp32 state) + select over "
+                        "16384 pooled blocks + attention over 64+1+2 blocks (Hq=32, Hkv=2)",
+            "us_per_step_median": round(us, 2), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+            "timing": "HIP events around the 5 launches, median of 20 reps, 1 GiB write between reps"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hybrid_sparse_linear_amd as sala
+    from hybrid_sparse_linear_amd import inputs as I
+    torch.cuda.set_device(0)
+    N = args.tokens
+    lin, sp = I.workload4_group("cuda", N)
+    for x in lin:
+        x["decay"] = x["decay"].cuda()
+        x["o"] = torch.empty_like(x["q"])
+        x["ws"] = torch.empty(max(1, sala.workspace_bytes("linear_prefill", dtype=1, B=1, H=32, N=N, d=128,
+                                                          chunk=128)), dtype=torch.uint8, device="cuda")
+    Hq, Hkv, d = sp["q"].shape[1], sp["k"].shape[1], sp["q"].shape[3]
+    nqb = (N + 63) // 64
+    idx = torch.empty((1, Hkv, nqb, 67), dtype=torch.int32, device="cuda")
+    kp = torch.empty((1, Hkv, nqb, d), dtype=torch.float32, device="cuda")
+    ws_sel = torch.empty(sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N,
+                                              block=64, topk=64, n_init=1, n_local=2), dtype=torch.uint8,
+                         device="cuda")
+    ws_att = torch.empty(sala.workspace_bytes("sparse_prefill", dtype=1, B=1, Hq=Hq, Hkv=Hkv, N=N, d=d, block=64,
+                                              n_sel=67), dtype=torch.uint8, device="cuda")
+    o_sp = torch.empty_like(sp["q"])
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record=False):
+        for x in lin:
+            sala.linear_prefill(x["q"], x["k"], x["v"], x["decay"], out=x["o"], workspace=x["ws"], want_state=False)
+        sala.sparse_select(sp["q"], sp["k"], k_pooled=kp, idx_out=idx, workspace=ws_sel)
+        if record:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+        sala.sparse_prefill(sp["q"], sp["k"], sp["v"], idx, out=o_sp, workspace=ws_att)
+        if record:
+            e.record(stream)
+            ev.append((s, e))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1000.0 / args.steps
+    att_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
+    flops = sparse_flops(idx, N, d, Hq // Hkv)
+    group_flops = 3 * (32 * N * (2 * 128 * 128 + 4 * 128 * 128)) * 1.0 + flops  # algorithmic (causal) counts
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    out = {
+        "metric": "prefill tokens/s for 3:1 linear:sparse layer group at 256K; % MFMA/HBM peak",
+        "value": round(N / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "SALA 3:1 layer-group prefill, B=1, N=%d: 3 linear layers (H=32, d=128, chunk 128, "
+                               "decay exp(-2^(-(h+1)/4))) + 1 block-sparse layer (Hq=32, Hkv=2, d=128, block 64, "
+                               "top-64 + 1 initial + 2 local)" % N,
+                   "tokens": N, "batch": 1},
+        "group_mfma_frac": round(group_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "roofline": {"kernel": "sparse_attn_bf16 (+ its V^T block staging, <1%)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4)},
+    }
+    if not args.no_decode:
+        del lin
+        torch.cuda.empty_cache()
+        out["decode"] = bench_decode(torch, sala, I)
+    if not args.no_cpu_baseline:
+        lin1 = [I.workload2_linear(0, "cuda", N=8192, workload=4)]
+        out["cpu_baseline"] = cpu_baseline(lin1, sp, idx, args.cpu_sample_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

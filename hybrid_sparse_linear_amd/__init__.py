@@ -1,0 +1,194 @@
+"""libsala Python binding: the SALA hybrid attention layer group on MI355X.
+
+Thin wrappers over the C ABI in ``include/sala.h``.  They check tensor
+shapes, dtypes and devices, allocate outputs and workspaces with torch when
+the caller does not pass them, and call the HIP library on torch's current
+stream.  Every step of the computation runs in the HIP kernels; there is no
+CPU or PyTorch fallback -- a missing ``libsala.so`` raises.
+
+Entry points (same names as the C ABI, without the ``sala_`` prefix):
+  linear_prefill   causal decayed linear attention over a sequence
+  linear_decode    one token of the same recurrence (state updated in place)
+  sparse_select    pooled block scores and top-k block selection
+  sparse_prefill   softmax attention over the selected blocks
+  sparse_decode    one query token against the selected cached blocks
+  layer_group_prefill  three linear layers then one sparse layer, one stream
+"""
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
+
+__all__ = ["linear_prefill", "linear_decode", "sparse_select", "sparse_prefill", "sparse_decode",
+           "layer_group_prefill", "workspace_bytes", "SalaError"]
+
+
+def _code(t):
+    if t.dtype == torch.float32:
+        return SALA_F32
+    if t.dtype == torch.bfloat16:
+        return SALA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0) if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libsala tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("libsala tensors must be contiguous")
+
+
+def _ws(nbytes, ws, like):
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
+def workspace_bytes(op, **kw):
+    """Workspace size in bytes of an entry point for the given arguments."""
+    L = lib()
+    if op == "linear_prefill":
+        return L.sala_linear_prefill_workspace(kw["dtype"], kw["B"], kw["H"], kw["N"], kw["d"], kw["chunk"])
+    if op == "sparse_select":
+        return L.sala_sparse_select_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["d"], kw["Nq"], kw["L"],
+                                              kw["block"], kw["topk"], kw["n_init"], kw["n_local"])
+    if op == "sparse_prefill":
+        return L.sala_sparse_prefill_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["N"], kw["d"],
+                                               kw["block"], kw["n_sel"])
+    if op == "sparse_decode":
+        return L.sala_sparse_decode_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["L"], kw["d"],
+                                              kw["block"], kw["n_sel"])
+    raise ValueError(op)
+
+
+def linear_prefill(q, k, v, decay=None, state=None, *, chunk=None, out=None, state_out=None, workspace=None,
+                   want_state=True):
+    """o, S_out = causal linear attention of q, k, v [B, H, N, d] with per-head decay [H] (fp32).
+
+    state: optional [B, H, d, d] fp32 carried state S[d_k][d_v].  Returns (o, S_out or None).
+    """
+    _dev(q, k, v, decay, state, out, state_out)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    chunk = chunk or (64 if d == 64 else 128)
+    dt = _code(q)
+    o = torch.empty_like(q) if out is None else out
+    so = state_out
+    if so is None and want_state:
+        so = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    nb = lib().sala_linear_prefill_workspace(dt, B, H, N, d, chunk)
+    ws = _ws(nb, workspace, q)
+    call("sala_linear_prefill", dt, B, H, N, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay), _ptr(state),
+         _ptr(so), _ptr(ws), nb, _stream())
+    return o, so
+
+
+def linear_decode(q, k, v, state, decay=None, *, out=None):
+    """One decode token: state [B, H, d, d] fp32 is updated in place; returns o [B, H, d]."""
+    _dev(q, k, v, state, decay, out)
+    B, H, d = q.shape
+    o = torch.empty_like(q) if out is None else out
+    call("sala_linear_decode", _code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay), _ptr(state),
+         _stream())
+    return o
+
+
+def sparse_select(q, k=None, *, k_pooled=None, L=None, block=64, topk=64, n_init=1, n_local=2, idx_out=None,
+                  return_scores=False, workspace=None):
+    """Block selection.  q [B, Hq, Nq, d] with Nq == L (prefill) or Nq == 1 (decode).
+
+    k [B, Hkv, L, d] (pooled into k_pooled), or k=None with k_pooled [B, Hkv, ceil(L/block), d] fp32 given.
+    Returns (idx [B, Hkv, NQB, topk+n_init+n_local] int32, k_pooled[, scores]).
+    """
+    _dev(q, k, k_pooled, idx_out)
+    B, Hq, Nq, d = q.shape
+    if k is not None:
+        Hkv, L = k.shape[1], k.shape[2]
+    else:
+        if k_pooled is None or L is None:
+            raise ValueError("without k, pass k_pooled and L")
+        Hkv = k_pooled.shape[1]
+    NB = (L + block - 1) // block
+    NQB = 1 if (Nq == 1 and L != 1) else NB
+    W = topk + n_init + n_local
+    dt = _code(q)
+    if k_pooled is None:
+        k_pooled = torch.empty((B, Hkv, NB, d), dtype=torch.float32, device=q.device)
+    idx = torch.empty((B, Hkv, NQB, W), dtype=torch.int32, device=q.device) if idx_out is None else idx_out
+    scores = torch.empty((B, Hkv, NQB, NB), dtype=torch.float32, device=q.device) if return_scores else None
+    nb = lib().sala_sparse_select_workspace(dt, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local)
+    if return_scores:
+        nb = max(0, nb - B * Hkv * NQB * NB * 4)
+    ws = _ws(nb, workspace, q)
+    call("sala_sparse_select", dt, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local, _ptr(q), _ptr(k),
+         _ptr(k_pooled), _ptr(idx), _ptr(scores), _ptr(ws), nb, _stream())
+    return (idx, k_pooled, scores) if return_scores else (idx, k_pooled)
+
+
+def sparse_prefill(q, k, v, idx, *, block=64, scale=None, out=None, workspace=None):
+    """Softmax attention of q [B, Hq, N, d] over the blocks listed in idx [B, Hkv, NQB, n_sel]."""
+    _dev(q, k, v, idx, out)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    n_sel = idx.shape[-1]
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _code(q)
+    o = torch.empty_like(q) if out is None else out
+    nb = lib().sala_sparse_prefill_workspace(dt, B, Hq, Hkv, N, d, block, n_sel)
+    ws = _ws(nb, workspace, q)
+    call("sala_sparse_prefill", dt, B, Hq, Hkv, N, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v),
+         _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
+    return o
+
+
+def sparse_decode(q, k_cache, v_cache, idx, *, L=None, block=64, scale=None, out=None, workspace=None):
+    """One query token per head, q [B, Hq, d], against the cached blocks listed in idx [B, Hkv, n_sel]."""
+    _dev(q, k_cache, v_cache, idx, out)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    L = k_cache.shape[2] if L is None else L
+    n_sel = idx.shape[-1]
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _code(q)
+    o = torch.empty_like(q) if out is None else out
+    nb = lib().sala_sparse_decode_workspace(dt, B, Hq, Hkv, L, d, block, n_sel)
+    ws = _ws(nb, workspace, q)
+    call("sala_sparse_decode", dt, B, Hq, Hkv, L, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k_cache),
+         _ptr(v_cache), _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
+    return o
+
+
+def layer_group_prefill(linear_layers, sparse_layer, *, block=64, topk=64, n_init=1, n_local=2, chunk=None):
+    """The 3:1 group: each linear layer {q,k,v,decay}, then select + attend on the sparse layer {q,k,v}.
+
+    Returns ([o_linear...], o_sparse, idx).  All launches go to torch's current stream.
+    """
+    outs = [linear_prefill(x["q"], x["k"], x["v"], x.get("decay"), chunk=chunk, want_state=False)[0]
+            for x in linear_layers]
+    sp = sparse_layer
+    idx, _ = sparse_select(sp["q"], sp["k"], block=block, topk=topk, n_init=n_init, n_local=n_local)
+    o = sparse_prefill(sp["q"], sp["k"], sp["v"], idx, block=block)
+    return outs, o, idx

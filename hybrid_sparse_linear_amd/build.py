@@ -1,0 +1,67 @@
+"""Build libsala.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+    python -m hybrid_sparse_linear_amd.build
+
+Objects go to ``_build/`` at the repository root; the shared library is
+written next to this file as ``libsala.so``.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libsala.so")
+
+SOURCES = [
+    "sala_api.cpp",
+    "linear_prefill.hip",
+    "linear_decode.hip",
+    "sparse_select.hip",
+    "sparse_prefill.hip",
+    "sparse_decode.hip",
+]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Packed fp32 VALU ops stay disabled in all device code.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _compile(src, verbose):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(line for line in (r.stderr or "").splitlines() if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed for {src}:\n{errs}")
+    if verbose and errs.strip():
+        print(errs)
+    return obj
+
+
+def build(verbose=False, jobs=6):
+    """Compile every source and link libsala.so.  Returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

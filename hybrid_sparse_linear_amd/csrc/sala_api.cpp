@@ -1,0 +1,216 @@
+// C ABI of libsala: argument validation and dispatch to the HIP launchers.
+// Every check runs on the host before any HIP call; on failure nothing is
+// enqueued and a negative status is returned with a thread-local message.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/sala.h"
+#include "sala_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p, name)                                                      \
+  do {                                                                            \
+    if (!(p)) return fail(SALA_ERR_INVALID_ARG, "%s must not be NULL", name);     \
+    if (!aligned16(p)) return fail(SALA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name); \
+  } while (0)
+
+#define OPT_PTR(p, name)                                                          \
+  do {                                                                            \
+    if ((p) && !aligned16(p)) return fail(SALA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name); \
+  } while (0)
+
+int check_dtype(int dtype) {
+  if (dtype != SALA_F32 && dtype != SALA_BF16) return fail(SALA_ERR_INVALID_ARG, "dtype %d is not SALA_F32/SALA_BF16", dtype);
+  return SALA_OK;
+}
+
+int check_d(int d) {
+  if (d <= 0) return fail(SALA_ERR_INVALID_ARG, "d = %d must be positive", d);
+  if (d != 64 && d != 128) return fail(SALA_ERR_UNSUPPORTED, "d = %d: this build supports 64 and 128", d);
+  return SALA_OK;
+}
+
+int check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return SALA_OK;
+  if (!ws) return fail(SALA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned16(ws)) return fail(SALA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  if (have < need) return fail(SALA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return SALA_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(SALA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SALA_OK;
+}
+
+int check_sparse_common(int B, int Hq, int Hkv, int block, int topk_or_nsel, const char *what) {
+  REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1, SALA_ERR_INVALID_ARG, "B, Hq, Hkv must be >= 1");
+  REQUIRE(Hq % Hkv == 0, SALA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  REQUIRE(block >= 1, SALA_ERR_INVALID_ARG, "block must be >= 1");
+  REQUIRE(block == 64, SALA_ERR_UNSUPPORTED, "block = %d: this build supports 64", block);
+  REQUIRE(topk_or_nsel >= 0, SALA_ERR_INVALID_ARG, "%s must be >= 0", what);
+  return SALA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sala_status_string(int status) {
+  switch (status) {
+    case SALA_OK: return "SALA_OK";
+    case SALA_ERR_INVALID_ARG: return "SALA_ERR_INVALID_ARG";
+    case SALA_ERR_UNSUPPORTED: return "SALA_ERR_UNSUPPORTED";
+    case SALA_ERR_WORKSPACE: return "SALA_ERR_WORKSPACE";
+    case SALA_ERR_HIP: return "SALA_ERR_HIP";
+    default: return "SALA_ERR_UNKNOWN";
+  }
+}
+
+const char *sala_last_error(void) { return g_err; }
+
+const char *sala_version(void) { return "libsala 0.1 (gfx950)"; }
+
+size_t sala_linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || (chunk != 64 && chunk != 128)) return 0;
+  return sala::linear_prefill_workspace(dtype, B, H, N, d, chunk);
+}
+
+int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk, const void *q, const void *k,
+                        const void *v, void *o, const float *decay, const float *state_in, float *state_out,
+                        void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if ((s = check_d(d))) return s;
+  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: this build supports 64 and 128", chunk);
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(o, "o");
+  OPT_PTR(decay, "decay");
+  OPT_PTR(state_in, "state_in");
+  OPT_PTR(state_out, "state_out");
+  if ((s = check_ws(ws, ws_bytes, sala::linear_prefill_workspace(dtype, B, H, N, d, chunk)))) return s;
+  sala::LinearPrefillArgs a{dtype, B, H, N, d, chunk, q, k, v, o, decay, state_in, state_out, ws};
+  return hip_status(sala::launch_linear_prefill(a, static_cast<hipStream_t>(stream)), "sala_linear_prefill launch");
+}
+
+int sala_linear_decode(int dtype, int B, int H, int d, const void *q, const void *k, const void *v, void *o,
+                       const float *decay, float *state, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(B >= 1 && H >= 1, SALA_ERR_INVALID_ARG, "B, H must be >= 1");
+  if ((s = check_d(d))) return s;
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(state, "state");
+  OPT_PTR(decay, "decay");
+  sala::LinearDecodeArgs a{dtype, B, H, d, q, k, v, o, decay, state};
+  return hip_status(sala::launch_linear_decode(a, static_cast<hipStream_t>(stream)), "sala_linear_decode launch");
+}
+
+size_t sala_sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk,
+                                    int n_init, int n_local) {
+  if (B < 1 || Hkv < 1 || L < 1 || block < 1 || (Nq != 1 && Nq != L)) return 0;
+  return sala::sparse_select_workspace(dtype, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local, false);
+}
+
+int sala_sparse_select(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk, int n_init,
+                       int n_local, const void *q, const void *k, float *k_pooled, int32_t *idx, float *scores,
+                       void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_sparse_common(B, Hq, Hkv, block, topk, "topk"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(L >= 1, SALA_ERR_INVALID_ARG, "L must be >= 1");
+  REQUIRE(Nq == L || Nq == 1, SALA_ERR_UNSUPPORTED, "Nq = %d: supported are Nq == L (prefill) and Nq == 1 (decode)", Nq);
+  REQUIRE(n_init >= 0 && n_local >= 0, SALA_ERR_INVALID_ARG, "n_init and n_local must be >= 0");
+  REQUIRE(topk + n_init + n_local >= 1, SALA_ERR_INVALID_ARG, "topk + n_init + n_local must be >= 1");
+  REQUIRE(topk + n_init + n_local <= 1024, SALA_ERR_UNSUPPORTED, "topk + n_init + n_local must be <= 1024");
+  REQUIRE_PTR(q, "q");
+  OPT_PTR(k, "k");
+  REQUIRE_PTR(k_pooled, "k_pooled");
+  REQUIRE_PTR(idx, "idx");
+  OPT_PTR(scores, "scores");
+  const size_t need = sala::sparse_select_workspace(dtype, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local,
+                                                    scores != nullptr);
+  if ((s = check_ws(ws, ws_bytes, need))) return s;
+  sala::SparseSelectArgs a{dtype, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local, q, k, k_pooled, idx, scores, ws};
+  return hip_status(sala::launch_sparse_select(a, static_cast<hipStream_t>(stream)), "sala_sparse_select launch");
+}
+
+size_t sala_sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel) {
+  if (B < 1 || Hkv < 1 || N < 1 || block != 64 || (d != 64 && d != 128)) return 0;
+  return sala::sparse_prefill_workspace(dtype, B, Hq, Hkv, N, d, block, n_sel);
+}
+
+int sala_sparse_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel, float scale,
+                        const void *q, const void *k, const void *v, const int32_t *idx, void *o, void *ws,
+                        size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_sparse_common(B, Hq, Hkv, block, n_sel, "n_sel"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(N >= 1, SALA_ERR_INVALID_ARG, "N must be >= 1");
+  REQUIRE(n_sel >= 1 && n_sel <= 1024, SALA_ERR_UNSUPPORTED, "n_sel = %d must be in [1, 1024]", n_sel);
+  REQUIRE(scale == scale, SALA_ERR_INVALID_ARG, "scale is NaN");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(idx, "idx");
+  REQUIRE_PTR(o, "o");
+  if ((s = check_ws(ws, ws_bytes, sala::sparse_prefill_workspace(dtype, B, Hq, Hkv, N, d, block, n_sel)))) return s;
+  sala::SparsePrefillArgs a{dtype, B, Hq, Hkv, N, d, block, n_sel, scale, q, k, v, idx, o, ws};
+  return hip_status(sala::launch_sparse_prefill(a, static_cast<hipStream_t>(stream)), "sala_sparse_prefill launch");
+}
+
+size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel) {
+  if (B < 1 || Hkv < 1 || n_sel < 1 || (d != 64 && d != 128)) return 0;
+  return sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel);
+}
+
+int sala_sparse_decode(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel, float scale,
+                       const void *q, const void *k_cache, const void *v_cache, const int32_t *idx, void *o, void *ws,
+                       size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_sparse_common(B, Hq, Hkv, block, n_sel, "n_sel"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(L >= 1, SALA_ERR_INVALID_ARG, "L must be >= 1");
+  REQUIRE(n_sel >= 1 && n_sel <= 1024, SALA_ERR_UNSUPPORTED, "n_sel = %d must be in [1, 1024]", n_sel);
+  REQUIRE(Hq / Hkv <= 32, SALA_ERR_UNSUPPORTED, "decode supports at most 32 query heads per KV head");
+  REQUIRE(scale == scale, SALA_ERR_INVALID_ARG, "scale is NaN");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(v_cache, "v_cache");
+  REQUIRE_PTR(idx, "idx");
+  REQUIRE_PTR(o, "o");
+  if ((s = check_ws(ws, ws_bytes, sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel)))) return s;
+  sala::SparseDecodeArgs a{dtype, B, Hq, Hkv, L, d, block, n_sel, scale, q, k_cache, v_cache, idx, o, ws};
+  return hip_status(sala::launch_sparse_decode(a, static_cast<hipStream_t>(stream)), "sala_sparse_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal interface between the C-ABI layer (sala_api.cpp) and the HIP
+// kernel files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sala {
+
+struct LinearPrefillArgs {
+  int dtype, B, H, N, d, chunk;
+  const void *q, *k, *v;
+  void *o;
+  const float *decay, *state_in;
+  float *state_out;
+  void *ws;
+};
+size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk);
+hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st);
+
+struct LinearDecodeArgs {
+  int dtype, B, H, d;
+  const void *q, *k, *v;
+  void *o;
+  const float *decay;
+  float *state;
+};
+hipError_t launch_linear_decode(const LinearDecodeArgs &a, hipStream_t st);
+
+struct SparseSelectArgs {
+  int dtype, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local;
+  const void *q, *k;
+  float *k_pooled;
+  int32_t *idx;
+  float *scores;  // user buffer or nullptr
+  void *ws;
+};
+size_t sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk,
+                               int n_init, int n_local, bool want_scores);
+hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st);
+
+struct SparsePrefillArgs {
+  int dtype, B, Hq, Hkv, N, d, block, n_sel;
+  float scale;
+  const void *q, *k, *v;
+  const int32_t *idx;
+  void *o;
+  void *ws;
+};
+size_t sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel);
+hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st);
+
+struct SparseDecodeArgs {
+  int dtype, B, Hq, Hkv, L, d, block, n_sel;
+  float scale;
+  const void *q, *k_cache, *v_cache;
+  const int32_t *idx;
+  void *o;
+  void *ws;
+};
+size_t sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel);
+hipError_t launch_sparse_decode(const SparseDecodeArgs &a, hipStream_t st);
+
+}  // namespace sala

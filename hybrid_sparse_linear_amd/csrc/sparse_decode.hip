@@ -1,0 +1,209 @@
+// Sparse-layer decode for gfx950: one query token per (b, hq) at position L-1
+// attends to every cached token (< L) of the blocks listed for its KV head.
+// Same restricted softmax as the prefill (exact attention over a block mask:
+// FlashAttention entry of the fugumt.com related list for arXiv 2607.21752);
+// the KV cache is kept whole (MiniCPM-SALA, gist.science (ja) 技術概要 section 1).
+//
+// Split-K: decode_partial gives each workgroup a few selected blocks of one
+// (b, kv head) and all G query heads of that group (one gathered block feeds
+// G heads), producing (max, sum, unnormalised o) per head in log2 units;
+// decode_combine merges the splits with the usual log-sum-exp rescaling.
+
+#include "sala_common.hpp"
+#include "sala_launch.hpp"
+
+namespace sala {
+namespace {
+
+constexpr int BLK = 64;
+constexpr int MAXG = 32;
+
+template <typename T>
+__device__ __forceinline__ void load_row16(const T *p, float *f) {  // 16 bytes -> floats
+  const u32x4 x = gload16(p);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f[2 * e] = bf16lo(x[e]); f[2 * e + 1] = bf16hi(x[e]); }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(x[e]);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_partial(const T *__restrict__ q, const T *__restrict__ kc,
+                                                      const T *__restrict__ vc, const int32_t *__restrict__ idx,
+                                                      float *__restrict__ part, int Hq, int Hkv, int L, int n_sel,
+                                                      int nsplit, int bps, float scale_log2) {
+  constexpr int KS = D + 4;                         // padded K row (floats)
+  constexpr int EPL = sizeof(T) == 2 ? 8 : 4;       // elements per 16-byte load
+  constexpr int CPR = D / EPL;                      // 16-byte loads per row
+  constexpr int CPL = D / 64;                       // d_v columns per lane
+  __shared__ __attribute__((aligned(16))) float ks[BLK * KS];
+  __shared__ __attribute__((aligned(16))) float vs[BLK * D];
+  __shared__ __attribute__((aligned(16))) float qs[MAXG * D];
+  __shared__ float ps[MAXG][BLK];
+  __shared__ int nvalid_sh;
+
+  const int bkv = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
+  const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int32_t *row = idx + (size_t)bkv * n_sel;
+  if (tid == 0) {
+    int n = 0;
+    while (n < n_sel && row[n] >= 0) ++n;
+    nvalid_sh = n;
+  }
+  for (int x = tid; x < G * D; x += 256) {
+    const int g = x / D, c = x % D;
+    const size_t off = (size_t)(b * Hq + kvh * G + g) * D + c;
+    float f;
+    if constexpr (sizeof(T) == 2) f = bf16_to_f32(reinterpret_cast<const uint16_t *>(q)[off]);
+    else f = q[off];
+    qs[g * D + c] = f * scale_log2;
+  }
+  __syncthreads();
+  const int e0 = sp * bps, e1 = min(nvalid_sh, e0 + bps);
+
+  constexpr int HPW = MAXG / 4;  // heads per wave, upper bound
+  float m_run[HPW], l_run[HPW], oacc[HPW][CPL];
+#pragma unroll
+  for (int a = 0; a < HPW; ++a) {
+    m_run[a] = -INFINITY;
+    l_run[a] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) oacc[a][c] = 0.f;
+  }
+  const T *kbase = kc + (size_t)bkv * L * D;
+  const T *vbase = vc + (size_t)bkv * L * D;
+
+  for (int e = e0; e < e1; ++e) {
+    const int j = row[e];
+    if ((size_t)j * BLK >= (size_t)L) continue;
+    const int cnt = min(BLK, L - j * BLK);
+    __syncthreads();
+    for (int x = tid; x < BLK * CPR; x += 256) {
+      const int r = x / CPR, c = (x % CPR) * EPL;
+      float f[EPL], g2[EPL];
+      if (r < cnt) {
+        load_row16(kbase + ((size_t)j * BLK + r) * D + c, f);
+        load_row16(vbase + ((size_t)j * BLK + r) * D + c, g2);
+      } else {
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) { f[u] = 0.f; g2[u] = 0.f; }
+      }
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) { ks[r * KS + c + u] = f[u]; vs[r * D + c + u] = g2[u]; }
+    }
+    __syncthreads();
+    // logits for this wave's heads (h = w, w+4, ...), lane = key
+#pragma unroll
+    for (int a = 0; a < HPW; ++a) {
+      const int h = w + 4 * a;
+      if (h >= G) break;
+      float s = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; c += 4) {
+        const float4 kk = *reinterpret_cast<const float4 *>(&ks[lane * KS + c]);
+        const float4 qq = *reinterpret_cast<const float4 *>(&qs[h * D + c]);
+        s = fmaf(kk.x, qq.x, s);
+        s = fmaf(kk.y, qq.y, s);
+        s = fmaf(kk.z, qq.z, s);
+        s = fmaf(kk.w, qq.w, s);
+      }
+      if (lane >= cnt) s = -INFINITY;
+      const float bm = wave_max(s);
+      const float mnew = fmaxf(m_run[a], bm);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[a] - mnew);
+      const float p = __builtin_amdgcn_exp2f(s - mnew);
+      l_run[a] = l_run[a] * alpha + wave_sum(p);
+      m_run[a] = mnew;
+      ps[h][lane] = p;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) oacc[a][c] *= alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < HPW; ++a) {
+      const int h = w + 4 * a;
+      if (h >= G) break;
+      for (int kk = 0; kk < cnt; ++kk) {
+        const float p = ps[h][kk];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) oacc[a][c] = fmaf(p, vs[kk * D + CPL * lane + c], oacc[a][c]);
+      }
+    }
+  }
+  // partials: [b*Hq + hq][split][D + 2] = (o..., m, l)
+#pragma unroll
+  for (int a = 0; a < HPW; ++a) {
+    const int h = w + 4 * a;
+    if (h >= G) break;
+    float *dst = part + ((size_t)(b * Hq + kvh * G + h) * nsplit + sp) * (D + 2);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dst[CPL * lane + c] = oacc[a][c];
+    if (lane == 0) { dst[D] = m_run[a]; dst[D + 1] = l_run[a]; }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_combine(const float *__restrict__ part, T *__restrict__ o, int nsplit) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const float *p = part + (size_t)bh * nsplit * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[(size_t)s * (D + 2) + D]);
+  float lsum = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = p[(size_t)s * (D + 2) + D];
+      if (ms == -INFINITY) continue;
+      const float wgt = __builtin_amdgcn_exp2f(ms - M);
+      lsum = fmaf(p[(size_t)s * (D + 2) + D + 1], wgt, lsum);
+      acc = fmaf(p[(size_t)s * (D + 2) + c], wgt, acc);
+    }
+  }
+  const float r = (lsum > 0.f) ? acc / lsum : 0.f;
+  if constexpr (sizeof(T) == 2) reinterpret_cast<uint16_t *>(o)[(size_t)bh * D + c] = f32_to_bf16(r);
+  else o[(size_t)bh * D + c] = r;
+}
+
+void split_plan(int BHkv, int n_sel, int *nsplit, int *bps) {
+  int want = (512 + BHkv - 1) / BHkv;
+  if (want > n_sel) want = n_sel;
+  if (want < 1) want = 1;
+  *bps = (n_sel + want - 1) / want;
+  *nsplit = (n_sel + *bps - 1) / *bps;
+}
+
+template <typename T, int D>
+void run(const SparseDecodeArgs &a, hipStream_t st) {
+  int nsplit, bps;
+  split_plan(a.B * a.Hkv, a.n_sel, &nsplit, &bps);
+  float *part = static_cast<float *>(a.ws);
+  hipLaunchKernelGGL((decode_partial<T, D>), dim3(a.B * a.Hkv * nsplit), dim3(256), 0, st, (const T *)a.q,
+                     (const T *)a.k_cache, (const T *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L, a.n_sel, nsplit, bps,
+                     a.scale * 1.4426950408889634f);
+  hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(D), 0, st, part, (T *)a.o, nsplit);
+}
+
+}  // namespace
+
+size_t sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel) {
+  (void)dtype; (void)L; (void)block;
+  int nsplit, bps;
+  split_plan(B * Hkv, n_sel, &nsplit, &bps);
+  return (size_t)B * Hq * nsplit * (d + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_decode(const SparseDecodeArgs &a, hipStream_t st) {
+  if (a.dtype == 1) {
+    if (a.d == 128) run<uint16_t, 128>(a, st);
+    else run<uint16_t, 64>(a, st);
+  } else {
+    if (a.d == 128) run<float, 128>(a, st);
+    else run<float, 64>(a, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sala

@@ -1,0 +1,372 @@
+// Block selection for the InfLLM-V2-style sparse layer (gfx950).
+//
+// The sparse layers add no parameters and reach the whole context while the
+// full KV cache is kept (MiniCPM-SALA, gist.science (ja) 技術概要 sections 1
+// and 2.1; gist.science (de) section 2, "Architektur-Hybridisierung"); block
+// selection of this family scores coarse block representations (PHSA
+// abstract, fugumt.com, arXiv 2601.02819).  Reading implemented here:
+//   kbar_j = mean of block j's keys;  qbar_i = mean over the GQA group's query
+//   heads and the tokens of query block i;  score = qbar_i . kbar_j / sqrt(d);
+//   chosen = forced {0..n_init-1} U {i-n_local+1..i}  U  top-k of the complete
+//   blocks strictly between (ties -> smaller index), ascending, -1 padded.
+//
+// Kernels:
+//   pool_rows       block means of K (fp32 out) and group/block means of Q
+//   score_tiles     prefill scores: 64x64 fp32 tiles of Qbar Kbar^T, lower triangle only
+//   score_decode    decode scores: one pooled query against every pooled key block
+//   select_rows     per row: 4-pass radix select of the k-th largest fp32 key,
+//                   index-ordered tie break, then the ascending write-out
+
+#include "sala_common.hpp"
+#include "sala_launch.hpp"
+
+namespace sala {
+namespace {
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {  // bf16
+  static constexpr int PER16 = 8;
+  __device__ static void unpack(const u32x4 &x, float *f) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) { f[2 * p] = bf16lo(x[p]); f[2 * p + 1] = bf16hi(x[p]); }
+  }
+};
+template <>
+struct Elem<float> {
+  static constexpr int PER16 = 4;
+  __device__ static void unpack(const u32x4 &x, float *f) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f[p] = __uint_as_float(x[p]);
+  }
+};
+
+// Mean of `nrows` rows of length d; row r lives at src(r).  256 threads.
+// Writes the fp32 mean to dst[0..d).
+template <typename T, typename RowPtr>
+__device__ void mean_rows(RowPtr src, int nrows, int d, float *dst, float *red /* 256*8 floats */) {
+  constexpr int E = Elem<T>::PER16;
+  const int cpr = d / E;  // 16-byte chunks per row
+  const int slots = 256 / cpr;
+  const int tid = threadIdx.x, c = tid % cpr, r0 = tid / cpr;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int r = r0; r < nrows; r += slots) {
+    float f[E];
+    Elem<T>::unpack(gload16(src(r) + c * E), f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += f[e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[r0 * d + c * E + e] = acc[e];
+  __syncthreads();
+  if (tid < d) {
+    float s = 0.f;
+    for (int r = 0; r < slots; ++r) s += red[r * d + tid];
+    dst[tid] = s / (float)nrows;
+  }
+}
+
+// grid.x = B*Hkv*NBk (key blocks, when k != null) + B*Hkv*NQB (query blocks, prefill)
+template <typename T>
+__global__ __launch_bounds__(256) void pool_rows(const T *__restrict__ q, const T *__restrict__ k,
+                                                 float *__restrict__ kbar, float *__restrict__ qbar, int Hq,
+                                                 int Hkv, int Nq, int L, int d, int block, int n_kblocks_total,
+                                                 int NBk, int NQB) {
+  __shared__ float red[256 * 8];
+  const int bid = blockIdx.x;
+  if (bid < n_kblocks_total) {
+    const int bh = bid / NBk, j = bid % NBk;
+    const int cnt = min(block, L - j * block);
+    const T *base = k + ((size_t)bh * L + (size_t)j * block) * d;
+    mean_rows<T>([&](int r) { return base + (size_t)r * d; }, cnt, d, kbar + ((size_t)bh * NBk + j) * d, red);
+  } else {
+    const int id = bid - n_kblocks_total;
+    const int bh = id / NQB, i = id % NQB;  // bh = b*Hkv + h
+    const int b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv;
+    const int cnt = min(block, Nq - i * block);
+    const T *base = q + ((size_t)(b * Hq + h * G) * Nq + (size_t)i * block) * d;
+    mean_rows<T>([&](int r) { return base + ((size_t)(r / cnt) * Nq + (r % cnt)) * d; }, G * cnt, d,
+                 qbar + ((size_t)bh * NQB + i) * d, red);
+  }
+}
+
+// scores[bh][i][j] = (qbar_i . kbar_j) * inv_sqrt_d for the 64x64 tiles with J <= I.
+__global__ __launch_bounds__(256) void score_tiles(const float *__restrict__ qbar, const float *__restrict__ kbar,
+                                                   float *__restrict__ scores, int NQB, int NB, int d,
+                                                   float inv_sqrt_d) {
+  __shared__ float qs[64][129];
+  __shared__ float ks[64][129];
+  const int T = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  int I = (int)((sqrtf(8.f * (float)T + 1.f) - 1.f) * 0.5f);
+  while ((I + 1) * (I + 2) / 2 <= T) ++I;
+  while (I * (I + 1) / 2 > T) --I;
+  const int J = T - I * (I + 1) / 2;
+  const float *qb = qbar + ((size_t)bh * NQB + 64 * I) * d;
+  const float *kb = kbar + ((size_t)bh * NB + 64 * J) * d;
+  for (int e = tid; e < 64 * d; e += 256) {
+    const int r = e / d, c = e % d;
+    qs[r][c] = (64 * I + r < NQB) ? qb[(size_t)r * d + c] : 0.f;
+    ks[r][c] = (64 * J + r < NB) ? kb[(size_t)r * d + c] : 0.f;
+  }
+  __syncthreads();
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  for (int kk = 0; kk < d; ++kk) {
+    float a[4], bb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = qs[ty + 16 * r][kk];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bb[c] = ks[tx + 16 * c][kk];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], bb[c], acc[r][c]);
+  }
+  float *out = scores + (size_t)bh * NQB * NB;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 64 * I + ty + 16 * r;
+    if (i >= NQB) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 64 * J + tx + 16 * c;
+      if (j < NB) out[(size_t)i * NB + j] = acc[r][c] * inv_sqrt_d;
+    }
+  }
+}
+
+// Decode: qbar = mean of the G query heads of KV head h; scores for 256 key
+// blocks per workgroup.  8 lanes per key block, 128-byte coalesced reads.
+template <typename T>
+__global__ __launch_bounds__(256) void score_decode(const T *__restrict__ q, const float *__restrict__ kbar,
+                                                    float *__restrict__ scores, int Hq, int Hkv, int NB, int d,
+                                                    float inv_sqrt_d) {
+  __shared__ float qm[128];
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv, tid = threadIdx.x;
+  if (tid < d) {
+    float s = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const size_t off = ((size_t)(b * Hq + h * G + g)) * d + tid;
+      if constexpr (sizeof(T) == 2) s += bf16_to_f32(q[off]);
+      else s += q[off];
+    }
+    qm[tid] = s / (float)G;
+  }
+  __syncthreads();
+  const int grp = tid >> 3, l8 = tid & 7;
+  const int nv = d / 32;  // float4 pieces per lane
+  float qr[16];
+  for (int vv = 0; vv < nv; ++vv)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qr[4 * vv + e] = qm[32 * vv + 4 * l8 + e];
+  const float *kb = kbar + (size_t)bh * NB * d;
+  for (int u = 0; u < 8; ++u) {
+    const int j = blockIdx.x * 256 + grp + 32 * u;
+    float acc = 0.f;
+    if (j < NB) {
+      for (int vv = 0; vv < nv; ++vv) {
+        const float4 x = *reinterpret_cast<const float4 *>(kb + (size_t)j * d + 32 * vv + 4 * l8);
+        acc = fmaf(x.x, qr[4 * vv], acc);
+        acc = fmaf(x.y, qr[4 * vv + 1], acc);
+        acc = fmaf(x.z, qr[4 * vv + 2], acc);
+        acc = fmaf(x.w, qr[4 * vv + 3], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    if (l8 == 0 && j < NB) scores[(size_t)bh * NB + j] = acc * inv_sqrt_d;
+  }
+}
+
+template <int NT>
+__device__ int block_excl_scan(int v, int *tmp, int &total) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) { const int t = tmp[w]; tmp[w] = run; run += t; }
+    tmp[NW] = run;
+  }
+  __syncthreads();
+  const int res = x - v + tmp[wid];
+  total = tmp[NW];
+  __syncthreads();
+  return res;
+}
+
+// One workgroup per selection row.  rows_per_bh = NQB (prefill) or 1 (decode).
+template <int NT, int MAXC>
+__global__ __launch_bounds__(NT) void select_rows(const float *__restrict__ scores, int32_t *__restrict__ idx,
+                                                  int rows_per_bh, int NB, int L, int block, int topk,
+                                                  int n_init, int n_local, int fixed_i) {
+  __shared__ uint32_t keys[MAXC];
+  __shared__ int hist[256];
+  __shared__ int tmp[NT / 64 + 1];
+  __shared__ uint32_t sh_digit;
+  __shared__ int sh_above;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;  // bh * rows_per_bh + r
+  const int bh = row / rows_per_bh, r = row % rows_per_bh;
+  const int i = (fixed_i >= 0) ? fixed_i : r;
+  const int width = topk + n_init + n_local;
+  const float *srow = scores + ((size_t)bh * rows_per_bh + r) * NB;
+  int32_t *out = idx + (size_t)row * width;
+
+  const int nfull = L / block;
+  const int lo = n_init;
+  const int hi = min(i - n_local, nfull - 1);
+  const int ncand = max(0, hi - lo + 1);
+  const int kk = min(topk, ncand);
+  const bool in_lds = ncand <= MAXC;
+
+  auto key_at = [&](int jj) -> uint32_t { return in_lds ? keys[jj] : float_key(srow[lo + jj]); };
+
+  uint32_t thr = 0;  // the kk-th largest key
+  int rem = 0;       // how many keys equal to thr are taken
+  const bool take_all = (kk == ncand);
+  if (!take_all && kk > 0) {
+    if (in_lds)
+      for (int jj = tid; jj < ncand; jj += NT) keys[jj] = float_key(srow[lo + jj]);
+    uint32_t prefix = 0, pmask = 0;
+    rem = kk;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int bb = tid; bb < 256; bb += NT) hist[bb] = 0;
+      __syncthreads();
+      for (int jj = tid; jj < ncand; jj += NT) {
+        const uint32_t key = key_at(jj);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane owns bins 255-4*lane .. 252-4*lane (descending digit order)
+        int c[4], s = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { c[e] = hist[255 - 4 * tid - e]; s += c[e]; }
+        int incl = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (tid >= o) incl += y;
+        }
+        int above = incl - s;  // keys with a larger digit (in lanes before this one)
+        if (above < rem && rem <= incl) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (above < rem && rem <= above + c[e]) { sh_digit = 255u - 4u * tid - e; sh_above = above; }
+            above += c[e];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= sh_digit << shift;
+      pmask |= 255u << shift;
+      rem -= sh_above;
+      __syncthreads();
+    }
+    thr = prefix;
+  }
+
+  // positions: [forced low][picks ascending][forced high][-1 ...]
+  const int nlow = min(n_init, i + 1);
+  const int hstart = max(n_init, i - n_local + 1);
+  const int nhigh = max(0, i - hstart + 1);
+  const int per = (ncand + NT - 1) / NT;
+  const int j0 = tid * per, j1 = min(ncand, j0 + per);
+  int total;
+  if (take_all) {
+    for (int jj = j0; jj < j1; ++jj) out[nlow + jj] = lo + jj;
+  } else if (kk > 0) {
+    int neq = 0;
+    for (int jj = j0; jj < j1; ++jj) neq += (key_at(jj) == thr);
+    const int eq_before = block_excl_scan<NT>(neq, tmp, total);
+    int npk = 0, e = eq_before;
+    for (int jj = j0; jj < j1; ++jj) {
+      const uint32_t key = key_at(jj);
+      if (key > thr) ++npk;
+      else if (key == thr) { if (e < rem) ++npk; ++e; }
+    }
+    const int pk_before = block_excl_scan<NT>(npk, tmp, total);
+    int pos = nlow + pk_before;
+    e = eq_before;
+    for (int jj = j0; jj < j1; ++jj) {
+      const uint32_t key = key_at(jj);
+      bool take = key > thr;
+      if (key == thr) { take = e < rem; ++e; }
+      if (take) out[pos++] = lo + jj;
+    }
+  }
+  for (int t = tid; t < width; t += NT) {
+    if (t < nlow) out[t] = t;
+    else if (t >= nlow + kk && t < nlow + kk + nhigh) out[t] = hstart + (t - nlow - kk);
+    else if (t >= nlow + kk + nhigh) out[t] = -1;
+  }
+}
+
+}  // namespace
+
+size_t sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk,
+                               int n_init, int n_local, bool want_scores) {
+  (void)dtype; (void)Hq; (void)topk; (void)n_init; (void)n_local;
+  const size_t NB = (size_t)(L + block - 1) / block;
+  const size_t NQB = (Nq == 1) ? 1 : (size_t)(Nq + block - 1) / block;
+  size_t bytes = 0;
+  if (Nq != 1) bytes += (size_t)B * Hkv * NQB * d * sizeof(float);             // qbar
+  if (!want_scores) bytes += (size_t)B * Hkv * NQB * NB * sizeof(float);       // scores
+  return bytes;
+}
+
+hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
+  const int NB = (a.L + a.block - 1) / a.block;
+  const bool decode = (a.Nq == 1);
+  const int NQB = decode ? 1 : (a.Nq + a.block - 1) / a.block;
+  const int BH = a.B * a.Hkv;
+  char *ws = static_cast<char *>(a.ws);
+  float *qbar = nullptr;
+  if (!decode) { qbar = reinterpret_cast<float *>(ws); ws += (size_t)BH * NQB * a.d * sizeof(float); }
+  float *scores = a.scores ? a.scores : reinterpret_cast<float *>(ws);
+  const float inv_sqrt_d = 1.0f / sqrtf((float)a.d);
+
+  const int nk = a.k ? BH * NB : 0;
+  const int nq = decode ? 0 : BH * NQB;
+  if (nk + nq > 0) {
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(pool_rows<uint16_t>, dim3(nk + nq), dim3(256), 0, st, (const uint16_t *)a.q,
+                         (const uint16_t *)a.k, a.k_pooled, qbar, a.Hq, a.Hkv, a.Nq, a.L, a.d, a.block, nk, NB,
+                         NQB);
+    else
+      hipLaunchKernelGGL(pool_rows<float>, dim3(nk + nq), dim3(256), 0, st, (const float *)a.q,
+                         (const float *)a.k, a.k_pooled, qbar, a.Hq, a.Hkv, a.Nq, a.L, a.d, a.block, nk, NB, NQB);
+  }
+  if (!decode) {
+    const int nT = (NQB + 63) / 64;
+    hipLaunchKernelGGL(score_tiles, dim3(nT * (nT + 1) / 2, BH), dim3(256), 0, st, qbar, a.k_pooled, scores, NQB,
+                       NB, a.d, inv_sqrt_d);
+    hipLaunchKernelGGL((select_rows<256, 8192>), dim3(BH * NQB), dim3(256), 0, st, scores, a.idx, NQB, NB, a.L,
+                       a.block, a.topk, a.n_init, a.n_local, -1);
+  } else {
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(score_decode<uint16_t>, dim3((NB + 255) / 256, BH), dim3(256), 0, st,
+                         (const uint16_t *)a.q, a.k_pooled, scores, a.Hq, a.Hkv, NB, a.d, inv_sqrt_d);
+    else
+      hipLaunchKernelGGL(score_decode<float>, dim3((NB + 255) / 256, BH), dim3(256), 0, st, (const float *)a.q,
+                         a.k_pooled, scores, a.Hq, a.Hkv, NB, a.d, inv_sqrt_d);
+    hipLaunchKernelGGL((select_rows<1024, 16384>), dim3(BH), dim3(1024), 0, st, scores, a.idx, 1, NB, a.L,
+                       a.block, a.topk, a.n_init, a.n_local, (a.L - 1) / a.block);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sala

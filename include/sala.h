@@ -1,0 +1,191 @@
+/*
+ * sala.h -- C ABI of libsala, the MI355X (gfx950) hot path of the SALA hybrid
+ * attention layer group: three Lightning (causal, decayed linear) attention
+ * layers for every InfLLM-V2-style block-sparse softmax layer.
+ *
+ * Sources for the operations (the pages describing the method):
+ *   "MiniCPM-SALA: Hybridizing Sparse and Linear Attention for Efficient
+ *   Long-Context Modeling" -- abstract (fugumt.com summary of arXiv
+ *   2602.11761); gist.science (ja) technical summary 技術概要 sections 1,
+ *   2.1, 2.2; gist.science (de) technical summary section 2 "Methodik",
+ *   subsection "Architektur-Hybridisierung".  Block selection from coarse
+ *   block representations: "Punctuation-aware Hybrid Trainable Sparse
+ *   Attention for Large Language Models", abstract.  Exact softmax attention
+ *   restricted to a block mask: the FlashAttention entry in the related list
+ *   of the fugumt.com page for arXiv 2607.21752.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, contiguous, row-major.  Q/K/V/O use the layout
+ *     [B, heads, tokens, d] (head-major), so one (head, 64-token block) of K or
+ *     V is one contiguous run.
+ *   - Every pointer argument is a DEVICE pointer (memory from hipMalloc or
+ *     torch on the current device) unless stated otherwise, 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued asynchronously on it; nothing synchronises.
+ *   - The caller owns every buffer, including the workspace `ws`.  libsala
+ *     never allocates or frees device memory and keeps no mutable global
+ *     state, so calls on different streams do not interfere (they must not
+ *     share output or workspace buffers while in flight).
+ *   - Arguments are validated on the host before any HIP call; on error no
+ *     device work is enqueued and a negative sala_status is returned.
+ *     sala_last_error() then returns a thread-local message naming the
+ *     offending argument.  No C++ exception crosses the ABI.
+ *   - Kernel faults surface at the caller's next synchronisation, as usual.
+ */
+#ifndef SALA_H
+#define SALA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SALA_F32 = 0,  /* fp32 inputs/outputs, fp32 arithmetic                      */
+  SALA_BF16 = 1  /* bf16 inputs/outputs, bf16 MFMA with fp32 accumulation     */
+} sala_dtype;
+
+typedef enum {
+  SALA_OK = 0,
+  SALA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or shape     */
+  SALA_ERR_UNSUPPORTED = -2, /* valid request outside what this build covers   */
+  SALA_ERR_WORKSPACE = -3,   /* ws too small (query the *_workspace call)      */
+  SALA_ERR_HIP = -4          /* a HIP launch/runtime call failed               */
+} sala_status;
+
+/* ------------------------------------------------------------------------
+ * sala_linear_prefill -- causal linear attention with per-head decay over a
+ * whole sequence, continuing from an optional carried state.
+ *
+ * Definition (per batch row b and head h, lam = decay[h]):
+ *   o_t   = sum_{s<=t} lam^(t-s) (q_t . k_s) v_s  +  lam^(t+1) q_t S_in
+ *   S_out = lam^N S_in + sum_{s<N} lam^(N-1-s) k_s v_s^T
+ * i.e. (Q K^T masked by the decayed causal mask) V, with no feature map, no
+ * normaliser and no 1/sqrt(d).  The pages give Lightning attention's O(N)
+ * cost through a recursive formulation (gist.science (de) section 2,
+ * "Architektur-Hybridisierung") and its closeness to softmax attention
+ * (gist.science (ja) section 2.1); the decay and the absence of a normaliser
+ * are the plainest reading consistent with both.
+ *
+ *   dtype        SALA_BF16 (MFMA path) or SALA_F32.
+ *   B, H, N, d   batch, heads, tokens (N >= 1), head dim (64 or 128).
+ *   chunk        intra-chunk length of the bf16 path (64 or 128); any value in
+ *                {64, 128} gives the same result up to rounding.
+ *   q, k, v      [B, H, N, d] of dtype.
+ *   o            [B, H, N, d] of dtype (output).
+ *   decay        [H] fp32 in [0, 1], or NULL for lam = 1 on every head.
+ *   state_in     [B, H, d, d] fp32, S[d_k][d_v], or NULL for a zero state.
+ *   state_out    [B, H, d, d] fp32 or NULL; may alias state_in.
+ *   ws, ws_bytes workspace of at least sala_linear_prefill_workspace(...)
+ *                bytes (may be NULL when that is 0).
+ * ------------------------------------------------------------------------ */
+int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk,
+                        const void *q, const void *k, const void *v, void *o,
+                        const float *decay, const float *state_in, float *state_out,
+                        void *ws, size_t ws_bytes, void *stream);
+
+size_t sala_linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk);
+
+/* ------------------------------------------------------------------------
+ * sala_linear_decode -- one token of the same recurrence:
+ *   S <- lam S + k v^T ;  o = q S        (state updated in place)
+ *
+ *   q, k, v   [B, H, d] of dtype (one token per (b, h)).
+ *   o         [B, H, d] of dtype (output).
+ *   decay     [H] fp32 or NULL (= 1).
+ *   state     [B, H, d, d] fp32, read and overwritten.
+ * ------------------------------------------------------------------------ */
+int sala_linear_decode(int dtype, int B, int H, int d,
+                       const void *q, const void *k, const void *v, void *o,
+                       const float *decay, float *state, void *stream);
+
+/* ------------------------------------------------------------------------
+ * sala_sparse_select -- block selection for the sparse layer.
+ *
+ * The sparse layers use InfLLM-V2, which adds no parameters and reaches the
+ * whole context while keeping the full KV cache (gist.science (ja) sections
+ * 1 and 2.1; gist.science (de) section 2); selection in this family scores
+ * coarse block representations (PHSA abstract).  Reading used here:
+ *   kbar_j = mean of the keys of block j (the valid ones, for a partial block)
+ *   qbar_i = mean over the G = Hq/Hkv query heads of a KV head and over the
+ *            query tokens of query block i (decode: the single query token)
+ *   score  = qbar_i . kbar_j / sqrt(d), computed in fp32
+ *   forced = blocks 0..n_init-1 and i-n_local+1..i (clipped to [0, i])
+ *   cands  = complete blocks j with n_init <= j <= i-n_local
+ *   chosen = forced U top-min(topk, |cands|) cands by score (exact fp32 ties
+ *            go to the smaller j), written ascending, padded with -1.
+ *
+ *   Nq, L        queries sit at positions L-Nq .. L-1.  Supported: Nq == L
+ *                (prefill: NQB = ceil(L/block) query blocks) and Nq == 1
+ *                (decode: NQB = 1, query block i = (L-1)/block).
+ *   block        64.   topk >= 0, n_init >= 0, n_local >= 0.
+ *   q            [B, Hq, Nq, d] of dtype.
+ *   k            [B, Hkv, L, d] of dtype, or NULL: then k_pooled must already
+ *                hold the block means (decode against a pooled cache).
+ *   k_pooled     [B, Hkv, ceil(L/block), d] fp32; written when k != NULL.
+ *   idx          [B, Hkv, NQB, topk + n_init + n_local] int32 (output).
+ *   scores       optional [B, Hkv, NQB, ceil(L/block)] fp32 (output, entry
+ *                (i, j) meaningful only for candidates j of row i), or NULL.
+ *   ws, ws_bytes at least sala_sparse_select_workspace(...) bytes.
+ * ------------------------------------------------------------------------ */
+int sala_sparse_select(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L,
+                       int block, int topk, int n_init, int n_local,
+                       const void *q, const void *k, float *k_pooled, int32_t *idx,
+                       float *scores, void *ws, size_t ws_bytes, void *stream);
+
+size_t sala_sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L,
+                                    int block, int topk, int n_init, int n_local);
+
+/* ------------------------------------------------------------------------
+ * sala_sparse_prefill -- softmax attention restricted to the selected blocks
+ * (block-sparse exact attention, the FlashAttention related-list entry).
+ *
+ * For query head hq (KV head hq / G) and token t in query block i:
+ *   A(t) = { s in the blocks listed in idx[b, hq/G, i] : s <= t }
+ *   o_t  = sum_{s in A(t)} softmax_s(scale * q_t . k_s) v_s
+ * idx rows list distinct blocks; the list ends at the first negative entry;
+ * entries greater than i contribute nothing (they are skipped).  Every row
+ * must contain its own block i (the forced local block does).
+ *
+ *   block        64.   n_sel = idx row length (topk + n_init + n_local).
+ *   scale        usually 1/sqrt(d).
+ *   q, o         [B, Hq, N, d];  k, v  [B, Hkv, N, d];  idx [B, Hkv, NQB, n_sel].
+ *   ws, ws_bytes at least sala_sparse_prefill_workspace(...) bytes.
+ * ------------------------------------------------------------------------ */
+int sala_sparse_prefill(int dtype, int B, int Hq, int Hkv, int N, int d,
+                        int block, int n_sel, float scale,
+                        const void *q, const void *k, const void *v, const int32_t *idx,
+                        void *o, void *ws, size_t ws_bytes, void *stream);
+
+size_t sala_sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d,
+                                     int block, int n_sel);
+
+/* ------------------------------------------------------------------------
+ * sala_sparse_decode -- one query token per (b, hq) at position L-1 attends
+ * to every cached token (< L) of the blocks listed in idx[b, hq/G].
+ *
+ *   q            [B, Hq, d];  k_cache, v_cache [B, Hkv, L, d];
+ *   idx          [B, Hkv, n_sel] int32 (distinct, ends at the first negative);
+ *   o            [B, Hq, d] (output).
+ *   ws, ws_bytes at least sala_sparse_decode_workspace(...) bytes.
+ * ------------------------------------------------------------------------ */
+int sala_sparse_decode(int dtype, int B, int Hq, int Hkv, int L, int d,
+                       int block, int n_sel, float scale,
+                       const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *idx, void *o, void *ws, size_t ws_bytes, void *stream);
+
+size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d,
+                                    int block, int n_sel);
+
+/* ------------------------------------------------------------------------ */
+const char *sala_status_string(int status);  /* static string, never NULL      */
+const char *sala_last_error(void);           /* thread-local detail, never NULL */
+const char *sala_version(void);              /* build identification           */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SALA_H */

@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sala.h declares, and rejects bad arguments on the host (before any
+HIP call) with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_sparse_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsala.so not built")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+F32, BF16 = 0, 1
+P = ctypes.c_void_p
+A = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
+MIS = ctypes.c_void_p(0x10004)
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sala_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"sala_linear_prefill", "sala_linear_decode", "sala_sparse_select", "sala_sparse_prefill",
+            "sala_sparse_decode"} <= names
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(handle, n), n
+
+
+def test_status_strings_and_version():
+    L = _lib.lib()
+    for code, name in _lib.STATUS.items():
+        assert L.sala_status_string(code).decode() == name
+    assert L.sala_status_string(-99).decode() == "SALA_ERR_UNKNOWN"
+    assert b"gfx950" in L.sala_version()
+
+
+def lp(**kw):
+    a = dict(dtype=BF16, B=1, H=2, N=256, d=128, chunk=128, q=A, k=A, v=A, o=A, decay=NUL, sin=NUL, sout=NUL,
+             ws=NUL, wsb=0)
+    a.update(kw)
+    return _lib.lib().sala_linear_prefill(a["dtype"], a["B"], a["H"], a["N"], a["d"], a["chunk"], a["q"], a["k"],
+                                          a["v"], a["o"], a["decay"], a["sin"], a["sout"], a["ws"], a["wsb"], NUL)
+
+
+def test_linear_prefill_validation():
+    assert lp(dtype=7) == INVALID
+    assert lp(N=0) == INVALID
+    assert lp(B=0) == INVALID
+    assert lp(d=96) == UNSUPPORTED
+    assert lp(chunk=32) == UNSUPPORTED
+    assert lp(q=NUL) == INVALID
+    assert lp(o=MIS) == INVALID
+    assert lp(sin=MIS) == INVALID
+    assert lp(q=NUL) == INVALID and b"q must not be NULL" in _lib.lib().sala_last_error()
+
+
+def test_linear_prefill_workspace_rules():
+    L = _lib.lib()
+    need = L.sala_linear_prefill_workspace(BF16, 1, 32, 32768, 128, 128)
+    assert need > 0 and need % (128 * 128 * 4) == 0
+    assert L.sala_linear_prefill_workspace(F32, 1, 32, 32768, 128, 128) == 0
+    assert lp(B=1, H=32, N=32768, ws=NUL, wsb=0) == WORKSPACE
+    assert lp(B=1, H=32, N=32768, ws=A, wsb=need - 1) == WORKSPACE
+    assert L.sala_linear_prefill_workspace(BF16, 1, 32, 100, 128, 128) == 0  # one segment: no workspace
+
+
+def test_linear_decode_validation():
+    L = _lib.lib()
+    assert L.sala_linear_decode(BF16, 1, 2, 128, A, A, A, A, NUL, NUL, NUL) == INVALID  # state NULL
+    assert L.sala_linear_decode(BF16, 1, 2, 80, A, A, A, A, NUL, A, NUL) == UNSUPPORTED
+    assert L.sala_linear_decode(3, 1, 2, 128, A, A, A, A, NUL, A, NUL) == INVALID
+
+
+def ss(**kw):
+    a = dict(dtype=BF16, B=1, Hq=4, Hkv=2, d=128, Nq=256, L=256, block=64, topk=4, n_init=1, n_local=2, q=A, k=A,
+             kp=A, idx=A, scores=NUL, ws=NUL, wsb=0)
+    a.update(kw)
+    return _lib.lib().sala_sparse_select(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["Nq"], a["L"], a["block"],
+                                         a["topk"], a["n_init"], a["n_local"], a["q"], a["k"], a["kp"], a["idx"],
+                                         a["scores"], a["ws"], a["wsb"], NUL)
+
+
+def test_sparse_select_validation():
+    assert ss(Hq=3) == INVALID            # Hq not a multiple of Hkv
+    assert ss(block=32) == UNSUPPORTED
+    assert ss(Nq=7) == UNSUPPORTED
+    assert ss(topk=-1) == INVALID
+    assert ss(topk=0, n_init=0, n_local=0) == INVALID
+    assert ss(kp=NUL) == INVALID
+    assert ss(idx=MIS) == INVALID
+    assert ss() == WORKSPACE              # prefill needs qbar + scores workspace
+    L = _lib.lib()
+    need = L.sala_sparse_select_workspace(BF16, 1, 4, 2, 128, 256, 256, 64, 4, 1, 2)
+    assert need == 2 * 4 * 128 * 4 + 2 * 4 * 4 * 4
+    assert ss(ws=A, wsb=need - 4) == WORKSPACE
+
+
+def test_sparse_prefill_and_decode_validation():
+    L = _lib.lib()
+    f = L.sala_sparse_prefill
+    assert f(BF16, 1, 4, 2, 256, 128, 64, 7, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == WORKSPACE
+    assert f(BF16, 1, 4, 3, 256, 128, 64, 7, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == INVALID
+    assert f(BF16, 1, 4, 2, 256, 128, 64, 0, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == UNSUPPORTED
+    assert f(BF16, 1, 4, 2, 256, 128, 64, 7, ctypes.c_float(float("nan")), A, A, A, A, A, A, 1 << 30, NUL) == INVALID
+    assert f(F32, 1, 4, 2, 256, 128, 64, 7, ctypes.c_float(0.1), A, NUL, A, A, A, NUL, 0, NUL) == INVALID
+    g = L.sala_sparse_decode
+    assert g(BF16, 1, 128, 2, 4096, 128, 64, 67, ctypes.c_float(0.1), A, A, A, A, A, A, 1 << 30, NUL) == UNSUPPORTED
+    assert g(BF16, 1, 32, 2, 4096, 128, 64, 67, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == WORKSPACE
+    assert L.sala_sparse_decode_workspace(BF16, 4, 32, 2, 1 << 20, 128, 64, 67) > 0
