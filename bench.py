@@ -101,23 +101,21 @@ def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
         s = (kbar @ qb) / math.sqrt(d)
         OS.select_row(s, i, N, 64, 64, 1, 2)
     t_sel_row = (time.perf_counter() - t0) / len(sample_blocks)
-    kv_k = sk.double().cpu().numpy() if False else None  # (full K/V stay on the GPU; rows gather their blocks)
     rows = [(0, h, i * 64 + r) for i in sample_blocks[:2] for h in range(2) for r in (0, 31, 63)]
-    kb = {}
     t0 = time.perf_counter()
     for (b, h, t) in rows:
         i = t // 64
         blocks = [int(j) for j in ix[0, h // G, i] if j >= 0]
         toks = np.concatenate([np.arange(j * 64, min((j + 1) * 64, N)) for j in blocks])
         toks = toks[toks <= t]
-        kk = sk[0, h // G, toks].double().cpu().numpy()
-        vv = sv[0, h // G, toks].double().cpu().numpy()
+        ti = torch.from_numpy(toks).to(sk.device)
+        kk = sk[0, h // G, ti].double().cpu().numpy()
+        vv = sv[0, h // G, ti].double().cpu().numpy()
         logit = (kk @ sq[0, h, t].double().cpu().numpy()) / math.sqrt(d)
         logit -= logit.max()
         p = np.exp(logit)
         (p / p.sum()) @ vv
     t_att_row = (time.perf_counter() - t0) / len(rows)
-    del kb, kv_k
     nqb = (N + 63) // 64
     total = 3 * H * N * t_lin_tok_head + Hkv * nqb * t_sel_row + Hq * N * t_att_row
     return {"value": N / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",

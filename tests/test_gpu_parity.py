@@ -28,13 +28,15 @@ def dev(x):
 # ---------------------------------------------------------------- linear prefill
 
 LIN_CASES = [
-    # B, H, N, d, chunk, dtype, std, with_state
-    (2, 3, 1000, 128, 128, I.BF16, 1.0 / math.sqrt(128), True),    # 8 segments, ragged tail
-    (1, 2, 777, 128, 64, I.BF16, 0.5, True),                      # chunk 64
-    (1, 2, 600, 64, 128, I.BF16, 0.5, False),                     # d 64
-    (1, 3, 333, 64, 64, I.BF16, 0.5, True),
-    (2, 2, 100, 128, 128, I.BF16, 1.0, True),                     # one segment, one partial chunk
-    (1, 4, 2048, 64, 64, I.F32, 1.0 / 8.0, False),                # tiny-group linear shape
+    # B, H, N, d, chunk, dtype, std, with_state.  bf16 cases use the workloads' input scale
+    # (std 1/sqrt(d)): bf16 operand rounding errors scale with the summed terms, which at this
+    # scale keeps the elementwise rule meaningful; the relative-norm check catches structure.
+    (2, 3, 1000, 128, 128, I.BF16, 1.0 / math.sqrt(128), True),   # 8 segments, ragged tail
+    (1, 2, 777, 128, 64, I.BF16, 1.0 / math.sqrt(128), True),     # chunk 64
+    (1, 2, 600, 64, 128, I.BF16, 1.0 / 8.0, False),               # d 64
+    (1, 3, 333, 64, 64, I.BF16, 1.0 / 8.0, True),
+    (2, 2, 100, 128, 128, I.BF16, 1.0 / math.sqrt(128), True),    # one segment, one partial chunk
+    (1, 4, 2048, 64, 64, I.F32, 1.0 / 8.0, False),               # tiny-group linear shape
     (1, 2, 517, 128, 128, I.F32, 0.5, True),
 ]
 
@@ -45,7 +47,7 @@ def test_linear_prefill(case):
     say("linear_prefill", case)
     x = I.linear_inputs(B, H, N, d, dt, 90, N % 97, std)
     decay = torch.tensor(([0.0, 1.0, 0.9, 0.43] * 4)[:H], dtype=torch.float32)
-    s0 = I.normal((B, H, d, d), 77, 0.05) if with_state else None
+    s0 = I.normal((B, H, d, d), 77, 1.0 / d) if with_state else None
     o, st = sala.linear_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(decay), dev(s0), chunk=chunk)
     torch.cuda.synchronize()
     ro, rs = OL.linear_prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), decay.double().numpy(),
@@ -57,8 +59,8 @@ def test_linear_prefill(case):
 def test_linear_prefill_state_alias_and_no_decay():
     say("linear_prefill alias")
     B, H, N, d = 1, 2, 700, 128
-    x = I.linear_inputs(B, H, N, d, I.BF16, 91, 0, 0.3)
-    s0 = I.normal((B, H, d, d), 78, 0.05)
+    x = I.linear_inputs(B, H, N, d, I.BF16, 91, 0, 1.0 / math.sqrt(d))
+    s0 = I.normal((B, H, d, d), 78, 1.0 / d)
     sd = dev(s0.clone())
     o, st = sala.linear_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), None, sd, state_out=sd)
     torch.cuda.synchronize()
@@ -71,7 +73,7 @@ def test_linear_prefill_state_alias_and_no_decay():
 def test_linear_prefill_split_equals_whole_on_gpu():
     say("linear_prefill split")
     B, H, N1, N2, d = 1, 2, 640, 300, 128
-    x = I.linear_inputs(B, H, N1 + N2, d, I.BF16, 92, 0, 0.3)
+    x = I.linear_inputs(B, H, N1 + N2, d, I.BF16, 92, 0, 1.0 / math.sqrt(d))
     decay = dev(torch.tensor([0.97, 0.999]))
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     o1, s1 = sala.linear_prefill(q[:, :, :N1].contiguous(), k[:, :, :N1].contiguous(), v[:, :, :N1].contiguous(), decay)
@@ -104,7 +106,7 @@ def test_linear_decode(dt, d):
 def test_linear_decode_continues_prefill():
     say("linear decode after prefill")
     B, H, N, d = 1, 2, 513, 128
-    x = I.linear_inputs(B, H, N + 1, d, I.BF16, 94, 0, 0.3)
+    x = I.linear_inputs(B, H, N + 1, d, I.BF16, 94, 0, 1.0 / math.sqrt(d))
     decay = dev(torch.tensor([0.95, 1.0]))
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     _, st = sala.linear_prefill(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(), decay)
