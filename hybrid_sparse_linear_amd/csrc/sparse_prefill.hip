@@ -78,16 +78,21 @@ __global__ __launch_bounds__(256) void transpose_v_blocks(const uint16_t *__rest
 
 template <int D>
 struct SpCfg {
-  static constexpr int NDS = D / 32;     // 32-deep feature steps
-  static constexpr int ND = D / 16;      // 16-wide d_v tiles
-  static constexpr int KCH = D / 8;      // chunks per K row
-  static constexpr int TCH = BLK / 8;    // chunks per V^T row (8)
-  static constexpr int KB = BLK * D * 2; // bytes of one K block (== V^T block)
-  static constexpr int PER_T = KB / 16 / 256;  // 16-byte pieces per thread per block
+  static constexpr int NDS = D / 32;        // 32-deep feature steps
+  static constexpr int ND = D / 16;         // 16-wide d_v tiles
+  static constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  static constexpr int TCH = BLK / 8;       // 16-byte chunks per V^T row (8)
+  static constexpr int KB = BLK * D * 2;    // bytes of one K block (== one V^T block)
+  static constexpr int NT = 512;            // threads per workgroup (8 waves)
+  static constexpr int PER_T = KB / 16 / NT;  // 16-byte direct loads per thread per block
 };
 
+// One workgroup = 8 waves = 4 query heads of a GQA group x 64 query tokens.
+// Wave w owns head 4*hg + (w & 3) and query tokens 32*(w >> 2) .. +31, i.e.
+// two 16-token query tiles, so two waves share each SIMD and one wave's
+// softmax overlaps the other's MFMAs.
 template <int D>
-__global__ __launch_bounds__(256) void sparse_attn_bf16(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                         const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
                                                         uint16_t *__restrict__ o, int Hq, int Hkv, int N, int NQB,
                                                         int n_sel, int HG, int ntasks, float scale_log2) {
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bf16(const uint16_t *__restri
   __shared__ __attribute__((aligned(16))) char kbuf[2][Cf::KB];
   __shared__ __attribute__((aligned(16))) char vbuf[2][Cf::KB];
   __shared__ int sel[1024];
-  __shared__ int nvalid_sh;
+  __shared__ int nvalid_sh, diag_sh;
 
   // XCD-aware mapping: the HG workgroups of one task share blockIdx % 8.
   const int x = blockIdx.x;
@@ -109,89 +114,94 @@ __global__ __launch_bounds__(256) void sparse_attn_bf16(const uint16_t *__restri
   const int G = Hq / Hkv;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int hl = 4 * hg + w;
+  const int hl = 4 * hg + (w & 3);
   const bool active = hl < G;
   const int hq = kvh * G + (active ? hl : 0);
+  const int qt0 = 2 * (w >> 2);  // this wave's query tiles: qt0, qt0 + 1
 
-  // selected-block list: entries in order until the first negative, skipping j > i
+  // Block list: entries before the first negative, blocks after the query
+  // block dropped, the query's own (diagonal) block moved last so that only
+  // the final step needs the causal mask.
   if (tid == 0) {
     const int32_t *row = idx + ((size_t)bkv * NQB + i) * n_sel;
-    int n = 0;
+    int n = 0, has_diag = 0;
     for (int e = 0; e < n_sel; ++e) {
       const int j = row[e];
       if (j < 0) break;
-      if (j <= i) sel[n++] = j;
+      if (j < i) sel[n++] = j;
+      else if (j == i) has_diag = 1;
     }
+    if (has_diag) sel[n++] = i;
     nvalid_sh = n;
+    diag_sh = has_diag;
   }
 
-  // Q fragments (B operand): lane holds Q[t = 64i + 16qt + lr][32s + 8lg .. +7]
+  // Q fragments (B operand of K Q^T): lane holds Q[t = 64i + 16qt + lr][32s + 8lg .. +7]
   const uint16_t *qb = q + ((size_t)(b * Hq + hq) * N) * D;
-  u32x4 qf[4][Cf::NDS];
+  u32x4 qf[2][Cf::NDS];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int t = BLK * i + 16 * qt + lr;
+  for (int a = 0; a < 2; ++a) {
+    const int t = BLK * i + 16 * (qt0 + a) + lr;
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s)
-      qf[qt][s] = (t < N) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
+      qf[a][s] = (t < N) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
   }
 
-  f32x4 Oacc[4][Cf::ND];
+  f32x4 Oacc[2][Cf::ND];
+  f32x4 Lacc[2];  // row sums of P, accumulated on MFMA against a tile of ones
+  float mref[2];  // per-row reference max (log2 units) used by the exponentials
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt)
+  for (int a = 0; a < 2; ++a) {
 #pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv) Oacc[qt][dv] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) { mrow[qt] = -INFINITY; lrow[qt] = 0.f; }
+    for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Lacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mref[a] = -INFINITY;
+  }
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
   __syncthreads();
   const int nvalid = nvalid_sh;
+  const bool has_diag = diag_sh != 0;
   const uint16_t *kbase = k + ((size_t)bkv * N) * D;
   const int NB = (N + BLK - 1) / BLK;
   const uint16_t *vtbase = vt + ((size_t)bkv * NB) * D * BLK;
 
-  u32x4 kreg[Cf::PER_T], vreg[Cf::PER_T];
-  auto gather = [&](int j) {
+  // Direct global -> LDS loads (16 bytes per lane): the LDS slot of lane l in
+  // wave w for step u is p = 512u + 64w + l, so each lane fetches the logical
+  // chunk that the row swizzle maps to its slot (the XOR swizzles are
+  // involutions).  K rows past N re-read the last valid row; causality masks
+  // them.  V^T blocks come zero-padded from transpose_v_blocks.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto load_block = [&](int j, int buf) {
     const uint16_t *ksrc = kbase + (size_t)j * BLK * D;
     const uint16_t *vsrc = vtbase + (size_t)j * D * BLK;
-    const int rows_valid = min(BLK, N - j * BLK);
+    const int last = min(BLK, N - j * BLK) - 1;
 #pragma unroll
     for (int u = 0; u < Cf::PER_T; ++u) {
-      const int c = tid + 256 * u;
-      const int row = c / Cf::KCH;
-      kreg[u] = (row < rows_valid) ? gload16(ksrc + (size_t)c * 8) : u32x4{0, 0, 0, 0};
-      vreg[u] = gload16(vsrc + (size_t)c * 8);
+      const int p = Cf::NT * u + tid;
+      const int krow = p / Cf::KCH, kch = swz_k<Cf::KCH>(krow, p % Cf::KCH);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(ksrc + (size_t)min(krow, last) * D + 8 * kch),
+          (void __attribute__((address_space(3))) *)(kbuf[buf] + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
+      const int vrow = p / Cf::TCH, vch = swz_t<Cf::TCH>(vrow, p % Cf::TCH);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(vsrc + (size_t)vrow * BLK + 8 * vch),
+          (void __attribute__((address_space(3))) *)(vbuf[buf] + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
     }
   };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < Cf::PER_T; ++u) {
-      const int c = tid + 256 * u;
-      const int krow = c / Cf::KCH, kch = c % Cf::KCH;
-      lds_store(kbuf[buf], (krow * Cf::KCH + swz_k<Cf::KCH>(krow, kch)) * 16u, kreg[u]);
-      const int vrow = c / Cf::TCH, vch = c % Cf::TCH;
-      lds_store(vbuf[buf], (vrow * Cf::TCH + swz_t<Cf::TCH>(vrow, vch)) * 16u, vreg[u]);
-    }
-  };
+  // this wave's direct loads done (vmcnt 0); the barrier that follows publishes them
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  if (nvalid > 0) {
-    gather(sel[0]);
-    stage(0);
-  }
-  __syncthreads();
-
-  for (int bi = 0; bi < nvalid; ++bi) {
-    const int buf = bi & 1;
-    const int j = sel[bi];
-    if (bi + 1 < nvalid) gather(sel[bi + 1]);
-
-    // S^T = K Q^T : tiles [kt][qt], lane holds keys 32p + 8lg + 4t + e for kt = 2p + t
-    f32x4 Sacc[4][4];
+  // One block: S^T = K Q^T (tiles [kt][a], lane holds keys 32p + 8lg + 4t + e
+  // for kt = 2p + t), softmax numerators against a per-row reference max that
+  // moves (rescaling O and L) only when the block max exceeds it by more than
+  // 2^8, then O^T += V^T P^T and L += 1 P^T.
+  auto step = [&](int buf, bool mask) {
+    f32x4 S[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) Sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < 2; ++a) S[kt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s) {
 #pragma unroll
@@ -199,82 +209,92 @@ __global__ __launch_bounds__(256) void sparse_attn_bf16(const uint16_t *__restri
         const int row = 32 * (kt >> 1) + pair_key(kt & 1, lr);
         const u32x4 A = lds_load<u32x4>(kbuf[buf], (row * Cf::KCH + swz_k<Cf::KCH>(row, 4 * s + lg)) * 16u);
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) Sacc[kt][qt] = mfma16x16x32(A, qf[qt][s], Sacc[kt][qt]);
+        for (int a = 0; a < 2; ++a) S[kt][a] = mfma16x16x32(A, qf[a][s], S[kt][a]);
       }
     }
-
-    // online softmax (log2 domain)
-    const bool diag = (j == i);
-    u32x4 Pf[4][2];
+    float mb[2];
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const int qq = 16 * qt + lr;  // query position inside the block
+    for (int a = 0; a < 2; ++a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + e;
-          float xv = Sacc[kt][qt][e] * scale_log2;
-          if (diag && key > qq) xv = -INFINITY;
-          Sacc[kt][qt][e] = xv;
-          mx = fmaxf(mx, xv);
+          if (mask) {
+            const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + e;
+            if (key > 16 * (qt0 + a) + lr) S[kt][a][e] = -INFINITY;
+          }
+          mx = fmaxf(mx, S[kt][a][e]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);
-      mrow[qt] = mnew;
-      float ps = 0.f;
+      mb[a] = mx * scale_log2;
+    }
+    if (__any((mb[0] > mref[0] + 8.0f) || (mb[1] > mref[1] + 8.0f))) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const float mnew = fmaxf(mref[a], mb[a]);
+        const float alpha = __builtin_amdgcn_exp2f(mref[a] - mnew);
+        mref[a] = mnew;
+#pragma unroll
+        for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] *= alpha;
+        Lacc[a] *= alpha;
+      }
+    }
+    u32x4 Pf[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      float p[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(Sacc[kt][qt][e] - mnew);
-          Sacc[kt][qt][e] = pv;
-          ps += pv;
-        }
-      lrow[qt] = lrow[qt] * alpha + ps;
+        for (int e = 0; e < 4; ++e) p[kt][e] = __builtin_amdgcn_exp2f(fmaf(S[kt][a][e], scale_log2, -mref[a]));
 #pragma unroll
-      for (int dv = 0; dv < Cf::ND; ++dv) Oacc[qt][dv] *= alpha;
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        Pf[qt][p] = u32x4{pack_bf16x2(Sacc[2 * p][qt][0], Sacc[2 * p][qt][1]),
-                          pack_bf16x2(Sacc[2 * p][qt][2], Sacc[2 * p][qt][3]),
-                          pack_bf16x2(Sacc[2 * p + 1][qt][0], Sacc[2 * p + 1][qt][1]),
-                          pack_bf16x2(Sacc[2 * p + 1][qt][2], Sacc[2 * p + 1][qt][3])};
+      for (int pp = 0; pp < 2; ++pp)
+        Pf[a][pp] = u32x4{pack_bf16x2(p[2 * pp][0], p[2 * pp][1]), pack_bf16x2(p[2 * pp][2], p[2 * pp][3]),
+                          pack_bf16x2(p[2 * pp + 1][0], p[2 * pp + 1][1]),
+                          pack_bf16x2(p[2 * pp + 1][2], p[2 * pp + 1][3])};
     }
-
-    // O^T += V^T P^T
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
       for (int dv = 0; dv < Cf::ND; ++dv) {
         const int row = 16 * dv + lr;
-        const u32x4 A = lds_load<u32x4>(vbuf[buf], (row * Cf::TCH + swz_t<Cf::TCH>(row, 4 * p + lg)) * 16u);
+        const u32x4 A = lds_load<u32x4>(vbuf[buf], (row * Cf::TCH + swz_t<Cf::TCH>(row, 4 * pp + lg)) * 16u);
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) Oacc[qt][dv] = mfma16x16x32(A, Pf[qt][p], Oacc[qt][dv]);
+        for (int a = 0; a < 2; ++a) Oacc[a][dv] = mfma16x16x32(A, Pf[a][pp], Oacc[a][dv]);
       }
+#pragma unroll
+      for (int a = 0; a < 2; ++a) Lacc[a] = mfma16x16x32(ones, Pf[a][pp], Lacc[a]);
+    }
+  };
 
-    if (bi + 1 < nvalid) stage(buf ^ 1);
+  if (nvalid > 0) {
+    load_block(sel[0], 0);
+    wait_loads();
     __syncthreads();
+    for (int j = 0; j + 1 < nvalid; ++j) {
+      load_block(sel[j + 1], (j + 1) & 1);  // lands while block j is processed
+      step(j & 1, false);
+      wait_loads();
+      __syncthreads();
+    }
+    step((nvalid - 1) & 1, has_diag);
   }
 
   if (!active) return;
   uint16_t *ob = o + ((size_t)(b * Hq + hq) * N) * D;
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    float lt = lrow[qt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+  for (int a = 0; a < 2; ++a) {
+    const float lt = Lacc[a][0];
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-    const int t = BLK * i + 16 * qt + lr;
+    const int t = BLK * i + 16 * (qt0 + a) + lr;
     if (t < N) {
 #pragma unroll
       for (int dv = 0; dv < Cf::ND; ++dv)
         *reinterpret_cast<u32x2 *>(ob + (size_t)t * D + 16 * dv + 4 * lg) =
-            u32x2{pack_bf16x2(Oacc[qt][dv][0] * inv, Oacc[qt][dv][1] * inv),
-                  pack_bf16x2(Oacc[qt][dv][2] * inv, Oacc[qt][dv][3] * inv)};
+            u32x2{pack_bf16x2(Oacc[a][dv][0] * inv, Oacc[a][dv][1] * inv),
+                  pack_bf16x2(Oacc[a][dv][2] * inv, Oacc[a][dv][3] * inv)};
     }
   }
 }
@@ -373,13 +393,13 @@ hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st) {
   if (a.d == 128) {
     hipLaunchKernelGGL(transpose_v_blocks<128>, dim3(a.B * a.Hkv * NB), dim3(256), 0, st, (const uint16_t *)a.v,
                        vt, a.N, NB);
-    hipLaunchKernelGGL(sparse_attn_bf16<128>, dim3(grid), dim3(256), 0, st, (const uint16_t *)a.q,
+    hipLaunchKernelGGL(sparse_attn_bf16<128>, dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
                        (const uint16_t *)a.k, vt, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HG,
                        ntasks, scale_log2);
   } else {
     hipLaunchKernelGGL(transpose_v_blocks<64>, dim3(a.B * a.Hkv * NB), dim3(256), 0, st, (const uint16_t *)a.v, vt,
                        a.N, NB);
-    hipLaunchKernelGGL(sparse_attn_bf16<64>, dim3(grid), dim3(256), 0, st, (const uint16_t *)a.q,
+    hipLaunchKernelGGL(sparse_attn_bf16<64>, dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
                        (const uint16_t *)a.k, vt, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HG,
                        ntasks, scale_log2);
   }
