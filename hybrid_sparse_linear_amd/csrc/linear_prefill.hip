@@ -33,22 +33,31 @@ namespace {
 
 template <int C, int D>
 struct LinCfg {
-  static constexpr int NQT = C / 16;            // 16-query tiles per chunk
-  static constexpr int QPW = NQT / 4;           // query tiles per wave
+  static constexpr int NT = 512;                // 8 waves, two per SIMD
+  static constexpr int NQT = C / 16;            // 16-query tiles per chunk (one per wave at C = 128)
   static constexpr int ND = D / 16;             // 16-wide feature tiles
   static constexpr int NDS = D / 32;            // 32-deep steps over features
   static constexpr int NKS = C / 32;            // 32-deep steps over chunk tokens
-  static constexpr int DKW = ND / 4;            // state d_k tiles per wave
+  static constexpr int NDV = ND * ND / 8;       // state tiles per wave (one d_k tile row or half of one)
   static constexpr int KCH = D / 8;             // 16-byte chunks per row of K_lds / St_lds
   static constexpr int TCH = C / 8;             // 16-byte chunks per row of Kt_lds / Vt_lds
-  static constexpr int NB8 = (C / 8) * (D / 8); // 8x8 staging blocks per chunk
+  static constexpr int NB8 = (C / 8) * (D / 8); // 8x8 staging blocks per chunk (of K, and of V)
   static constexpr uint32_t K_OFF = 0;
   static constexpr uint32_t KT_OFF = K_OFF + C * D * 2;
   static constexpr uint32_t VT_OFF = KT_OFF + C * D * 2;
   static constexpr uint32_t ST_OFF = VT_OFF + C * D * 2;
   static constexpr uint32_t PW_OFF = ST_OFF + D * D * 2;
   static constexpr uint32_t LDS = PW_OFF + (C + 4) * 4;
-  static_assert(NB8 <= 256, "one 8x8 staging block per thread at most");
+  static_assert(2 * NB8 <= NT, "one 8x8 staging block per thread at most");
+  // wave -> state tiles: d_k tile dkt(w), d_v tiles dv0(w) .. dv0(w)+NDV-1
+  __device__ static int dkt(int w) { return ND == 8 ? w : (w >> 1); }
+  __device__ static int dv0(int w) { return ND == 8 ? 0 : 2 * (w & 1); }
+  // wave -> query tile (-1: none).  Waves w and w+4 share a SIMD; pairing
+  // tiles w and 7-w balances the causal work per SIMD.
+  __device__ static int qtile(int w) {
+    if (NQT == 8) return w < 4 ? w : 11 - w;
+    return w < NQT ? w : -1;
+  }
 };
 
 // XOR swizzles of 16-byte chunks inside an LDS row (bank-conflict avoidance).
@@ -71,7 +80,8 @@ __device__ __forceinline__ uint32_t off_k(uint32_t row, uint32_t ch) { return (r
 // Key permutation inside a 32-key pair of 16-key tiles: MFMA row r of tile t
 // (t = 0, 1) holds key 8*(r/4) + 4*t + r%4, so that after K Q^T each lane's
 // 4+4 accumulator rows of the two tiles are 8 consecutive keys -- exactly the
-// k slots of the B operand of the following V^T P^T product.
+// k slots of the B operand of the following V^T P^T product.  Both tiles of a
+// pair therefore hold keys from the whole 32-key range.
 __device__ __forceinline__ int pair_key(int t, int r) { return ((r >> 2) << 3) + (t << 2) + (r & 3); }
 
 // Transpose an 8x8 bf16 block: x[e] = row e (8 features, 4 dwords);
@@ -88,84 +98,85 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&x)[8], u32x4 (&y)[8])
   }
 }
 
-// Stage one chunk (rows c0 .. c0+m-1 of K and V, already in registers as one
-// 8x8 block per thread) into K_lds (row-major), Kt_lds (transposed, row j
-// scaled by lam^(m-1-j)) and Vt_lds (transposed).
-template <int C, int D, bool WITH_K>
-__device__ __forceinline__ void stage_chunk(char *lds, int tid, int m, const float *pw,
-                                            u32x4 (&kst)[8], const u32x4 (&vst)[8]) {
-  using Cf = LinCfg<C, D>;
-  if (tid >= Cf::NB8) return;
-  const int tg = tid / (D / 8), fg = tid % (D / 8);
-  if constexpr (WITH_K) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lds_store(lds + Cf::K_OFF, off_k<Cf::KCH>(8 * tg + e, fg), kst[e]);
-  }
-  // scale K rows by lam^(m-1-j) in fp32, round once to bf16
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int j = 8 * tg + e;
-    const float sc = (j < m) ? pw[m - 1 - j] : 0.f;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) kst[e][p] = pack_bf16x2(bf16lo(kst[e][p]) * sc, bf16hi(kst[e][p]) * sc);
-  }
-  u32x4 y[8];
-  transpose8x8(kst, y);
-#pragma unroll
-  for (int f = 0; f < 8; ++f) lds_store(lds + Cf::KT_OFF, off_t<Cf::TCH>(8 * fg + f, tg), y[f]);
-  transpose8x8(vst, y);
-#pragma unroll
-  for (int f = 0; f < 8; ++f) lds_store(lds + Cf::VT_OFF, off_t<Cf::TCH>(8 * fg + f, tg), y[f]);
-}
-
-// Load this thread's 8x8 block of K and V for the chunk starting at token c0
-// (rows at or past t_end read as zero).
+// Staging job of a thread: one 8x8 block of K (jobs 0 .. NB8-1) or of V
+// (jobs NB8 .. 2*NB8-1) of the chunk starting at token c0; rows at or past
+// t_end read as zero.
 template <int C, int D>
-__device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end,
-                                        u32x4 (&kst)[8], u32x4 (&vst)[8]) {
+__device__ __forceinline__ void load_block8(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end,
+                                            u32x4 (&x)[8]) {
   using Cf = LinCfg<C, D>;
-  if (tid >= Cf::NB8) return;
-  const int tg = tid / (D / 8), fg = tid % (D / 8);
+  if (tid >= 2 * Cf::NB8) return;
+  const bool is_v = tid >= Cf::NB8;
+  const int job = is_v ? tid - Cf::NB8 : tid;
+  const int tg = job / (D / 8), fg = job % (D / 8);
+  const uint16_t *src = is_v ? vb : kb;
+  // unconditional loads of clamped rows, then zero the rows past t_end
+  // (selects instead of a branch per load)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int t = c0 + 8 * tg + e;
-    if (t < t_end) {
-      kst[e] = gload16(kb + (size_t)t * D + 8 * fg);
-      vst[e] = gload16(vb + (size_t)t * D + 8 * fg);
-    } else {
-      kst[e] = u32x4{0, 0, 0, 0};
-      vst[e] = u32x4{0, 0, 0, 0};
-    }
+    x[e] = gload16(src + (size_t)min(t, t_end - 1) * D + 8 * fg);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (c0 + 8 * tg + e >= t_end) x[e] = u32x4{0, 0, 0, 0};
   }
 }
 
-// State update S = lam^m S + (Kt scaled)^T V for this wave's d_k tiles.
+// Write a staged block: K -> K_lds (row-major, when WITH_K) and Kt_lds
+// (transposed, row j scaled by lam^(m-1-j) in fp32 and rounded once);
+// V -> Vt_lds (transposed).
+template <int C, int D, bool WITH_K>
+__device__ __forceinline__ void stage_block8(char *lds, int tid, int m, const float *pw, u32x4 (&x)[8]) {
+  using Cf = LinCfg<C, D>;
+  if (tid >= 2 * Cf::NB8) return;
+  const bool is_v = tid >= Cf::NB8;
+  const int job = is_v ? tid - Cf::NB8 : tid;
+  const int tg = job / (D / 8), fg = job % (D / 8);
+  u32x4 y[8];
+  if (!is_v) {
+    if constexpr (WITH_K) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lds_store(lds + Cf::K_OFF, off_k<Cf::KCH>(8 * tg + e, fg), x[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * tg + e;
+      const float sc = (j < m) ? pw[m - 1 - j] : 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) x[e][p] = pack_bf16x2(bf16lo(x[e][p]) * sc, bf16hi(x[e][p]) * sc);
+    }
+    transpose8x8(x, y);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) lds_store(lds + Cf::KT_OFF, off_t<Cf::TCH>(8 * fg + f, tg), y[f]);
+  } else {
+    transpose8x8(x, y);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) lds_store(lds + Cf::VT_OFF, off_t<Cf::TCH>(8 * fg + f, tg), y[f]);
+  }
+}
+
+// State update S = lam^m S + (Kt scaled)^T V for this wave's state tiles.
 template <int C, int D>
 __device__ __forceinline__ void state_update(const char *lds, int w, int lr, int lg, float lam_m,
-                                             f32x4 (&Sacc)[LinCfg<C, D>::DKW][LinCfg<C, D>::ND]) {
+                                             f32x4 (&Sacc)[LinCfg<C, D>::NDV]) {
   using Cf = LinCfg<C, D>;
 #pragma unroll
-  for (int a = 0; a < Cf::DKW; ++a)
-#pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv) Sacc[a][dv] *= lam_m;
+  for (int a = 0; a < Cf::NDV; ++a) Sacc[a] *= lam_m;
 #pragma unroll
   for (int ks = 0; ks < Cf::NKS; ++ks) {
-    u32x4 A[Cf::DKW];
+    const u32x4 A = lds_load<u32x4>(lds + Cf::KT_OFF, off_t<Cf::TCH>(16 * Cf::dkt(w) + lr, 4 * ks + lg));
 #pragma unroll
-    for (int a = 0; a < Cf::DKW; ++a)
-      A[a] = lds_load<u32x4>(lds + Cf::KT_OFF, off_t<Cf::TCH>(16 * (Cf::DKW * w + a) + lr, 4 * ks + lg));
-#pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv) {
-      const u32x4 Bv = lds_load<u32x4>(lds + Cf::VT_OFF, off_t<Cf::TCH>(16 * dv + lr, 4 * ks + lg));
-#pragma unroll
-      for (int a = 0; a < Cf::DKW; ++a) Sacc[a][dv] = mfma16x16x32(A[a], Bv, Sacc[a][dv]);
+    for (int a = 0; a < Cf::NDV; ++a) {
+      const u32x4 Bv = lds_load<u32x4>(lds + Cf::VT_OFF, off_t<Cf::TCH>(16 * (Cf::dv0(w) + a) + lr, 4 * ks + lg));
+      Sacc[a] = mfma16x16x32(A, Bv, Sacc[a]);
     }
   }
 }
 
 // ---------------------------------------------------------------- pass 1
 template <int C, int D>
-__global__ __launch_bounds__(256) void lin_seg_aggregate(const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v,
                                                          const float *__restrict__ decay,
                                                          float *__restrict__ seg_state, int H, int N,
@@ -179,34 +190,30 @@ __global__ __launch_bounds__(256) void lin_seg_aggregate(const uint16_t *__restr
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
   float *pw = reinterpret_cast<float *>(lds + Cf::PW_OFF);
-  for (int n = tid; n <= C; n += 256) pw[n] = (float)pow((double)lam, (double)n);
+  for (int n = tid; n <= C; n += Cf::NT) pw[n] = (float)pow((double)lam, (double)n);
   const uint16_t *kb = k + (size_t)bh * N * D;
   const uint16_t *vb = v + (size_t)bh * N * D;
 
-  f32x4 Sacc[Cf::DKW][Cf::ND];
+  f32x4 Sacc[Cf::NDV];
 #pragma unroll
-  for (int a = 0; a < Cf::DKW; ++a)
-#pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv) Sacc[a][dv] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < Cf::NDV; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 kst[8], vst[8];
-  load_kv<C, D>(kb, vb, tid, t_begin, t_end, kst, vst);
+  u32x4 x[8];
+  load_block8<C, D>(kb, vb, tid, t_begin, t_end, x);
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    stage_chunk<C, D, false>(lds, tid, m, pw, kst, vst);
+    stage_block8<C, D, false>(lds, tid, m, pw, x);
     __syncthreads();
-    if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, kst, vst);
+    if (c0 + C < t_end) load_block8<C, D>(kb, vb, tid, c0 + C, t_end, x);
     state_update<C, D>(lds, w, lr, lg, pw[m], Sacc);
   }
   float *out = seg_state + ((size_t)bh * nseg + seg) * D * D;
 #pragma unroll
-  for (int a = 0; a < Cf::DKW; ++a)
+  for (int a = 0; a < Cf::NDV; ++a)
 #pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        out[(size_t)(16 * (Cf::DKW * w + a) + 4 * lg + i) * D + 16 * dv + lr] = Sacc[a][dv][i];
+    for (int i = 0; i < 4; ++i)
+      out[(size_t)(16 * Cf::dkt(w) + 4 * lg + i) * D + 16 * (Cf::dv0(w) + a) + lr] = Sacc[a][i];
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_stat
 
 // ---------------------------------------------------------------- pass 3
 template <int C, int D>
-__global__ __launch_bounds__(256) void lin_seg_output(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict__ q,
                                                       const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
                                                       uint16_t *__restrict__ o,
@@ -248,95 +255,71 @@ __global__ __launch_bounds__(256) void lin_seg_output(const uint16_t *__restrict
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
   float *pw = reinterpret_cast<float *>(lds + Cf::PW_OFF);
-  for (int n = tid; n <= C; n += 256) pw[n] = (float)pow((double)lam, (double)n);
+  for (int n = tid; n <= C; n += Cf::NT) pw[n] = (float)pow((double)lam, (double)n);
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t *qb = q + head_off, *kb = k + head_off, *vb = v + head_off;
   uint16_t *ob = o + head_off;
+  const int qt = Cf::qtile(w);
+  const int dkt = Cf::dkt(w), dv0 = Cf::dv0(w);
 
-  int qts[Cf::QPW];
-  if constexpr (Cf::QPW == 2) { qts[0] = w; qts[1] = Cf::NQT - 1 - w; }
-  else { qts[0] = w; }
-
-  f32x4 Sacc[Cf::DKW][Cf::ND];
+  f32x4 Sacc[Cf::NDV];
   const float *sin = seg_state ? seg_state + (size_t)bh * seg_stride * nseg + (size_t)seg * seg_stride : nullptr;
 #pragma unroll
-  for (int a = 0; a < Cf::DKW; ++a)
+  for (int a = 0; a < Cf::NDV; ++a)
 #pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Sacc[a][dv][i] = sin ? sin[(size_t)(16 * (Cf::DKW * w + a) + 4 * lg + i) * D + 16 * dv + lr] : 0.f;
+    for (int i = 0; i < 4; ++i)
+      Sacc[a][i] = sin ? sin[(size_t)(16 * dkt + 4 * lg + i) * D + 16 * (dv0 + a) + lr] : 0.f;
 
-  u32x4 kst[8], vst[8];
-  u32x4 qf[Cf::QPW][Cf::NDS];
-  auto load_q = [&](int c0, u32x4 (&dst)[Cf::QPW][Cf::NDS]) {
+  u32x4 x[8];
+  u32x4 qf[Cf::NDS];
+  auto load_q = [&](int c0, u32x4 (&dst)[Cf::NDS]) {
+    // rows past t_end load a clamped row; their outputs are never stored
+    const int t = min(c0 + 16 * max(qt, 0) + lr, t_end - 1);
 #pragma unroll
-    for (int a = 0; a < Cf::QPW; ++a) {
-      const int t = c0 + 16 * qts[a] + lr;
-#pragma unroll
-      for (int s = 0; s < Cf::NDS; ++s)
-        dst[a][s] = (t < t_end) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < Cf::NDS; ++s) dst[s] = gload16(qb + (size_t)t * D + 32 * s + 8 * lg);
   };
-  load_kv<C, D>(kb, vb, tid, t_begin, t_end, kst, vst);
+  load_block8<C, D>(kb, vb, tid, t_begin, t_end, x);
   load_q(t_begin, qf);
 
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    stage_chunk<C, D, true>(lds, tid, m, pw, kst, vst);
+    stage_block8<C, D, true>(lds, tid, m, pw, x);
     // bf16 copy of S^T (rows d_v, columns d_k) for the Q S product
 #pragma unroll
-    for (int a = 0; a < Cf::DKW; ++a) {
-      const int dkt = Cf::DKW * w + a;
-#pragma unroll
-      for (int dv = 0; dv < Cf::ND; ++dv) {
-        const int row = 16 * dv + lr;
-        const uint32_t off = off_t<Cf::KCH>(row, 2 * dkt + (lg >> 1)) + (lg & 1) * 8;
-        lds_store(lds + Cf::ST_OFF, off,
-                  u32x2{pack_bf16x2(Sacc[a][dv][0], Sacc[a][dv][1]), pack_bf16x2(Sacc[a][dv][2], Sacc[a][dv][3])});
-      }
+    for (int a = 0; a < Cf::NDV; ++a) {
+      const int row = 16 * (dv0 + a) + lr;
+      const uint32_t off = off_t<Cf::KCH>(row, 2 * dkt + (lg >> 1)) + (lg & 1) * 8;
+      lds_store(lds + Cf::ST_OFF, off, u32x2{pack_bf16x2(Sacc[a][0], Sacc[a][1]), pack_bf16x2(Sacc[a][2], Sacc[a][3])});
     }
     __syncthreads();
-    u32x4 qn[Cf::QPW][Cf::NDS];
+    u32x4 qn[Cf::NDS];
     if (c0 + C < t_end) {
-      load_kv<C, D>(kb, vb, tid, c0 + C, t_end, kst, vst);
+      load_block8<C, D>(kb, vb, tid, c0 + C, t_end, x);
       load_q(c0 + C, qn);
     }
 
-    // (1) O^T = lam^(i+1) * S^T Q^T
-    f32x4 Oacc[Cf::QPW][Cf::ND];
+    if (qt >= 0) {
+      const int qq = 16 * qt + lr;  // this lane's query inside the chunk
+      // (1) O^T = lam^(qq+1) * S^T Q^T
+      f32x4 Oacc[Cf::ND];
+#pragma unroll 2
+      for (int dv = 0; dv < Cf::ND; ++dv) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dv = 0; dv < Cf::ND; ++dv) {
-      f32x4 acc[Cf::QPW];
-#pragma unroll
-      for (int a = 0; a < Cf::QPW; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < Cf::NDS; ++s) {
-        const u32x4 A = lds_load<u32x4>(lds + Cf::ST_OFF, off_t<Cf::KCH>(16 * dv + lr, 4 * s + lg));
-#pragma unroll
-        for (int a = 0; a < Cf::QPW; ++a) acc[a] = mfma16x16x32(A, qf[a][s], acc[a]);
+        for (int s = 0; s < Cf::NDS; ++s)
+          acc = mfma16x16x32(lds_load<u32x4>(lds + Cf::ST_OFF, off_t<Cf::KCH>(16 * dv + lr, 4 * s + lg)), qf[s], acc);
+        Oacc[dv] = acc * pw[qq + 1];
       }
-#pragma unroll
-      for (int a = 0; a < Cf::QPW; ++a) Oacc[a][dv] = acc[a] * pw[16 * qts[a] + lr + 1];
-    }
-
-    // (2)+(3) P^T = decay-masked K Q^T ; O^T += V^T P^T
-#pragma unroll
-    for (int a = 0; a < Cf::QPW; ++a) {
-      const int qt = qts[a];
-      const int qq = 16 * qt + lr;
+      // (2)+(3) P^T = decay-masked K Q^T over the causal key pairs; O^T += V^T P^T
       for (int p = 0; p <= (qt >> 1); ++p) {
-        // Both 16-row tiles of a pair hold keys from the whole 32-key range
-        // (pair_key interleaves them), so neither can be skipped; the causal
-        // mask below zeroes keys past the query.
         f32x4 P0 = {0.f, 0.f, 0.f, 0.f}, P1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < Cf::NDS; ++s) {
           const u32x4 A0 = lds_load<u32x4>(lds + Cf::K_OFF, off_k<Cf::KCH>(32 * p + pair_key(0, lr), 4 * s + lg));
           const u32x4 A1 = lds_load<u32x4>(lds + Cf::K_OFF, off_k<Cf::KCH>(32 * p + pair_key(1, lr), 4 * s + lg));
-          P0 = mfma16x16x32(A0, qf[a][s], P0);
-          P1 = mfma16x16x32(A1, qf[a][s], P1);
+          P0 = mfma16x16x32(A0, qf[s], P0);
+          P1 = mfma16x16x32(A1, qf[s], P1);
         }
         const int j0 = 32 * p + 8 * lg;
 #pragma unroll
@@ -345,26 +328,20 @@ __global__ __launch_bounds__(256) void lin_seg_output(const uint16_t *__restrict
           P0[i] = (ja <= qq) ? P0[i] * pw[qq - ja] : 0.f;
           P1[i] = (jb <= qq) ? P1[i] * pw[qq - jb] : 0.f;
         }
-        const u32x4 Bp = {pack_bf16x2(P0[0], P0[1]), pack_bf16x2(P0[2], P0[3]),
-                          pack_bf16x2(P1[0], P1[1]), pack_bf16x2(P1[2], P1[3])};
+        const u32x4 Bp = {pack_bf16x2(P0[0], P0[1]), pack_bf16x2(P0[2], P0[3]), pack_bf16x2(P1[0], P1[1]),
+                          pack_bf16x2(P1[2], P1[3])};
 #pragma unroll
-        for (int dv = 0; dv < Cf::ND; ++dv) {
-          const u32x4 A = lds_load<u32x4>(lds + Cf::VT_OFF, off_t<Cf::TCH>(16 * dv + lr, 4 * p + lg));
-          Oacc[a][dv] = mfma16x16x32(A, Bp, Oacc[a][dv]);
-        }
+        for (int dv = 0; dv < Cf::ND; ++dv)
+          Oacc[dv] = mfma16x16x32(lds_load<u32x4>(lds + Cf::VT_OFF, off_t<Cf::TCH>(16 * dv + lr, 4 * p + lg)), Bp,
+                                  Oacc[dv]);
       }
-    }
-
-    // (4) write O rows of this chunk
-#pragma unroll
-    for (int a = 0; a < Cf::QPW; ++a) {
-      const int qq = 16 * qts[a] + lr;
+      // (4) write this lane's output row
       if (qq < m) {
         uint16_t *orow = ob + (size_t)(c0 + qq) * D;
 #pragma unroll
         for (int dv = 0; dv < Cf::ND; ++dv)
           *reinterpret_cast<u32x2 *>(orow + 16 * dv + 4 * lg) =
-              u32x2{pack_bf16x2(Oacc[a][dv][0], Oacc[a][dv][1]), pack_bf16x2(Oacc[a][dv][2], Oacc[a][dv][3])};
+              u32x2{pack_bf16x2(Oacc[dv][0], Oacc[dv][1]), pack_bf16x2(Oacc[dv][2], Oacc[dv][3])};
       }
     }
 
@@ -373,21 +350,16 @@ __global__ __launch_bounds__(256) void lin_seg_output(const uint16_t *__restrict
 
     if (c0 + C < t_end) {
 #pragma unroll
-      for (int a = 0; a < Cf::QPW; ++a)
-#pragma unroll
-        for (int s = 0; s < Cf::NDS; ++s) qf[a][s] = qn[a][s];
+      for (int s = 0; s < Cf::NDS; ++s) qf[s] = qn[s];
     }
   }
 
   if (state_out && seg == nseg - 1) {
     float *so = state_out + (size_t)bh * D * D;
 #pragma unroll
-    for (int a = 0; a < Cf::DKW; ++a)
+    for (int a = 0; a < Cf::NDV; ++a)
 #pragma unroll
-      for (int dv = 0; dv < Cf::ND; ++dv)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          so[(size_t)(16 * (Cf::DKW * w + a) + 4 * lg + i) * D + 16 * dv + lr] = Sacc[a][dv][i];
+      for (int i = 0; i < 4; ++i) so[(size_t)(16 * dkt + 4 * lg + i) * D + 16 * (dv0 + a) + lr] = Sacc[a][i];
   }
 }
 
@@ -454,13 +426,13 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   const size_t DD = (size_t)D * D;
   const float *seg_state = a.state_in;  // nseg == 1: segment 0 starts from state_in
   if (nseg > 1) {
-    hipLaunchKernelGGL((lin_seg_aggregate<C, D>), dim3(BH * (nseg - 1)), dim3(256), 0, st,
+    hipLaunchKernelGGL((lin_seg_aggregate<C, D>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
                        (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws,
                        a.state_in, a.decay, a.H, (int)DD, a.N, seg_len, nseg);
     seg_state = ws;
   }
-  hipLaunchKernelGGL((lin_seg_output<C, D>), dim3(BH * nseg), dim3(256), 0, st, (const uint16_t *)a.q,
+  hipLaunchKernelGGL((lin_seg_output<C, D>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, DD,
                      a.state_out, a.H, a.N, seg_len, nseg);
   return hipGetLastError();
