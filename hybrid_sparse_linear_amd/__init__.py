@@ -135,9 +135,8 @@ def sparse_select(q, k=None, *, k_pooled=None, L=None, block=64, topk=64, n_init
         k_pooled = torch.empty((B, Hkv, NB, d), dtype=torch.float32, device=q.device)
     idx = torch.empty((B, Hkv, NQB, W), dtype=torch.int32, device=q.device) if idx_out is None else idx_out
     scores = torch.empty((B, Hkv, NQB, NB), dtype=torch.float32, device=q.device) if return_scores else None
+    # the size for scores == NULL covers every case (with a scores buffer the need is never larger)
     nb = lib().sala_sparse_select_workspace(dt, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local)
-    if return_scores:
-        nb = max(0, nb - B * Hkv * NQB * NB * 4)
     ws = _ws(nb, workspace, q)
     call("sala_sparse_select", dt, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local, _ptr(q), _ptr(k),
          _ptr(k_pooled), _ptr(idx), _ptr(scores), _ptr(ws), nb, _stream())

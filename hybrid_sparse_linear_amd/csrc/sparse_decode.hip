@@ -4,10 +4,12 @@
 // FlashAttention entry of the fugumt.com related list for arXiv 2607.21752);
 // the KV cache is kept whole (MiniCPM-SALA, gist.science (ja) 技術概要 section 1).
 //
-// Split-K: decode_partial gives each workgroup a few selected blocks of one
-// (b, kv head) and all G query heads of that group (one gathered block feeds
-// G heads), producing (max, sum, unnormalised o) per head in log2 units;
-// decode_combine merges the splits with the usual log-sum-exp rescaling.
+// Split-K: a workgroup takes selected blocks of one (b, kv head) for all G
+// query heads of that group (one gathered block feeds G heads) and writes
+// (max, sum, unnormalised o) per head in log2 units; decode_combine merges the
+// splits with the usual log-sum-exp rescaling.  bf16 with G <= 16 uses
+// decode_attend_mfma (one block per workgroup, logits on MFMA); other cases
+// use decode_partial (fp32 VALU, a few blocks per workgroup).
 
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
@@ -146,20 +148,152 @@ __global__ __launch_bounds__(256) void decode_partial(const T *__restrict__ q, c
   }
 }
 
+// bf16, G <= 16: one workgroup per (b, kv head, entry e of the selected list).
+// Wave w takes keys 16w .. 16w+15 of the block: S^T = K Q^T on one MFMA
+// 16x16x32 tile per d-step (A = 16 keys, B = the group's <= 16 query heads,
+// both loaded straight into operand registers).  Softmax pieces for the 64
+// keys go through LDS; O = P V runs on the VALU from V staged in LDS.
+// Writes (o unnormalised, max, sum) per head in log2 units for the combine.
+template <int D>
+__global__ __launch_bounds__(256) void decode_attend_mfma(const uint16_t *__restrict__ q,
+                                                          const uint16_t *__restrict__ kc,
+                                                          const uint16_t *__restrict__ vc,
+                                                          const int32_t *__restrict__ idx, float *__restrict__ part,
+                                                          int Hq, int Hkv, int L, int n_sel, float scale_log2) {
+  constexpr int NDS = D / 32;
+  constexpr int VS = D + 8;        // padded V row (elements)
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int DPG = D / 16;      // d_v columns per thread in O = P V
+  __shared__ __attribute__((aligned(16))) uint16_t vs[BLK * VS];
+  __shared__ float ps[16][BLK + 4];
+  __shared__ float red_m[4][16], red_l[4][16];
+  const int bkv = blockIdx.x / n_sel, e = blockIdx.x % n_sel;
+  const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int32_t *row = idx + (size_t)bkv * n_sel;
+  bool valid = true;
+  for (int x = 0; x <= e; ++x) valid = valid && row[x] >= 0;  // entries end at the first negative
+  const int j = row[e];
+  valid = valid && (size_t)j * BLK < (size_t)L;
+  const int hh = tid >> 4, g = tid & 15;  // O = P V: head hh, columns DPG*g ..
+  float *dst = part + ((size_t)(b * Hq + kvh * G + hh) * n_sel + e) * (D + 2);
+  if (!valid) {  // an empty split: the combine gives it zero weight
+    if (hh < G) {
+#pragma unroll
+      for (int c = 0; c < DPG; ++c) dst[DPG * g + c] = 0.f;
+      if (g == 0) { dst[D] = -INFINITY; dst[D + 1] = 0.f; }
+    }
+    return;
+  }
+  const int cnt = min(BLK, L - j * BLK);
+  const size_t base = (size_t)bkv * L + (size_t)j * BLK;
+  // issue every load up front: K and Q operand fragments, V rows to LDS
+  u32x4 kf[NDS], qfr[NDS], vr[(BLK * CPR) / 256];
+  const uint16_t *kp = kc + (base + min(16 * w + lr, cnt - 1)) * D;
+  const uint16_t *qp = q + (size_t)(b * Hq + kvh * G + min(lr, G - 1)) * D;
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) {
+    kf[s] = gload16(kp + 32 * s + 8 * lg);
+    qfr[s] = gload16(qp + 32 * s + 8 * lg);
+  }
+#pragma unroll
+  for (int u = 0; u < (BLK * CPR) / 256; ++u) {
+    const int c = tid + 256 * u, r = c / CPR, ch = c % CPR;
+    vr[u] = gload16(vc + (base + min(r, cnt - 1)) * D + 8 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < (BLK * CPR) / 256; ++u) {
+    const int c = tid + 256 * u, r = c / CPR, ch = c % CPR;
+    *reinterpret_cast<u32x4 *>(&vs[r * VS + 8 * ch]) = (r < cnt) ? vr[u] : u32x4{0, 0, 0, 0};
+  }
+  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) S = mfma16x16x32(kf[s], (lr < G) ? qfr[s] : u32x4{0, 0, 0, 0}, S);
+  // lane (head lr, group lg) holds keys 16w + 4lg + i
+  float x[4], mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (16 * w + 4 * lg + i < cnt) ? S[i] * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, x[i]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (lg == 0) red_m[w][lr] = mx;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red_m[0][lr], red_m[1][lr]), fmaxf(red_m[2][lr], red_m[3][lr]));
+  float ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = __builtin_amdgcn_exp2f(x[i] - m);
+    ps[lr][16 * w + 4 * lg + i] = p;
+    ls += p;
+  }
+  ls += __shfl_xor(ls, 16, 64);
+  ls += __shfl_xor(ls, 32, 64);
+  if (lg == 0) red_l[w][lr] = ls;
+  __syncthreads();
+  if (hh >= G) return;
+  float o[DPG];
+#pragma unroll
+  for (int c = 0; c < DPG; ++c) o[c] = 0.f;
+  for (int key = 0; key < cnt; ++key) {
+    const float p = ps[hh][key];
+    if constexpr (DPG == 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&vs[key * VS + 8 * g]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[2 * c] = fmaf(p, bf16lo(v[c]), o[2 * c]);
+        o[2 * c + 1] = fmaf(p, bf16hi(v[c]), o[2 * c + 1]);
+      }
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2 *>(&vs[key * VS + 4 * g]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        o[2 * c] = fmaf(p, bf16lo(v[c]), o[2 * c]);
+        o[2 * c + 1] = fmaf(p, bf16hi(v[c]), o[2 * c + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < DPG; ++c) dst[DPG * g + c] = o[c];
+  if (g == 0) {
+    dst[D] = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
+    dst[D + 1] = red_l[0][hh] + red_l[1][hh] + red_l[2][hh] + red_l[3][hh];
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine(const float *__restrict__ part, T *__restrict__ o, int nsplit) {
+  // log-sum-exp merge of the splits; loads are batched so they overlap
   const int bh = blockIdx.x, c = threadIdx.x;
   const float *p = part + (size_t)bh * nsplit * (D + 2);
+  constexpr int U = 8;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[(size_t)s * (D + 2) + D]);
+  for (int s0 = 0; s0 < nsplit; s0 += U) {
+    float mm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mm[u] = (s0 + u < nsplit) ? p[(size_t)(s0 + u) * (D + 2) + D] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
+  }
   float lsum = 0.f, acc = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = p[(size_t)s * (D + 2) + D];
-      if (ms == -INFINITY) continue;
-      const float wgt = __builtin_amdgcn_exp2f(ms - M);
-      lsum = fmaf(p[(size_t)s * (D + 2) + D + 1], wgt, lsum);
-      acc = fmaf(p[(size_t)s * (D + 2) + c], wgt, acc);
+    for (int s0 = 0; s0 < nsplit; s0 += U) {
+      float mm[U], ll[U], oo[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = s0 + u < nsplit;
+        const float *r = p + (size_t)(s0 + u) * (D + 2);
+        mm[u] = ok ? r[D] : -INFINITY;
+        ll[u] = ok ? r[D + 1] : 0.f;
+        oo[u] = ok ? r[c] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wgt = (mm[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm[u] - M);
+        lsum = fmaf(ll[u], wgt, lsum);
+        acc = fmaf(oo[u], wgt, acc);
+      }
     }
   }
   const float r = (lsum > 0.f) ? acc / lsum : 0.f;
@@ -177,9 +311,16 @@ void split_plan(int BHkv, int n_sel, int *nsplit, int *bps) {
 
 template <typename T, int D>
 void run(const SparseDecodeArgs &a, hipStream_t st) {
+  float *part = static_cast<float *>(a.ws);
+  if (sizeof(T) == 2 && a.Hq / a.Hkv <= 16) {
+    hipLaunchKernelGGL((decode_attend_mfma<D>), dim3(a.B * a.Hkv * a.n_sel), dim3(256), 0, st, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L,
+                       a.n_sel, a.scale * 1.4426950408889634f);
+    hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(D), 0, st, part, (T *)a.o, a.n_sel);
+    return;
+  }
   int nsplit, bps;
   split_plan(a.B * a.Hkv, a.n_sel, &nsplit, &bps);
-  float *part = static_cast<float *>(a.ws);
   hipLaunchKernelGGL((decode_partial<T, D>), dim3(a.B * a.Hkv * nsplit), dim3(256), 0, st, (const T *)a.q,
                      (const T *)a.k_cache, (const T *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L, a.n_sel, nsplit, bps,
                      a.scale * 1.4426950408889634f);
@@ -189,9 +330,10 @@ void run(const SparseDecodeArgs &a, hipStream_t st) {
 }  // namespace
 
 size_t sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel) {
-  (void)dtype; (void)L; (void)block;
+  (void)L; (void)block;
   int nsplit, bps;
   split_plan(B * Hkv, n_sel, &nsplit, &bps);
+  if (dtype == 1 && Hq / Hkv <= 16) nsplit = n_sel;  // one split per selected block
   return (size_t)B * Hq * nsplit * (d + 2) * sizeof(float);
 }
 

@@ -16,6 +16,10 @@
 //   score_decode    decode scores: one pooled query against every pooled key block
 //   select_rows     per row: 4-pass radix select of the k-th largest fp32 key,
 //                   index-ordered tie break, then the ascending write-out
+//   score_decode_top64 + select_decode_final
+//                   decode with top-k <= 64: exact local top-64 per 256 blocks
+//                   (wave bitonic sort and merges), then a tree of top-64
+//                   merges per row -- no contended histogram atomics
 
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
@@ -315,6 +319,159 @@ __global__ __launch_bounds__(NT) void select_rows(const float *__restrict__ scor
   }
 }
 
+// ---------------------------------------------------------------- decode selection, two exact levels
+// Packed 64-bit candidate key: order-preserving score key in the high word,
+// inverted block index in the low word, so a larger key is a better block
+// and equal scores rank the smaller index first.  0 marks "not a candidate".
+__device__ __forceinline__ uint64_t pack_key(float score, int j) {
+  return ((uint64_t)float_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Descending bitonic sort of one key per lane across a wave.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor64(x, j);
+      const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+      x = keep_max ? (x > o ? x : o) : (x < o ? x : o);
+    }
+  return x;
+}
+// a (this lane's element of a descending list) and b[] (another descending
+// list of 64 in LDS): the top 64 of their union, descending.
+__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, const uint64_t *b, int lane) {
+  const uint64_t bb = b[63 - lane];
+  uint64_t x = a > bb ? a : bb;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t o = shfl_xor64(x, j);
+    x = ((lane & j) == 0) ? (x > o ? x : o) : (x < o ? x : o);
+  }
+  return x;
+}
+
+// Level 1: scores of 256 pooled blocks against the group-pooled query, and
+// their exact local top-64 (descending packed keys) written to tops.
+template <typename T, int d>
+__global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ q, const float *__restrict__ kbar,
+                                                          float *__restrict__ scores, uint64_t *__restrict__ tops,
+                                                          int Hq, int Hkv, int NB, float inv_sqrt_d, int lo,
+                                                          int hi) {
+  __shared__ float qm[128];
+  __shared__ float sc[256];
+  __shared__ uint64_t lists[3][64];
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  if (tid < d) {
+    float s = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const size_t off = ((size_t)(b * Hq + h * G + g)) * d + tid;
+      if constexpr (sizeof(T) == 2) s += bf16_to_f32(q[off]);
+      else s += q[off];
+    }
+    qm[tid] = s / (float)G;
+  }
+  __syncthreads();
+  const int grp = tid >> 3, l8 = tid & 7;
+  constexpr int nv = d / 32;  // float4 pieces per lane per pooled key
+  float qr[4 * nv];
+#pragma unroll
+  for (int vv = 0; vv < nv; ++vv)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qr[4 * vv + e] = qm[32 * vv + 4 * l8 + e];
+  const float *kb = kbar + (size_t)bh * NB * d;
+  const int j0 = blockIdx.x * 256;
+  // all 8 x nv loads of this lane in flight before any arithmetic
+  float4 xs[8][nv];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int j = min(j0 + grp + 32 * u, NB - 1);
+#pragma unroll
+    for (int vv = 0; vv < nv; ++vv) xs[u][vv] = *reinterpret_cast<const float4 *>(kb + (size_t)j * d + 32 * vv + 4 * l8);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float acc = 0.f;
+#pragma unroll
+    for (int vv = 0; vv < nv; ++vv) {
+      acc = fmaf(xs[u][vv].x, qr[4 * vv], acc);
+      acc = fmaf(xs[u][vv].y, qr[4 * vv + 1], acc);
+      acc = fmaf(xs[u][vv].z, qr[4 * vv + 2], acc);
+      acc = fmaf(xs[u][vv].w, qr[4 * vv + 3], acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    const int jl = grp + 32 * u;
+    if (l8 == 0) {
+      sc[jl] = acc * inv_sqrt_d;
+      if (scores && j0 + jl < NB) scores[(size_t)bh * NB + j0 + jl] = acc * inv_sqrt_d;
+    }
+  }
+  __syncthreads();
+  const int j = j0 + tid;
+  uint64_t key = (j >= lo && j <= hi) ? pack_key(sc[tid], j) : 0ull;
+  key = wave_sort_desc(key, lane);
+  if (w & 1) lists[w >> 1][lane] = key;  // waves 1 and 3 hand their lists over
+  __syncthreads();
+  if (w == 0 || w == 2) key = wave_merge_top(key, lists[w >> 1], lane);
+  if (w == 2) lists[2][lane] = key;
+  __syncthreads();
+  if (w == 0) {
+    key = wave_merge_top(key, lists[2], lane);
+    tops[((size_t)bh * gridDim.x + blockIdx.x) * 64 + lane] = key;
+  }
+}
+
+// Level 2 (one workgroup per row): the top 64 of a union is the top 64 of the
+// union of the parts' top 64s, so the row's sorted local lists are merged
+// pairwise (wave_merge_top) in a tree until one list is left; its first
+// min(topk, candidates) keys are the picks.  Output: forced low blocks,
+// picks ascending, forced high blocks, -1 padding.
+__global__ __launch_bounds__(1024) void select_decode_final(const uint64_t *__restrict__ tops, int32_t *__restrict__ idx,
+                                                            int nchunk, int topk, int n_init, int n_local, int i,
+                                                            int ncand) {
+  __shared__ uint64_t lists[2][64][64];
+  __shared__ uint32_t pick_idx[64];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t *t = tops + (size_t)row * nchunk * 64;
+  const int width = topk + n_init + n_local;
+  int32_t *out = idx + (size_t)row * width;
+  const int kk = min(topk, ncand);
+  int n = 1;
+  while (n < nchunk) n <<= 1;  // lists padded to a power of two with empty lists
+  for (int e = tid; e < n * 64; e += 1024) lists[0][e >> 6][e & 63] = (e >> 6) < nchunk ? t[e] : 0ull;
+  __syncthreads();
+  int cur = 0;
+  for (; n > 1; n >>= 1) {
+    for (int m = w; m < n / 2; m += 16)
+      lists[cur ^ 1][m][lane] = wave_merge_top(lists[cur][2 * m][lane], lists[cur][2 * m + 1], lane);
+    __syncthreads();
+    cur ^= 1;
+  }
+  if (tid < 64) pick_idx[tid] = 0xFFFFFFFFu - (uint32_t)(lists[cur][0][tid] & 0xFFFFFFFFull);
+  __syncthreads();
+  const int nlow = min(n_init, i + 1);
+  const int hstart = max(n_init, i - n_local + 1);
+  const int nhigh = max(0, i - hstart + 1);
+  if (tid < kk) {
+    const uint32_t me = pick_idx[tid];
+    int pos = 0;
+    for (int r = 0; r < kk; ++r) pos += pick_idx[r] < me;
+    out[nlow + pos] = (int32_t)me;
+  }
+  for (int x = tid; x < width; x += 1024) {
+    if (x < nlow) out[x] = x;
+    else if (x >= nlow + kk && x < nlow + kk + nhigh) out[x] = hstart + (x - nlow - kk);
+    else if (x >= nlow + kk + nhigh) out[x] = -1;
+  }
+}
+
 }  // namespace
 
 size_t sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk,
@@ -324,7 +481,11 @@ size_t sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq,
   const size_t NQB = (Nq == 1) ? 1 : (size_t)(Nq + block - 1) / block;
   size_t bytes = 0;
   if (Nq != 1) bytes += (size_t)B * Hkv * NQB * d * sizeof(float);             // qbar
-  if (!want_scores) bytes += (size_t)B * Hkv * NQB * NB * sizeof(float);       // scores
+  if (Nq == 1 && topk <= 64 && (NB + 255) / 256 * 64 <= 4096) {
+    bytes += (size_t)B * Hkv * ((NB + 255) / 256) * 64 * sizeof(uint64_t);    // local top-64 lists
+  } else if (!want_scores) {
+    bytes += (size_t)B * Hkv * NQB * NB * sizeof(float);                      // scores
+  }
   return bytes;
 }
 
@@ -356,6 +517,23 @@ hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
                        NB, a.d, inv_sqrt_d);
     hipLaunchKernelGGL((select_rows<256, 8192>), dim3(BH * NQB), dim3(256), 0, st, scores, a.idx, NQB, NB, a.L,
                        a.block, a.topk, a.n_init, a.n_local, -1);
+  } else if (a.topk <= 64 && (NB + 255) / 256 * 64 <= 4096) {
+    // two exact levels: local top-64 per 256 blocks, then threshold + rank per row
+    const int nchunk = (NB + 255) / 256;
+    uint64_t *tops = reinterpret_cast<uint64_t *>(ws);
+    const int i = (a.L - 1) / a.block;
+    const int lo = a.n_init, hi = min(i - a.n_local, a.L / a.block - 1);
+    const int ncand = max(0, hi - lo + 1);
+#define SALA_SCORE_TOP64(T, DD)                                                                                  \
+  hipLaunchKernelGGL((score_decode_top64<T, DD>), dim3(nchunk, BH), dim3(256), 0, st, (const T *)a.q, a.k_pooled,   \
+                     a.scores, tops, a.Hq, a.Hkv, NB, inv_sqrt_d, lo, hi)
+    if (a.dtype == 1 && a.d == 128) SALA_SCORE_TOP64(uint16_t, 128);
+    else if (a.dtype == 1) SALA_SCORE_TOP64(uint16_t, 64);
+    else if (a.d == 128) SALA_SCORE_TOP64(float, 128);
+    else SALA_SCORE_TOP64(float, 64);
+#undef SALA_SCORE_TOP64
+    hipLaunchKernelGGL(select_decode_final, dim3(BH), dim3(1024), 0, st, tops, a.idx, nchunk, a.topk, a.n_init,
+                       a.n_local, i, ncand);
   } else {
     if (a.dtype == 1)
       hipLaunchKernelGGL(score_decode<uint16_t>, dim3((NB + 255) / 256, BH), dim3(256), 0, st,
