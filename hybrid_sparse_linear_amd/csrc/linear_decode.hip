@@ -32,46 +32,48 @@ __global__ __launch_bounds__(256) void lin_decode(const T *__restrict__ q, const
   constexpr int CG = D / 32;      // column groups per (b, h)
   constexpr int RG = 32;          // row groups
   constexpr int RPT = D / RG;     // rows per thread
-  __shared__ float qs[D], ks[D];
   __shared__ float part[RG][33];
   const int bh = blockIdx.x / CG, cg = blockIdx.x % CG;
   const int h = bh % H, tid = threadIdx.x;
   const int cq = tid & 7, rg = tid >> 3;  // column quad 0..7, row group 0..31
-  const float lam = decay ? decay[h] : 1.f;
-  if (tid < D) {
-    qs[tid] = ld(q, (size_t)bh * D + tid);
-    ks[tid] = ld(k, (size_t)bh * D + tid);
-  }
   const int c0 = 32 * cg + 4 * cq;
-  float vv[4];
+  float *S = state + (size_t)bh * D * D;
+  // the state reads go out first; q, k, v (a few bytes, shared by many
+  // threads) follow without a barrier, so everything is one round trip
+  float4 s[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) s[r] = *reinterpret_cast<const float4 *>(S + (size_t)(rg + RG * r) * D + c0);
+  float qr[RPT], kr[RPT], vv[4];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    qr[r] = ld(q, (size_t)bh * D + rg + RG * r);
+    kr[r] = ld(k, (size_t)bh * D + rg + RG * r);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = ld(v, (size_t)bh * D + c0 + e);
-  __syncthreads();
-  float *S = state + (size_t)bh * D * D;
+  const float lam = decay ? decay[h] : 1.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
-    const int row = rg + RG * r;
-    float4 s = *reinterpret_cast<const float4 *>(S + (size_t)row * D + c0);
-    const float kr = ks[row], qr = qs[row];
-    s.x = fmaf(lam, s.x, kr * vv[0]);
-    s.y = fmaf(lam, s.y, kr * vv[1]);
-    s.z = fmaf(lam, s.z, kr * vv[2]);
-    s.w = fmaf(lam, s.w, kr * vv[3]);
-    *reinterpret_cast<float4 *>(S + (size_t)row * D + c0) = s;
-    acc[0] = fmaf(qr, s.x, acc[0]);
-    acc[1] = fmaf(qr, s.y, acc[1]);
-    acc[2] = fmaf(qr, s.z, acc[2]);
-    acc[3] = fmaf(qr, s.w, acc[3]);
+    float4 x = s[r];
+    x.x = fmaf(lam, x.x, kr[r] * vv[0]);
+    x.y = fmaf(lam, x.y, kr[r] * vv[1]);
+    x.z = fmaf(lam, x.z, kr[r] * vv[2]);
+    x.w = fmaf(lam, x.w, kr[r] * vv[3]);
+    *reinterpret_cast<float4 *>(S + (size_t)(rg + RG * r) * D + c0) = x;
+    acc[0] = fmaf(qr[r], x.x, acc[0]);
+    acc[1] = fmaf(qr[r], x.y, acc[1]);
+    acc[2] = fmaf(qr[r], x.z, acc[2]);
+    acc[3] = fmaf(qr[r], x.w, acc[3]);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) part[rg][4 * cq + e] = acc[e];
   __syncthreads();
   if (tid < 32) {
-    float s = 0.f;
+    float t = 0.f;
 #pragma unroll
-    for (int r = 0; r < RG; ++r) s += part[r][tid];
-    st(o, (size_t)bh * D + 32 * cg + tid, s);
+    for (int r = 0; r < RG; ++r) t += part[r][tid];
+    st(o, (size_t)bh * D + 32 * cg + tid, t);
   }
 }
 

@@ -171,10 +171,14 @@ __global__ __launch_bounds__(256) void decode_attend_mfma(const uint16_t *__rest
   const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int32_t *row = idx + (size_t)bkv * n_sel;
-  bool valid = true;
-  for (int x = 0; x <= e; ++x) valid = valid && row[x] >= 0;  // entries end at the first negative
+  // entries end at the first negative one: each wave checks 0..e itself, 64 at a time
   const int j = row[e];
-  valid = valid && (size_t)j * BLK < (size_t)L;
+  bool neg = false;
+  for (int x0 = 0; x0 <= e; x0 += 64) {
+    const int x = x0 + l;
+    if (x <= e && row[x] < 0) neg = true;
+  }
+  const bool valid = !__any(neg) && (size_t)j * BLK < (size_t)L;
   const int hh = tid >> 4, g = tid & 15;  // O = P V: head hh, columns DPG*g ..
   float *dst = part + ((size_t)(b * Hq + kvh * G + hh) * n_sel + e) * (D + 2);
   if (!valid) {  // an empty split: the combine gives it zero weight
@@ -262,41 +266,61 @@ __global__ __launch_bounds__(256) void decode_attend_mfma(const uint16_t *__rest
   }
 }
 
+// Log-sum-exp merge of the splits of one (b, hq): thread (column c, part p)
+// takes splits p, p + P, ... with all of its loads in flight at once (up to
+// CU splits per thread, else in rounds), then the P parts merge through LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine(const float *__restrict__ part, T *__restrict__ o, int nsplit) {
-  // log-sum-exp merge of the splits; loads are batched so they overlap
-  const int bh = blockIdx.x, c = threadIdx.x;
-  const float *p = part + (size_t)bh * nsplit * (D + 2);
-  constexpr int U = 8;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += U) {
-    float mm[U];
+__global__ __launch_bounds__(512) void decode_combine(const float *__restrict__ part, T *__restrict__ o, int nsplit) {
+  constexpr int P = 512 / D, CU = 24;
+  __shared__ float red_m[P][D], red_l[P][D], red_o[P][D];
+  const int bh = blockIdx.x, c = threadIdx.x % D, p = threadIdx.x / D;
+  const float *base = part + (size_t)bh * nsplit * (D + 2);
+  float M = -INFINITY, lsum = 0.f, acc = 0.f;
+  for (int s0 = p; s0 < nsplit; s0 += P * CU) {
+    float mm[CU], ll[CU], oo[CU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) mm[u] = (s0 + u < nsplit) ? p[(size_t)(s0 + u) * (D + 2) + D] : -INFINITY;
+    for (int u = 0; u < CU; ++u) {
+      const int sp = min(s0 + P * u, nsplit - 1);
+      const float *r = base + (size_t)sp * (D + 2);
+      mm[u] = r[D];
+      ll[u] = r[D + 1];
+      oo[u] = r[c];
+    }
+    float mnew = M;
 #pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
-  }
-  float lsum = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < nsplit; s0 += U) {
-      float mm[U], ll[U], oo[U];
+    for (int u = 0; u < CU; ++u)
+      if (s0 + P * u < nsplit) mnew = fmaxf(mnew, mm[u]);
+    if (mnew != -INFINITY) {
+      const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
+      lsum *= a;
+      acc *= a;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = s0 + u < nsplit;
-        const float *r = p + (size_t)(s0 + u) * (D + 2);
-        mm[u] = ok ? r[D] : -INFINITY;
-        ll[u] = ok ? r[D + 1] : 0.f;
-        oo[u] = ok ? r[c] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wgt = (mm[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm[u] - M);
+      for (int u = 0; u < CU; ++u) {
+        const float wgt = (s0 + P * u < nsplit && mm[u] != -INFINITY) ? __builtin_amdgcn_exp2f(mm[u] - mnew) : 0.f;
         lsum = fmaf(ll[u], wgt, lsum);
         acc = fmaf(oo[u], wgt, acc);
       }
+      M = mnew;
     }
   }
-  const float r = (lsum > 0.f) ? acc / lsum : 0.f;
+  red_m[p][c] = M;
+  red_l[p][c] = lsum;
+  red_o[p][c] = acc;
+  __syncthreads();
+  if (p != 0) return;
+  float Mall = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < P; ++x) Mall = fmaxf(Mall, red_m[x][c]);
+  float L = 0.f, A = 0.f;
+  if (Mall != -INFINITY) {
+#pragma unroll
+    for (int x = 0; x < P; ++x) {
+      const float wgt = (red_m[x][c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red_m[x][c] - Mall);
+      L = fmaf(red_l[x][c], wgt, L);
+      A = fmaf(red_o[x][c], wgt, A);
+    }
+  }
+  const float r = (L > 0.f) ? A / L : 0.f;
   if constexpr (sizeof(T) == 2) reinterpret_cast<uint16_t *>(o)[(size_t)bh * D + c] = f32_to_bf16(r);
   else o[(size_t)bh * D + c] = r;
 }
@@ -316,7 +340,7 @@ void run(const SparseDecodeArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((decode_attend_mfma<D>), dim3(a.B * a.Hkv * a.n_sel), dim3(256), 0, st, (const uint16_t *)a.q,
                        (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L,
                        a.n_sel, a.scale * 1.4426950408889634f);
-    hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(D), 0, st, part, (T *)a.o, a.n_sel);
+    hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(512), 0, st, part, (T *)a.o, a.n_sel);
     return;
   }
   int nsplit, bps;
@@ -324,7 +348,7 @@ void run(const SparseDecodeArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((decode_partial<T, D>), dim3(a.B * a.Hkv * nsplit), dim3(256), 0, st, (const T *)a.q,
                      (const T *)a.k_cache, (const T *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L, a.n_sel, nsplit, bps,
                      a.scale * 1.4426950408889634f);
-  hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(D), 0, st, part, (T *)a.o, nsplit);
+  hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(512), 0, st, part, (T *)a.o, nsplit);
 }
 
 }  // namespace

@@ -363,37 +363,63 @@ __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ 
                                                           int Hq, int Hkv, int NB, float inv_sqrt_d, int lo,
                                                           int hi) {
   __shared__ float qm[128];
+  __shared__ float qpart[256];
   __shared__ float sc[256];
   __shared__ uint64_t lists[3][64];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  if (tid < d) {
-    float s = 0.f;
-    for (int g = 0; g < G; ++g) {
-      const size_t off = ((size_t)(b * Hq + h * G + g)) * d + tid;
-      if constexpr (sizeof(T) == 2) s += bf16_to_f32(q[off]);
-      else s += q[off];
-    }
-    qm[tid] = s / (float)G;
-  }
-  __syncthreads();
   const int grp = tid >> 3, l8 = tid & 7;
   constexpr int nv = d / 32;  // float4 pieces per lane per pooled key
+  const float *kb = kbar + (size_t)bh * NB * d;
+  // block of local slot (u, grp): the u-th loads of all workgroups of a row
+  // cover one contiguous run of 32 * gridDim.x blocks, so the HBM channels see
+  // an even spread at every moment.  Any partition keeps the two levels exact.
+  const int nchunk = gridDim.x, x = blockIdx.x;
+  auto blk = [&](int u, int g) { return (u * nchunk + x) * 32 + g; };
+  // all 8 x nv pooled-key loads of this lane go out first, the query loads
+  // right behind them: one round trip for both
+  float4 xs[8][nv];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int j = min(blk(u, grp), NB - 1);
+#pragma unroll
+    for (int vv = 0; vv < nv; ++vv) xs[u][vv] = *reinterpret_cast<const float4 *>(kb + (size_t)j * d + 32 * vv + 4 * l8);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the key loads ahead of the query loads
+  constexpr int P = 256 / d;   // the G heads are split over P thread groups per dimension
+  constexpr int QPT = 32 / P;  // at most 32 heads per group
+  const int qc = tid % d, qp = tid / d;
+  float qv[QPT];
+  {
+    const T *qb = q + (size_t)(b * Hq + h * G) * d + qc;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int g = min(qp + P * i, G - 1);
+      if constexpr (sizeof(T) == 2) qv[i] = bf16_to_f32(qb[(size_t)g * d]);
+      else qv[i] = qb[(size_t)g * d];
+    }
+  }
+  {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) s += (qp + P * i < G) ? qv[i] : 0.f;
+    qpart[tid] = s;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  if (tid < d) {
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < 256 / d; ++p) s += qpart[p * d + tid];
+    qm[tid] = s / (float)G;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
   float qr[4 * nv];
 #pragma unroll
   for (int vv = 0; vv < nv; ++vv)
 #pragma unroll
     for (int e = 0; e < 4; ++e) qr[4 * vv + e] = qm[32 * vv + 4 * l8 + e];
-  const float *kb = kbar + (size_t)bh * NB * d;
-  const int j0 = blockIdx.x * 256;
-  // all 8 x nv loads of this lane in flight before any arithmetic
-  float4 xs[8][nv];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int j = min(j0 + grp + 32 * u, NB - 1);
-#pragma unroll
-    for (int vv = 0; vv < nv; ++vv) xs[u][vv] = *reinterpret_cast<const float4 *>(kb + (size_t)j * d + 32 * vv + 4 * l8);
-  }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     float acc = 0.f;
@@ -407,14 +433,14 @@ __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ 
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
     acc += __shfl_xor(acc, 4, 64);
-    const int jl = grp + 32 * u;
+    const int jl = grp + 32 * u, jg = blk(u, grp);
     if (l8 == 0) {
       sc[jl] = acc * inv_sqrt_d;
-      if (scores && j0 + jl < NB) scores[(size_t)bh * NB + j0 + jl] = acc * inv_sqrt_d;
+      if (scores && jg < NB) scores[(size_t)bh * NB + jg] = acc * inv_sqrt_d;
     }
   }
   __syncthreads();
-  const int j = j0 + tid;
+  const int j = blk(tid >> 5, tid & 31);
   uint64_t key = (j >= lo && j <= hi) ? pack_key(sc[tid], j) : 0ull;
   key = wave_sort_desc(key, lane);
   if (w & 1) lists[w >> 1][lane] = key;  // waves 1 and 3 hand their lists over
@@ -424,7 +450,7 @@ __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ 
   __syncthreads();
   if (w == 0) {
     key = wave_merge_top(key, lists[2], lane);
-    tops[((size_t)bh * gridDim.x + blockIdx.x) * 64 + lane] = key;
+    tops[((size_t)bh * nchunk + x) * 64 + lane] = key;
   }
 }
 
@@ -445,7 +471,19 @@ __global__ __launch_bounds__(1024) void select_decode_final(const uint64_t *__re
   const int kk = min(topk, ncand);
   int n = 1;
   while (n < nchunk) n <<= 1;  // lists padded to a power of two with empty lists
-  for (int e = tid; e < n * 64; e += 1024) lists[0][e >> 6][e & 63] = (e >> 6) < nchunk ? t[e] : 0ull;
+  {  // every load in flight at once (n * 64 <= 4096 keys, four per thread)
+    uint64_t tv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 1024 * u;
+      tv[u] = ((e >> 6) < nchunk) ? t[e] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 1024 * u;
+      if (e < n * 64) lists[0][e >> 6][e & 63] = tv[u];
+    }
+  }
   __syncthreads();
   int cur = 0;
   for (; n > 1; n >>= 1) {
