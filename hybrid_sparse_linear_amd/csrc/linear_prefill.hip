@@ -33,49 +33,49 @@ namespace {
 
 template <int C, int D>
 struct LinCfg {
-  static constexpr int NT = 512;                // 8 waves, two per SIMD
-  static constexpr int NQT = C / 16;            // 16-query tiles per chunk (one per wave at C = 128)
-  static constexpr int ND = D / 16;             // 16-wide feature tiles
-  static constexpr int NDS = D / 32;            // 32-deep steps over features
-  static constexpr int NKS = C / 32;            // 32-deep steps over chunk tokens
-  static constexpr int NDV = ND * ND / 8;       // state tiles per wave (one d_k tile row or half of one)
-  static constexpr int KCH = D / 8;             // 16-byte chunks per row of K_lds / St_lds
-  static constexpr int TCH = C / 8;             // 16-byte chunks per row of Kt_lds / Vt_lds
-  static constexpr int NB8 = (C / 8) * (D / 8); // 8x8 staging blocks per chunk (of K, and of V)
-  static constexpr uint32_t K_OFF = 0;
-  static constexpr uint32_t KT_OFF = K_OFF + C * D * 2;
-  static constexpr uint32_t VT_OFF = KT_OFF + C * D * 2;
-  static constexpr uint32_t ST_OFF = VT_OFF + C * D * 2;
-  static constexpr uint32_t PW_OFF = ST_OFF + D * D * 2;
-  static constexpr uint32_t LDS = PW_OFF + (C + 4) * 4;
-  static_assert(2 * NB8 <= NT, "one 8x8 staging block per thread at most");
-  // wave -> state tiles: d_k tile dkt(w), d_v tiles dv0(w) .. dv0(w)+NDV-1
-  __device__ static int dkt(int w) { return ND == 8 ? w : (w >> 1); }
-  __device__ static int dv0(int w) { return ND == 8 ? 0 : 2 * (w & 1); }
-  // wave -> query tile (-1: none).  Waves w and w+4 share a SIMD; pairing
-  // tiles w and 7-w balances the causal work per SIMD.
-  __device__ static int qtile(int w) {
-    if (NQT == 8) return w < 4 ? w : 11 - w;
-    return w < NQT ? w : -1;
+  static constexpr int NT = 512;               // 8 waves, two per SIMD
+  static constexpr int NCH = D / 8;            // 16-byte chunks per K / V / S^T row
+  static constexpr int ROWB = D * 2;           // bytes per row
+  static constexpr int ND = D / 16;            // 16-wide feature tiles
+  static constexpr int NDS = D / 32;           // 32-deep steps over features
+  static constexpr int NKS = C / 32;           // 32-deep steps over chunk tokens
+  static constexpr int NQP = C / 32;           // pairs of 16-query tiles per chunk
+  static constexpr int WPP = 8 / NQP;          // waves sharing one query pair (split over d_v)
+  static constexpr int DVW = ND / WPP;         // output d_v tiles per wave
+  static constexpr int SDV = ND * ND / 8;      // state tiles per wave (one d_k tile, SDV d_v tiles)
+  static constexpr int RPP = NT / NCH;         // K/V rows staged per pass of the workgroup
+  static constexpr int NSTG = C / RPP;         // staging passes (16-byte K and V pieces per thread)
+  static constexpr uint32_t KN = 0;                    // K, natural [token][d_k], swizzled
+  static constexpr uint32_t VN = KN + C * ROWB;        // V, natural [token][d_v], swizzled
+  static constexpr uint32_t ST = VN + C * ROWB;        // bf16 S^T [d_v][d_k], swizzled
+  static constexpr uint32_t PW = ST + D * ROWB;        // lam^n, n = 0..C
+  static constexpr uint32_t RW = PW + (C + 4) * 4;     // lam^(m-1-j) for the chunk's rows, 0 past m
+  static constexpr uint32_t LDS = RW + C * 4;
+  static_assert(DVW >= 1 && NSTG >= 1 && SDV >= 1, "unsupported chunk / head size");
+  // wave -> (query pair, d_v part).  Waves w and w+4 share a SIMD; they get
+  // query pairs from opposite ends of the chunk so the causal work per SIMD
+  // is even.
+  __device__ static void qrole(int w, int &gq, int &part) {
+    if (w < 4) {
+      gq = w % NQP;
+      part = w / NQP;
+    } else {
+      gq = NQP - 1 - (w - 4) % NQP;
+      part = WPP / 2 + (w - 4) / NQP;
+    }
   }
 };
 
-// XOR swizzles of 16-byte chunks inside an LDS row (bank-conflict avoidance).
-// swz_t: rows read 16 consecutive rows at one chunk, and written by 16 rows 8 apart.
-template <int NCH>
-__device__ __forceinline__ uint32_t swz_t(uint32_t row, uint32_t ch) {
-  return ch ^ ((row ^ (row >> 3)) & (NCH - 1));
+// K and V rows live in LDS in their natural layout with 16-byte chunks XOR-
+// swizzled by row.  fkv spreads both access patterns over all banks: the
+// plain 16-byte reads of 16 rows of one key pair (rows of pair_key below), and
+// the transposed 8-byte reads of rows k0 + 8g + 4h + r (the swizzle of those
+// rows depends on g and r only, so it is a per-lane constant).
+__device__ __forceinline__ uint32_t fkv(uint32_t row) {
+  return ((row & 3u) << 1) | (((row >> 3) & 1u) << 3) | ((row >> 4) & 1u);
 }
-// swz_k: K rows are read in the key order of the 32-key pair permutation below.
-template <int NCH>
-__device__ __forceinline__ uint32_t swz_k(uint32_t row, uint32_t ch) {
-  if constexpr (NCH == 16) return ch ^ ((row & 3) | ((row >> 1) & 12));
-  else return ch ^ (((row >> 1) & 1) | ((row >> 2) & 6));
-}
-template <int NCH>
-__device__ __forceinline__ uint32_t off_t(uint32_t row, uint32_t ch) { return (row * NCH + swz_t<NCH>(row, ch)) * 16u; }
-template <int NCH>
-__device__ __forceinline__ uint32_t off_k(uint32_t row, uint32_t ch) { return (row * NCH + swz_k<NCH>(row, ch)) * 16u; }
+// S^T rows are read 16 consecutive rows at one chunk.
+__device__ __forceinline__ uint32_t fst(uint32_t row) { return row ^ (row >> 3); }
 
 // Key permutation inside a 32-key pair of 16-key tiles: MFMA row r of tile t
 // (t = 0, 1) holds key 8*(r/4) + 4*t + r%4, so that after K Q^T each lane's
@@ -84,93 +84,87 @@ __device__ __forceinline__ uint32_t off_k(uint32_t row, uint32_t ch) { return (r
 // pair therefore hold keys from the whole 32-key range.
 __device__ __forceinline__ int pair_key(int t, int r) { return ((r >> 2) << 3) + (t << 2) + (r & 3); }
 
-// Transpose an 8x8 bf16 block: x[e] = row e (8 features, 4 dwords);
-// y[f] = feature f across the 8 rows.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&x)[8], u32x4 (&y)[8]) {
-#pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int p = f >> 1;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      uint32_t a = x[2 * qq][p], b = x[2 * qq + 1][p];
-      y[f][qq] = (f & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
+// gfx950 transposed LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte pieces read by lanes 4r + i/4,
+// r = 0..3, as its elements r.  So if lane 4r + c of group g reads the 4
+// columns m0+4c .. m0+4c+3 of row k0 + 8g + 4h + r of a k-major matrix, lane
+// i of group g receives column m0 + i at rows k0 + 8g + 4h + 0..3: half (h) of
+// the 16x32 MFMA operand fragment with m = i.  Two reads (h = 0, 1) give the
+// whole fragment.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const char *lds, uint32_t off) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds + off));
+  return __builtin_bit_cast(u32x2, v);
 }
-
-// Staging job of a thread: one 8x8 block of K (jobs 0 .. NB8-1) or of V
-// (jobs NB8 .. 2*NB8-1) of the chunk starting at token c0; rows at or past
-// t_end read as zero.
+// Fragment of a k-major LDS matrix at rows k0.., columns of tile `tile`:
+// base_k0 = buffer + k0 * ROWB; lane_tr, xtr: the per-lane constants above.
 template <int C, int D>
-__device__ __forceinline__ void load_block8(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end,
-                                            u32x4 (&x)[8]) {
+__device__ __forceinline__ u32x4 tr_frag(const char *lds, uint32_t base_k0, uint32_t lane_tr, uint32_t xtr,
+                                         int tile) {
   using Cf = LinCfg<C, D>;
-  if (tid >= 2 * Cf::NB8) return;
-  const bool is_v = tid >= Cf::NB8;
-  const int job = is_v ? tid - Cf::NB8 : tid;
-  const int tg = job / (D / 8), fg = job % (D / 8);
-  const uint16_t *src = is_v ? vb : kb;
-  // unconditional loads of clamped rows, then zero the rows past t_end
-  // (selects instead of a branch per load)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = c0 + 8 * tg + e;
-    x[e] = gload16(src + (size_t)min(t, t_end - 1) * D + 8 * fg);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (c0 + 8 * tg + e >= t_end) x[e] = u32x4{0, 0, 0, 0};
-  }
+  const uint32_t off = base_k0 + lane_tr + (((uint32_t)(2 * tile) ^ xtr) & (Cf::NCH - 1)) * 16u;
+  const u32x2 a = lds_read_tr(lds, off), b = lds_read_tr(lds, off + 4 * Cf::ROWB);
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// Write a staged block: K -> K_lds (row-major, when WITH_K) and Kt_lds
-// (transposed, row j scaled by lam^(m-1-j) in fp32 and rounded once);
-// V -> Vt_lds (transposed).
-template <int C, int D, bool WITH_K>
-__device__ __forceinline__ void stage_block8(char *lds, int tid, int m, const float *pw, u32x4 (&x)[8]) {
-  using Cf = LinCfg<C, D>;
-  if (tid >= 2 * Cf::NB8) return;
-  const bool is_v = tid >= Cf::NB8;
-  const int job = is_v ? tid - Cf::NB8 : tid;
-  const int tg = job / (D / 8), fg = job % (D / 8);
-  u32x4 y[8];
-  if (!is_v) {
-    if constexpr (WITH_K) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lds_store(lds + Cf::K_OFF, off_k<Cf::KCH>(8 * tg + e, fg), x[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * tg + e;
-      const float sc = (j < m) ? pw[m - 1 - j] : 0.f;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) x[e][p] = pack_bf16x2(bf16lo(x[e][p]) * sc, bf16hi(x[e][p]) * sc);
-    }
-    transpose8x8(x, y);
-#pragma unroll
-    for (int f = 0; f < 8; ++f) lds_store(lds + Cf::KT_OFF, off_t<Cf::TCH>(8 * fg + f, tg), y[f]);
-  } else {
-    transpose8x8(x, y);
-#pragma unroll
-    for (int f = 0; f < 8; ++f) lds_store(lds + Cf::VT_OFF, off_t<Cf::TCH>(8 * fg + f, tg), y[f]);
-  }
-}
-
-// State update S = lam^m S + (Kt scaled)^T V for this wave's state tiles.
+// K and V rows c0 .. c0+C-1 -> registers (thread: NSTG 16-byte pieces of each);
+// rows at or past t_end read as zero.
 template <int C, int D>
-__device__ __forceinline__ void state_update(const char *lds, int w, int lr, int lg, float lam_m,
-                                             f32x4 (&Sacc)[LinCfg<C, D>::NDV]) {
+__device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end,
+                                        u32x4 (&xk)[LinCfg<C, D>::NSTG], u32x4 (&xv)[LinCfg<C, D>::NSTG]) {
+  using Cf = LinCfg<C, D>;
+  const int ch = tid % Cf::NCH;
+#pragma unroll
+  for (int u = 0; u < Cf::NSTG; ++u) {
+    const int t = min(c0 + tid / Cf::NCH + Cf::RPP * u, t_end - 1);
+    xk[u] = gload16(kb + (size_t)t * D + 8 * ch);
+    xv[u] = gload16(vb + (size_t)t * D + 8 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < Cf::NSTG; ++u) {
+    if (c0 + tid / Cf::NCH + Cf::RPP * u >= t_end) {
+      xk[u] = u32x4{0, 0, 0, 0};
+      xv[u] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+template <int C, int D>
+__device__ __forceinline__ void store_kv(char *lds, int tid, const u32x4 (&xk)[LinCfg<C, D>::NSTG],
+                                         const u32x4 (&xv)[LinCfg<C, D>::NSTG]) {
+  using Cf = LinCfg<C, D>;
+  const uint32_t ch = tid % Cf::NCH;
+#pragma unroll
+  for (int u = 0; u < Cf::NSTG; ++u) {
+    const uint32_t row = tid / Cf::NCH + Cf::RPP * u;
+    const uint32_t off = row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
+    lds_store(lds + Cf::KN, off, xk[u]);
+    lds_store(lds + Cf::VN, off, xv[u]);
+  }
+}
+
+// State update for this wave's tiles (d_k tile sdk, d_v tiles sdv0 ..):
+//   S = lam^m S + (diag(lam^(m-1-j)) K)^T V
+// A = K^T fragments by transposed reads, scaled per token in fp32 and rounded
+// once to bf16; B = V fragments by transposed reads.
+template <int C, int D>
+__device__ __forceinline__ void state_update(const char *lds, int sdk, int sdv0, int g, uint32_t lane_tr,
+                                             uint32_t xtr, float lam_m, f32x4 (&Sacc)[LinCfg<C, D>::SDV]) {
   using Cf = LinCfg<C, D>;
 #pragma unroll
-  for (int a = 0; a < Cf::NDV; ++a) Sacc[a] *= lam_m;
+  for (int a = 0; a < Cf::SDV; ++a) Sacc[a] *= lam_m;
 #pragma unroll
   for (int ks = 0; ks < Cf::NKS; ++ks) {
-    const u32x4 A = lds_load<u32x4>(lds + Cf::KT_OFF, off_t<Cf::TCH>(16 * Cf::dkt(w) + lr, 4 * ks + lg));
+    u32x4 A = tr_frag<C, D>(lds, Cf::KN + 32 * ks * Cf::ROWB, lane_tr, xtr, sdk);
+    const f32x4 w0 = lds_load<f32x4>(lds + Cf::RW, (32 * ks + 8 * g) * 4);
+    const f32x4 w1 = lds_load<f32x4>(lds + Cf::RW, (32 * ks + 8 * g + 4) * 4);
+    A[0] = pack_bf16x2(bf16lo(A[0]) * w0[0], bf16hi(A[0]) * w0[1]);
+    A[1] = pack_bf16x2(bf16lo(A[1]) * w0[2], bf16hi(A[1]) * w0[3]);
+    A[2] = pack_bf16x2(bf16lo(A[2]) * w1[0], bf16hi(A[2]) * w1[1]);
+    A[3] = pack_bf16x2(bf16lo(A[3]) * w1[2], bf16hi(A[3]) * w1[3]);
 #pragma unroll
-    for (int a = 0; a < Cf::NDV; ++a) {
-      const u32x4 Bv = lds_load<u32x4>(lds + Cf::VT_OFF, off_t<Cf::TCH>(16 * (Cf::dv0(w) + a) + lr, 4 * ks + lg));
-      Sacc[a] = mfma16x16x32(A, Bv, Sacc[a]);
-    }
+    for (int a = 0; a < Cf::SDV; ++a)
+      Sacc[a] = mfma16x16x32(A, tr_frag<C, D>(lds, Cf::VN + 32 * ks * Cf::ROWB, lane_tr, xtr, sdv0 + a), Sacc[a]);
   }
 }
 
@@ -183,37 +177,40 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
                                                          int seg_len, int nseg) {
   using Cf = LinCfg<C, D>;
   __shared__ __attribute__((aligned(16))) char lds[Cf::LDS];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
   const int nagg = nseg - 1;
   const int bh = blockIdx.x / nagg, seg = blockIdx.x % nagg;
   const int h = bh % H;
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
-  float *pw = reinterpret_cast<float *>(lds + Cf::PW_OFF);
+  float *pw = reinterpret_cast<float *>(lds + Cf::PW);
+  float *rw = reinterpret_cast<float *>(lds + Cf::RW);
   for (int n = tid; n <= C; n += Cf::NT) pw[n] = (float)pow((double)lam, (double)n);
   const uint16_t *kb = k + (size_t)bh * N * D;
   const uint16_t *vb = v + (size_t)bh * N * D;
+  const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
+  const uint32_t r4 = lr >> 2, c4 = l & 3;
+  const uint32_t lane_tr = (8 * g + r4) * Cf::ROWB + (c4 & 1) * 8, xtr = (c4 >> 1) ^ fkv(8 * g + r4);
 
-  f32x4 Sacc[Cf::NDV];
+  f32x4 Sacc[Cf::SDV];
 #pragma unroll
-  for (int a = 0; a < Cf::NDV; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 x[8];
-  load_block8<C, D>(kb, vb, tid, t_begin, t_end, x);
+  for (int a = 0; a < Cf::SDV; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
+  load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    stage_block8<C, D, false>(lds, tid, m, pw, x);
+    store_kv<C, D>(lds, tid, xk, xv);
+    if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
     __syncthreads();
-    if (c0 + C < t_end) load_block8<C, D>(kb, vb, tid, c0 + C, t_end, x);
-    state_update<C, D>(lds, w, lr, lg, pw[m], Sacc);
+    if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
+    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
   }
   float *out = seg_state + ((size_t)bh * nseg + seg) * D * D;
 #pragma unroll
-  for (int a = 0; a < Cf::NDV; ++a)
+  for (int a = 0; a < Cf::SDV; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out[(size_t)(16 * Cf::dkt(w) + 4 * lg + i) * D + 16 * (Cf::dv0(w) + a) + lr] = Sacc[a][i];
+    for (int i = 0; i < 4; ++i) out[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] = Sacc[a][i];
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -249,117 +246,143 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
                                                       int H, int N, int seg_len, int nseg) {
   using Cf = LinCfg<C, D>;
   __shared__ __attribute__((aligned(16))) char lds[Cf::LDS];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
   const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const int h = bh % H;
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
-  float *pw = reinterpret_cast<float *>(lds + Cf::PW_OFF);
+  float *pw = reinterpret_cast<float *>(lds + Cf::PW);
+  float *rw = reinterpret_cast<float *>(lds + Cf::RW);
   for (int n = tid; n <= C; n += Cf::NT) pw[n] = (float)pow((double)lam, (double)n);
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t *qb = q + head_off, *kb = k + head_off, *vb = v + head_off;
   uint16_t *ob = o + head_off;
-  const int qt = Cf::qtile(w);
-  const int dkt = Cf::dkt(w), dv0 = Cf::dv0(w);
+  int gq, part;
+  Cf::qrole(w, gq, part);
+  const int dvb = part * Cf::DVW;  // first output d_v tile of this wave
+  const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
+  const uint32_t r4 = lr >> 2, c4 = l & 3;
+  const uint32_t lane_tr = (8 * g + r4) * Cf::ROWB + (c4 & 1) * 8, xtr = (c4 >> 1) ^ fkv(8 * g + r4);
 
-  f32x4 Sacc[Cf::NDV];
+  f32x4 Sacc[Cf::SDV];
   const float *sin = seg_state ? seg_state + (size_t)bh * seg_stride * nseg + (size_t)seg * seg_stride : nullptr;
 #pragma unroll
-  for (int a = 0; a < Cf::NDV; ++a)
+  for (int a = 0; a < Cf::SDV; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      Sacc[a][i] = sin ? sin[(size_t)(16 * dkt + 4 * lg + i) * D + 16 * (dv0 + a) + lr] : 0.f;
+      Sacc[a][i] = sin ? sin[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] : 0.f;
 
-  u32x4 x[8];
-  u32x4 qf[Cf::NDS];
-  auto load_q = [&](int c0, u32x4 (&dst)[Cf::NDS]) {
-    // rows past t_end load a clamped row; their outputs are never stored
-    const int t = min(c0 + 16 * max(qt, 0) + lr, t_end - 1);
+  // Q fragments (B operands of Q^T): query tiles 2gq, 2gq+1 of the chunk;
+  // rows past t_end load a clamped row whose outputs are never stored
+  u32x4 qf[2][Cf::NDS];
+  auto load_q = [&](int c0) {
 #pragma unroll
-    for (int s = 0; s < Cf::NDS; ++s) dst[s] = gload16(qb + (size_t)t * D + 32 * s + 8 * lg);
+    for (int tq = 0; tq < 2; ++tq) {
+      const int t = min(c0 + 32 * gq + 16 * tq + lr, t_end - 1);
+#pragma unroll
+      for (int s = 0; s < Cf::NDS; ++s) qf[tq][s] = gload16(qb + (size_t)t * D + 32 * s + 8 * g);
+    }
   };
-  load_block8<C, D>(kb, vb, tid, t_begin, t_end, x);
-  load_q(t_begin, qf);
+  u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
+  load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
+  load_q(t_begin);
 
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    stage_block8<C, D, true>(lds, tid, m, pw, x);
+    store_kv<C, D>(lds, tid, xk, xv);
     // bf16 copy of S^T (rows d_v, columns d_k) for the Q S product
 #pragma unroll
-    for (int a = 0; a < Cf::NDV; ++a) {
-      const int row = 16 * (dv0 + a) + lr;
-      const uint32_t off = off_t<Cf::KCH>(row, 2 * dkt + (lg >> 1)) + (lg & 1) * 8;
-      lds_store(lds + Cf::ST_OFF, off, u32x2{pack_bf16x2(Sacc[a][0], Sacc[a][1]), pack_bf16x2(Sacc[a][2], Sacc[a][3])});
+    for (int a = 0; a < Cf::SDV; ++a) {
+      const uint32_t row = 16 * (sdv0 + a) + lr;
+      const uint32_t off = row * Cf::ROWB + (((2 * sdk + (g >> 1)) ^ fst(row)) & (Cf::NCH - 1)) * 16u + (g & 1) * 8;
+      lds_store(lds + Cf::ST, off, u32x2{pack_bf16x2(Sacc[a][0], Sacc[a][1]), pack_bf16x2(Sacc[a][2], Sacc[a][3])});
     }
+    if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
     __syncthreads();
-    u32x4 qn[Cf::NDS];
-    if (c0 + C < t_end) {
-      load_block8<C, D>(kb, vb, tid, c0 + C, t_end, x);
-      load_q(c0 + C, qn);
-    }
+    if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
 
-    if (qt >= 0) {
-      const int qq = 16 * qt + lr;  // this lane's query inside the chunk
-      // (1) O^T = lam^(qq+1) * S^T Q^T
-      f32x4 Oacc[Cf::ND];
-#pragma unroll 2
-      for (int dv = 0; dv < Cf::ND; ++dv) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // (1) O^T = lam^(qq+1) * S^T Q^T for d_v tiles dvb .. and both query tiles
+    f32x4 Oacc[Cf::DVW][2];
 #pragma unroll
-        for (int s = 0; s < Cf::NDS; ++s)
-          acc = mfma16x16x32(lds_load<u32x4>(lds + Cf::ST_OFF, off_t<Cf::KCH>(16 * dv + lr, 4 * s + lg)), qf[s], acc);
-        Oacc[dv] = acc * pw[qq + 1];
+    for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t row = 16 * (dvb + dvi) + lr;
+#pragma unroll
+      for (int s = 0; s < Cf::NDS; ++s) {
+        const u32x4 A = lds_load<u32x4>(lds + Cf::ST, row * Cf::ROWB + (((4 * s + g) ^ fst(row)) & (Cf::NCH - 1)) * 16u);
+        a0 = mfma16x16x32(A, qf[0][s], a0);
+        a1 = mfma16x16x32(A, qf[1][s], a1);
       }
-      // (2)+(3) P^T = decay-masked K Q^T over the causal key pairs; O^T += V^T P^T
-      for (int p = 0; p <= (qt >> 1); ++p) {
-        f32x4 P0 = {0.f, 0.f, 0.f, 0.f}, P1 = {0.f, 0.f, 0.f, 0.f};
+      Oacc[dvi][0] = a0;
+      Oacc[dvi][1] = a1;
+    }
 #pragma unroll
-        for (int s = 0; s < Cf::NDS; ++s) {
-          const u32x4 A0 = lds_load<u32x4>(lds + Cf::K_OFF, off_k<Cf::KCH>(32 * p + pair_key(0, lr), 4 * s + lg));
-          const u32x4 A1 = lds_load<u32x4>(lds + Cf::K_OFF, off_k<Cf::KCH>(32 * p + pair_key(1, lr), 4 * s + lg));
-          P0 = mfma16x16x32(A0, qf[s], P0);
-          P1 = mfma16x16x32(A1, qf[s], P1);
+    for (int tq = 0; tq < 2; ++tq) {
+      const float f = pw[32 * gq + 16 * tq + lr + 1];
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi][tq] *= f;
+    }
+    // (2)+(3) P^T = decay-masked K Q^T over the causal key pairs; O^T += V^T P^T
+    for (int p = 0; p <= gq; ++p) {
+      f32x4 P[2][2];
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) P[tq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < Cf::NDS; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t row = 32 * p + pair_key(t, lr);
+          const u32x4 A = lds_load<u32x4>(lds + Cf::KN, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
+          P[0][t] = mfma16x16x32(A, qf[0][s], P[0][t]);
+          P[1][t] = mfma16x16x32(A, qf[1][s], P[1][t]);
         }
-        const int j0 = 32 * p + 8 * lg;
+      u32x4 Bp[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ja = j0 + i, jb = j0 + 4 + i;
-          P0[i] = (ja <= qq) ? P0[i] * pw[qq - ja] : 0.f;
-          P1[i] = (jb <= qq) ? P1[i] * pw[qq - jb] : 0.f;
-        }
-        const u32x4 Bp = {pack_bf16x2(P0[0], P0[1]), pack_bf16x2(P0[2], P0[3]), pack_bf16x2(P1[0], P1[1]),
-                          pack_bf16x2(P1[2], P1[3])};
+      for (int tq = 0; tq < 2; ++tq) {
+        const int qq = 32 * gq + 16 * tq + lr;
 #pragma unroll
-        for (int dv = 0; dv < Cf::ND; ++dv)
-          Oacc[dv] = mfma16x16x32(lds_load<u32x4>(lds + Cf::VT_OFF, off_t<Cf::TCH>(16 * dv + lr, 4 * p + lg)), Bp,
-                                  Oacc[dv]);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 32 * p + 8 * g + 4 * t + i;
+            P[tq][t][i] = (j <= qq) ? P[tq][t][i] * pw[max(qq - j, 0)] : 0.f;
+          }
+        Bp[tq] = u32x4{pack_bf16x2(P[tq][0][0], P[tq][0][1]), pack_bf16x2(P[tq][0][2], P[tq][0][3]),
+                       pack_bf16x2(P[tq][1][0], P[tq][1][1]), pack_bf16x2(P[tq][1][2], P[tq][1][3])};
       }
-      // (4) write this lane's output row
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        const u32x4 A = tr_frag<C, D>(lds, Cf::VN + 32 * p * Cf::ROWB, lane_tr, xtr, dvb + dvi);
+        Oacc[dvi][0] = mfma16x16x32(A, Bp[0], Oacc[dvi][0]);
+        Oacc[dvi][1] = mfma16x16x32(A, Bp[1], Oacc[dvi][1]);
+      }
+    }
+    if (c0 + C < t_end) load_q(c0 + C);  // the Q fragments are free from here on
+    // (4) this lane's output rows
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) {
+      const int qq = 32 * gq + 16 * tq + lr;
       if (qq < m) {
         uint16_t *orow = ob + (size_t)(c0 + qq) * D;
 #pragma unroll
-        for (int dv = 0; dv < Cf::ND; ++dv)
-          *reinterpret_cast<u32x2 *>(orow + 16 * dv + 4 * lg) =
-              u32x2{pack_bf16x2(Oacc[dv][0], Oacc[dv][1]), pack_bf16x2(Oacc[dv][2], Oacc[dv][3])};
+        for (int dvi = 0; dvi < Cf::DVW; ++dvi)
+          *reinterpret_cast<u32x2 *>(orow + 16 * (dvb + dvi) + 4 * g) =
+              u32x2{pack_bf16x2(Oacc[dvi][tq][0], Oacc[dvi][tq][1]), pack_bf16x2(Oacc[dvi][tq][2], Oacc[dvi][tq][3])};
       }
     }
-
     // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V
-    state_update<C, D>(lds, w, lr, lg, pw[m], Sacc);
-
-    if (c0 + C < t_end) {
-#pragma unroll
-      for (int s = 0; s < Cf::NDS; ++s) qf[s] = qn[s];
-    }
+    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
   }
 
   if (state_out && seg == nseg - 1) {
     float *so = state_out + (size_t)bh * D * D;
 #pragma unroll
-    for (int a = 0; a < Cf::NDV; ++a)
+    for (int a = 0; a < Cf::SDV; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) so[(size_t)(16 * dkt + 4 * lg + i) * D + 16 * (dv0 + a) + lr] = Sacc[a][i];
+      for (int i = 0; i < 4; ++i) so[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] = Sacc[a][i];
   }
 }
 
