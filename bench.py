@@ -135,7 +135,7 @@ def bench_decode(torch, sala, I, reps=20):
     q = sp["q"]
     q4 = q[:, :, None].contiguous()
     idx, kp = sala.sparse_select(q4, sp["k_cache"])  # pooled cache built once, outside the timed region
-    ws_sel = torch.empty(sala.workspace_bytes("sparse_select", dtype=1, B=4, Hq=32, Hkv=2, d=128, Nq=1, L=L,
+    ws_sel = torch.zeros(sala.workspace_bytes("sparse_select", dtype=1, B=4, Hq=32, Hkv=2, d=128, Nq=1, L=L,
                                               block=64, topk=64, n_init=1, n_local=2), dtype=torch.uint8,
                          device="cuda")
     ws_att = torch.empty(sala.workspace_bytes("sparse_decode", dtype=1, B=4, Hq=32, Hkv=2, L=L, d=128, block=64,
@@ -211,7 +211,7 @@ def main():
     nqb = (N + 63) // 64
     idx = torch.empty((1, Hkv, nqb, 67), dtype=torch.int32, device="cuda")
     kp = torch.empty((1, Hkv, nqb, d), dtype=torch.float32, device="cuda")
-    ws_sel = torch.empty(sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N,
+    ws_sel = torch.zeros(sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N,
                                               block=64, topk=64, n_init=1, n_local=2), dtype=torch.uint8,
                          device="cuda")
     ws_att = torch.empty(sala.workspace_bytes("sparse_prefill", dtype=1, B=1, Hq=Hq, Hkv=Hkv, N=N, d=d, block=64,

@@ -67,49 +67,21 @@ struct LinCfg {
 };
 
 // K and V rows live in LDS in their natural layout with 16-byte chunks XOR-
-// swizzled by row.  fkv spreads both access patterns over all banks: the
-// plain 16-byte reads of 16 rows of one key pair (rows of pair_key below), and
-// the transposed 8-byte reads of rows k0 + 8g + 4h + r (the swizzle of those
-// rows depends on g and r only, so it is a per-lane constant).
-__device__ __forceinline__ uint32_t fkv(uint32_t row) {
-  return ((row & 3u) << 1) | (((row >> 3) & 1u) << 3) | ((row >> 4) & 1u);
-}
+// swizzled by row (fkv): conflict-free for the plain 16-byte reads of 16 rows
+// of one key pair and for the transposed reads (lds_read_tr).
 // S^T rows are read 16 consecutive rows at one chunk.
 __device__ __forceinline__ uint32_t fst(uint32_t row) { return row ^ (row >> 3); }
 
-// Key permutation inside a 32-key pair of 16-key tiles: MFMA row r of tile t
-// (t = 0, 1) holds key 8*(r/4) + 4*t + r%4, so that after K Q^T each lane's
-// 4+4 accumulator rows of the two tiles are 8 consecutive keys -- exactly the
-// k slots of the B operand of the following V^T P^T product.  Both tiles of a
-// pair therefore hold keys from the whole 32-key range.
-__device__ __forceinline__ int pair_key(int t, int r) { return ((r >> 2) << 3) + (t << 2) + (r & 3); }
-
-// gfx950 transposed LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes,
-// lane i receives element i%4 of the 8-byte pieces read by lanes 4r + i/4,
-// r = 0..3, as its elements r.  So if lane 4r + c of group g reads the 4
-// columns m0+4c .. m0+4c+3 of row k0 + 8g + 4h + r of a k-major matrix, lane
-// i of group g receives column m0 + i at rows k0 + 8g + 4h + 0..3: half (h) of
-// the 16x32 MFMA operand fragment with m = i.  Two reads (h = 0, 1) give the
-// whole fragment.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_read_tr(const char *lds, uint32_t off) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds + off));
-  return __builtin_bit_cast(u32x2, v);
-}
-// Fragment of a k-major LDS matrix at rows k0.., columns of tile `tile`:
-// base_k0 = buffer + k0 * ROWB; lane_tr, xtr: the per-lane constants above.
 template <int C, int D>
 __device__ __forceinline__ u32x4 tr_frag(const char *lds, uint32_t base_k0, uint32_t lane_tr, uint32_t xtr,
                                          int tile) {
-  using Cf = LinCfg<C, D>;
-  const uint32_t off = base_k0 + lane_tr + (((uint32_t)(2 * tile) ^ xtr) & (Cf::NCH - 1)) * 16u;
-  const u32x2 a = lds_read_tr(lds, off), b = lds_read_tr(lds, off + 4 * Cf::ROWB);
-  return u32x4{a[0], a[1], b[0], b[1]};
+  return sala::tr_frag(lds, base_k0, lane_tr, xtr, tile, LinCfg<C, D>::NCH, LinCfg<C, D>::ROWB);
 }
 
-// K and V rows c0 .. c0+C-1 -> registers (thread: NSTG 16-byte pieces of each);
-// rows at or past t_end read as zero.
+// K and V rows c0 .. c0+C-1 -> registers (thread: NSTG 16-byte pieces of
+// each).  Rows at or past t_end load a clamped row; store_kv zeroes them.
+// Nothing here uses the loaded values, so the loads stay in flight until
+// store_kv of the next chunk step.
 template <int C, int D>
 __device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end,
                                         u32x4 (&xk)[LinCfg<C, D>::NSTG], u32x4 (&xv)[LinCfg<C, D>::NSTG]) {
@@ -121,25 +93,22 @@ __device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, 
     xk[u] = gload16(kb + (size_t)t * D + 8 * ch);
     xv[u] = gload16(vb + (size_t)t * D + 8 * ch);
   }
-#pragma unroll
-  for (int u = 0; u < Cf::NSTG; ++u) {
-    if (c0 + tid / Cf::NCH + Cf::RPP * u >= t_end) {
-      xk[u] = u32x4{0, 0, 0, 0};
-      xv[u] = u32x4{0, 0, 0, 0};
-    }
-  }
 }
+// Registers -> K_lds / V_lds (natural layout, fkv-swizzled); chunk rows at or
+// past m are written as zero.
 template <int C, int D>
-__device__ __forceinline__ void store_kv(char *lds, int tid, const u32x4 (&xk)[LinCfg<C, D>::NSTG],
+__device__ __forceinline__ void store_kv(char *lds, int tid, int m, const u32x4 (&xk)[LinCfg<C, D>::NSTG],
                                          const u32x4 (&xv)[LinCfg<C, D>::NSTG]) {
   using Cf = LinCfg<C, D>;
   const uint32_t ch = tid % Cf::NCH;
+  const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < Cf::NSTG; ++u) {
     const uint32_t row = tid / Cf::NCH + Cf::RPP * u;
     const uint32_t off = row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
-    lds_store(lds + Cf::KN, off, xk[u]);
-    lds_store(lds + Cf::VN, off, xv[u]);
+    const bool live = (int)row < m;
+    lds_store(lds + Cf::KN, off, live ? xk[u] : zero);
+    lds_store(lds + Cf::VN, off, live ? xv[u] : zero);
   }
 }
 
@@ -189,8 +158,7 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
   const uint16_t *kb = k + (size_t)bh * N * D;
   const uint16_t *vb = v + (size_t)bh * N * D;
   const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
-  const uint32_t r4 = lr >> 2, c4 = l & 3;
-  const uint32_t lane_tr = (8 * g + r4) * Cf::ROWB + (c4 & 1) * 8, xtr = (c4 >> 1) ^ fkv(8 * g + r4);
+  const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
 
   f32x4 Sacc[Cf::SDV];
 #pragma unroll
@@ -200,7 +168,7 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    store_kv<C, D>(lds, tid, xk, xv);
+    store_kv<C, D>(lds, tid, m, xk, xv);
     if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
     __syncthreads();
     if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
@@ -261,8 +229,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   Cf::qrole(w, gq, part);
   const int dvb = part * Cf::DVW;  // first output d_v tile of this wave
   const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
-  const uint32_t r4 = lr >> 2, c4 = l & 3;
-  const uint32_t lane_tr = (8 * g + r4) * Cf::ROWB + (c4 & 1) * 8, xtr = (c4 >> 1) ^ fkv(8 * g + r4);
+  const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
 
   f32x4 Sacc[Cf::SDV];
   const float *sin = seg_state ? seg_state + (size_t)bh * seg_stride * nseg + (size_t)seg * seg_stride : nullptr;
@@ -290,7 +257,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    store_kv<C, D>(lds, tid, xk, xv);
+    store_kv<C, D>(lds, tid, m, xk, xv);
     // bf16 copy of S^T (rows d_v, columns d_k) for the Q S product
 #pragma unroll
     for (int a = 0; a < Cf::SDV; ++a) {

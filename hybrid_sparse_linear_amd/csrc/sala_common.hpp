@@ -49,6 +49,54 @@ __device__ __forceinline__ void lds_store(void *base, uint32_t byte_off, const T
   *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off) = v;
 }
 
+// gfx950 transposed LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte pieces read by lanes 4r + i/4,
+// r = 0..3, as its elements r.  So if lane 4r + c of group g reads the 4
+// columns m0+4c .. m0+4c+3 of row k0 + 8g + 4h + r of a k-major bf16 matrix,
+// lane i of group g receives column m0 + i at rows k0 + 8g + 4h + 0..3: half
+// (h) of the 16x32 MFMA operand fragment with m = i.  Two reads (h = 0, 1)
+// give the whole fragment.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const void *lds, uint32_t byte_off) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(reinterpret_cast<const char *>(lds) + byte_off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Row swizzle of 16-byte chunks for row-major bf16 tiles in LDS that are read
+// both as plain 16-byte operand rows and with lds_read_tr: spreads 16 rows of
+// a 32-key pair (see pair_key) and the transposed reads of rows k0 + 8g + 4h
+// + r over all banks.  For those transposed reads it depends on g and r only.
+__device__ __forceinline__ uint32_t fkv(uint32_t row) {
+  return ((row & 3u) << 1) | (((row >> 3) & 1u) << 3) | ((row >> 4) & 1u);
+}
+// Per-lane constants of a transposed fragment read (lane l = 16g + 4r + c):
+// byte offset of its row and 8-byte half, and the XOR applied to the tile's
+// chunk index.
+__device__ __forceinline__ uint32_t tr_lane_off(int l, int rowb) {
+  return (8 * (l >> 4) + ((l & 15) >> 2)) * rowb + (l & 1) * 8;
+}
+__device__ __forceinline__ uint32_t tr_lane_xor(int l) {
+  return (((l & 3) >> 1) ^ fkv(8 * (l >> 4) + ((l & 15) >> 2)));
+}
+// 16x32 operand fragment (m = 16 columns of tile `tile`, k = 32 rows from the
+// row whose byte offset is base_k0) of a k-major, fkv-swizzled LDS matrix with
+// nch 16-byte chunks per row.
+__device__ __forceinline__ u32x4 tr_frag(const void *lds, uint32_t base_k0, uint32_t lane_off, uint32_t lane_xor,
+                                         int tile, int nch, int rowb) {
+  const uint32_t off = base_k0 + lane_off + (((uint32_t)(2 * tile) ^ lane_xor) & (uint32_t)(nch - 1)) * 16u;
+  const u32x2 a = lds_read_tr(lds, off), b = lds_read_tr(lds, off + 4 * rowb);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Key permutation inside a 32-key pair of 16-key tiles: MFMA row r of tile t
+// (t = 0, 1) holds key 8*(r/4) + 4*t + r%4, so that after K Q^T each lane's
+// 4+4 accumulator rows of the two tiles are 8 consecutive keys -- exactly the
+// k slots of the B operand of a following V^T P^T product.  Both tiles of a
+// pair therefore hold keys from the whole 32-key range.
+__device__ __forceinline__ int pair_key(int t, int r) { return ((r >> 2) << 3) + (t << 2) + (r & 3); }
+
 // ---------------------------------------------------------------- global access
 __device__ __forceinline__ u32x4 gload16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void gstore16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }

@@ -8,8 +8,8 @@
 // query heads of that group (one gathered block feeds G heads) and writes
 // (max, sum, unnormalised o) per head in log2 units; decode_combine merges the
 // splits with the usual log-sum-exp rescaling.  bf16 with G <= 16 uses
-// decode_attend_mfma (one block per workgroup, logits on MFMA); other cases
-// use decode_partial (fp32 VALU, a few blocks per workgroup).
+// decode_attend_mfma (one wave per selected block, both products on MFMA);
+// other cases use decode_partial (fp32 VALU, a few blocks per workgroup).
 
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
@@ -148,30 +148,27 @@ __global__ __launch_bounds__(256) void decode_partial(const T *__restrict__ q, c
   }
 }
 
-// bf16, G <= 16: one workgroup per (b, kv head, entry e of the selected list).
-// Wave w takes keys 16w .. 16w+15 of the block: S^T = K Q^T on one MFMA
-// 16x16x32 tile per d-step (A = 16 keys, B = the group's <= 16 query heads,
-// both loaded straight into operand registers).  Softmax pieces for the 64
-// keys go through LDS; O = P V runs on the VALU from V staged in LDS.
-// Writes (o unnormalised, max, sum) per head in log2 units for the combine.
+// bf16, G <= 16: one wave per (b, kv head, entry e of the selected list).
+// S^T = K Q^T for the block's 64 keys on MFMA (A = K rows in the 32-key pair
+// order, loaded straight into registers; B = the group's <= 16 query heads),
+// so each lane's accumulators are 8 consecutive keys of one head -- the B
+// operand of O^T = V^T P^T.  Softmax over the 64 keys stays in registers
+// (two cross-lane steps); V goes to LDS row-major by direct loads and its
+// V^T fragments come from transposed LDS reads.  Writes (o unnormalised,
+// max, sum) per head in log2 units for the combine.
 template <int D>
-__global__ __launch_bounds__(256) void decode_attend_mfma(const uint16_t *__restrict__ q,
-                                                          const uint16_t *__restrict__ kc,
-                                                          const uint16_t *__restrict__ vc,
-                                                          const int32_t *__restrict__ idx, float *__restrict__ part,
-                                                          int Hq, int Hkv, int L, int n_sel, float scale_log2) {
-  constexpr int NDS = D / 32;
-  constexpr int VS = D + 8;        // padded V row (elements)
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int DPG = D / 16;      // d_v columns per thread in O = P V
-  __shared__ __attribute__((aligned(16))) uint16_t vs[BLK * VS];
-  __shared__ float ps[16][BLK + 4];
-  __shared__ float red_m[4][16], red_l[4][16];
+__global__ __launch_bounds__(64) void decode_attend_mfma(const uint16_t *__restrict__ q,
+                                                         const uint16_t *__restrict__ kc,
+                                                         const uint16_t *__restrict__ vc,
+                                                         const int32_t *__restrict__ idx, float *__restrict__ part,
+                                                         int Hq, int Hkv, int L, int n_sel, float scale_log2) {
+  constexpr int NDS = D / 32, ND = D / 16, NCH = D / 8, ROWB = 2 * D;
+  __shared__ __attribute__((aligned(16))) char vs[BLK * ROWB];
   const int bkv = blockIdx.x / n_sel, e = blockIdx.x % n_sel;
   const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int l = threadIdx.x, lr = l & 15, g = l >> 4;
   const int32_t *row = idx + (size_t)bkv * n_sel;
-  // entries end at the first negative one: each wave checks 0..e itself, 64 at a time
+  // entries end at the first negative one: the wave checks 0..e, 64 at a time
   const int j = row[e];
   bool neg = false;
   for (int x0 = 0; x0 <= e; x0 += 64) {
@@ -179,90 +176,101 @@ __global__ __launch_bounds__(256) void decode_attend_mfma(const uint16_t *__rest
     if (x <= e && row[x] < 0) neg = true;
   }
   const bool valid = !__any(neg) && (size_t)j * BLK < (size_t)L;
-  const int hh = tid >> 4, g = tid & 15;  // O = P V: head hh, columns DPG*g ..
-  float *dst = part + ((size_t)(b * Hq + kvh * G + hh) * n_sel + e) * (D + 2);
+  float *dst = part + ((size_t)(b * Hq + kvh * G + lr) * n_sel + e) * (D + 2);
   if (!valid) {  // an empty split: the combine gives it zero weight
-    if (hh < G) {
+    if (lr < G) {
 #pragma unroll
-      for (int c = 0; c < DPG; ++c) dst[DPG * g + c] = 0.f;
+      for (int dvt = 0; dvt < ND; ++dvt)
+        *reinterpret_cast<f32x4 *>(dst + 16 * dvt + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (g == 0) { dst[D] = -INFINITY; dst[D + 1] = 0.f; }
     }
     return;
   }
   const int cnt = min(BLK, L - j * BLK);
   const size_t base = (size_t)bkv * L + (size_t)j * BLK;
-  // issue every load up front: K and Q operand fragments, V rows to LDS
-  u32x4 kf[NDS], qfr[NDS], vr[(BLK * CPR) / 256];
-  const uint16_t *kp = kc + (base + min(16 * w + lr, cnt - 1)) * D;
+  // V rows -> LDS by direct loads: slot p = 64u + l holds row p / NCH, chunk
+  // p % NCH after the fkv swizzle, so the lane fetches the logical chunk that
+  // maps there (the XOR is an involution).  Rows past cnt repeat row cnt-1;
+  // their weights are zero.
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int p = 64 * u + l, vrow = p / NCH, ch = (p % NCH) ^ (int)(fkv(vrow) & (NCH - 1));
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1))) *)(vc + (base + min(vrow, cnt - 1)) * D + 8 * ch),
+        (void __attribute__((address_space(3))) *)(vs + 64 * u * 16), 16, 0, 0);
+  }
+  // K fragments (A operands) and the group's query fragments (B operands)
+  u32x4 kf[2][2][NDS], qf[NDS];
   const uint16_t *qp = q + (size_t)(b * Hq + kvh * G + min(lr, G - 1)) * D;
 #pragma unroll
-  for (int s = 0; s < NDS; ++s) {
-    kf[s] = gload16(kp + 32 * s + 8 * lg);
-    qfr[s] = gload16(qp + 32 * s + 8 * lg);
-  }
+  for (int s = 0; s < NDS; ++s) qf[s] = gload16(qp + 32 * s + 8 * g);
 #pragma unroll
-  for (int u = 0; u < (BLK * CPR) / 256; ++u) {
-    const int c = tid + 256 * u, r = c / CPR, ch = c % CPR;
-    vr[u] = gload16(vc + (base + min(r, cnt - 1)) * D + 8 * ch);
-  }
+  for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-  for (int u = 0; u < (BLK * CPR) / 256; ++u) {
-    const int c = tid + 256 * u, r = c / CPR, ch = c % CPR;
-    *reinterpret_cast<u32x4 *>(&vs[r * VS + 8 * ch]) = (r < cnt) ? vr[u] : u32x4{0, 0, 0, 0};
-  }
-  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t *kp = kc + (base + min(32 * pp + pair_key(t, lr), cnt - 1)) * D;
 #pragma unroll
-  for (int s = 0; s < NDS; ++s) S = mfma16x16x32(kf[s], (lr < G) ? qfr[s] : u32x4{0, 0, 0, 0}, S);
-  // lane (head lr, group lg) holds keys 16w + 4lg + i
-  float x[4], mx = -INFINITY;
+      for (int s = 0; s < NDS; ++s) kf[pp][t][s] = gload16(kp + 32 * s + 8 * g);
+    }
+  if (lr >= G) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = (16 * w + 4 * lg + i < cnt) ? S[i] * scale_log2 : -INFINITY;
-    mx = fmaxf(mx, x[i]);
+    for (int s = 0; s < NDS; ++s) qf[s] = u32x4{0, 0, 0, 0};
   }
+  f32x4 S[2][2];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) acc = mfma16x16x32(kf[pp][t][s], qf[s], acc);
+      S[pp][t] = acc;
+    }
+  // lane (head lr, group g) holds keys 32pp + 8g + 4t + i
+  float mx = -INFINITY;
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = (32 * pp + 8 * g + 4 * t + i < cnt) ? S[pp][t][i] * scale_log2 : -INFINITY;
+        S[pp][t][i] = x;
+        mx = fmaxf(mx, x);
+      }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (lg == 0) red_m[w][lr] = mx;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(red_m[0][lr], red_m[1][lr]), fmaxf(red_m[2][lr], red_m[3][lr]));
   float ls = 0.f;
+  u32x4 Bp[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = __builtin_amdgcn_exp2f(x[i] - m);
-    ps[lr][16 * w + 4 * lg + i] = p;
-    ls += p;
+  for (int pp = 0; pp < 2; ++pp) {
+    float p[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[t][i] = __builtin_amdgcn_exp2f(S[pp][t][i] - mx);
+        ls += p[t][i];
+      }
+    Bp[pp] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                   pack_bf16x2(p[1][2], p[1][3])};
   }
   ls += __shfl_xor(ls, 16, 64);
   ls += __shfl_xor(ls, 32, 64);
-  if (lg == 0) red_l[w][lr] = ls;
-  __syncthreads();
-  if (hh >= G) return;
-  float o[DPG];
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the V rows are in LDS
+  const uint32_t lane_off = tr_lane_off(l, ROWB), lane_xor = tr_lane_xor(l);
+  // every lane takes part in the MFMAs; only heads < G store
 #pragma unroll
-  for (int c = 0; c < DPG; ++c) o[c] = 0.f;
-  for (int key = 0; key < cnt; ++key) {
-    const float p = ps[hh][key];
-    if constexpr (DPG == 8) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(&vs[key * VS + 8 * g]);
+  for (int dvt = 0; dvt < ND; ++dvt) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        o[2 * c] = fmaf(p, bf16lo(v[c]), o[2 * c]);
-        o[2 * c + 1] = fmaf(p, bf16hi(v[c]), o[2 * c + 1]);
-      }
-    } else {
-      const u32x2 v = *reinterpret_cast<const u32x2 *>(&vs[key * VS + 4 * g]);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        o[2 * c] = fmaf(p, bf16lo(v[c]), o[2 * c]);
-        o[2 * c + 1] = fmaf(p, bf16hi(v[c]), o[2 * c + 1]);
-      }
-    }
+    for (int pp = 0; pp < 2; ++pp)
+      o = mfma16x16x32(tr_frag(vs, 32 * pp * ROWB, lane_off, lane_xor, dvt, NCH, ROWB), Bp[pp], o);
+    if (lr < G) *reinterpret_cast<f32x4 *>(dst + 16 * dvt + 4 * g) = o;
   }
-#pragma unroll
-  for (int c = 0; c < DPG; ++c) dst[DPG * g + c] = o[c];
-  if (g == 0) {
-    dst[D] = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
-    dst[D + 1] = red_l[0][hh] + red_l[1][hh] + red_l[2][hh] + red_l[3][hh];
+  if (lr < G && g == 0) {
+    dst[D] = mx;
+    dst[D + 1] = ls;
   }
 }
 
@@ -337,7 +345,7 @@ template <typename T, int D>
 void run(const SparseDecodeArgs &a, hipStream_t st) {
   float *part = static_cast<float *>(a.ws);
   if (sizeof(T) == 2 && a.Hq / a.Hkv <= 16) {
-    hipLaunchKernelGGL((decode_attend_mfma<D>), dim3(a.B * a.Hkv * a.n_sel), dim3(256), 0, st, (const uint16_t *)a.q,
+    hipLaunchKernelGGL((decode_attend_mfma<D>), dim3(a.B * a.Hkv * a.n_sel), dim3(64), 0, st, (const uint16_t *)a.q,
                        (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L,
                        a.n_sel, a.scale * 1.4426950408889634f);
     hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(512), 0, st, part, (T *)a.o, a.n_sel);

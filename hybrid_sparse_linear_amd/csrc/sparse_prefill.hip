@@ -43,7 +43,6 @@ __device__ __forceinline__ uint32_t swz_k(uint32_t row, uint32_t ch) {
   if constexpr (NCH == 16) return ch ^ ((row & 3) | ((row >> 1) & 12));
   else return ch ^ (((row >> 1) & 1) | ((row >> 2) & 6));
 }
-__device__ __forceinline__ int pair_key(int t, int r) { return ((r >> 2) << 3) + (t << 2) + (r & 3); }
 
 // V [bh][N][D] -> Vt [bh][NB][D][64] (keys contiguous), zero past N.
 template <int D>

@@ -23,7 +23,7 @@ def test_decode_step_graph_replays_match_eager():
     decay = I.slope_decay(H).cuda()
     q4 = q[:, :, None].contiguous()
     idx, kp = sala.sparse_select(q4, kc, topk=16)
-    ws_s = torch.empty(sala.workspace_bytes("sparse_select", dtype=1, B=B, Hq=Hq, Hkv=Hkv, d=d, Nq=1, L=L, block=64,
+    ws_s = torch.zeros(sala.workspace_bytes("sparse_select", dtype=1, B=B, Hq=Hq, Hkv=Hkv, d=d, Nq=1, L=L, block=64,
                                             topk=16, n_init=1, n_local=2), dtype=torch.uint8, device="cuda")
     ws_a = torch.empty(sala.workspace_bytes("sparse_decode", dtype=1, B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=64,
                                             n_sel=19), dtype=torch.uint8, device="cuda")

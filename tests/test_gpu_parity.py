@@ -204,6 +204,39 @@ def test_sparse_select_decode(L, dt, d, pooled_only):
                           f"decode b{b} h{h}")
 
 
+def test_sparse_select_decode_many_chunks_reuses_workspace():
+    """Decode selection over 1501 pooled blocks (several workgroups per row, a
+    ragged last one), top-64: exact against the oracle, twice on one
+    workspace with the same result."""
+    say("sparse_select decode, 1501 blocks, workspace reuse")
+    B, Hq, Hkv, d, topk = 2, 8, 2, 128, 64
+    L = 64 * 1500 + 3
+    NB = (L + 63) // 64
+    kbar = I.normal((B, Hkv, NB, d), 131, 1.0, I.F32)
+    q = I.normal((B, Hq, 1, d), 132, 1.0, I.BF16)
+    nb = sala.workspace_bytes("sparse_select", dtype=1, B=B, Hq=Hq, Hkv=Hkv, d=d, Nq=1, L=L, block=64, topk=topk,
+                              n_init=1, n_local=2)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    kp = dev(kbar)
+    ridx, scores = OS.sparse_select_decode(host64(q[:, :, 0]), host64(kbar), L, 64, topk)
+    i = (L - 1) // 64
+    cands = OS.candidate_blocks(i, L, 64, 1, 2)
+    first = None
+    for call in range(2):
+        idx, _ = sala.sparse_select(dev(q), None, k_pooled=kp, L=L, topk=topk, workspace=ws)
+        torch.cuda.synchronize()
+        g = idx.cpu().numpy()
+        for b in range(B):
+            for h in range(Hkv):
+                nt = near_tie_rows([scores[b, h]], [cands], topk)[0]
+                check_idx_row(g[b, h, 0], ridx[b, h], scores[b, h], cands, sorted(OS.forced_blocks(i, 1, 2)), topk,
+                              nt, f"call {call} b{b} h{h}")
+        if first is None:
+            first = idx.clone()
+        else:
+            assert torch.equal(idx, first)
+
+
 # ---------------------------------------------------------------- sparse prefill
 
 ATT_CASES = [

@@ -107,7 +107,7 @@ def sparse_full_check(N, workload, n_rows=10, attn_rows_per_block=3):
     Hq, Hkv, d = q.shape[1], k.shape[1], q.shape[3]
     G = Hq // Hkv
     nqb = N // 64
-    ws_sel = torch.empty(sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N, block=64,
+    ws_sel = torch.zeros(sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N, block=64,
                                               topk=64, n_init=1, n_local=2), dtype=torch.uint8, device="cuda")
     idx = torch.empty((1, Hkv, nqb, 67), dtype=torch.int32, device="cuda")
     kp = torch.empty((1, Hkv, nqb, d), dtype=torch.float32, device="cuda")
