@@ -96,8 +96,11 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
                                                         uint16_t *__restrict__ o, int Hq, int Hkv, int N, int NQB,
                                                         int n_sel, int HG, int ntasks, float scale_log2) {
   using Cf = SpCfg<D>;
-  __shared__ __attribute__((aligned(16))) char kbuf[2][Cf::KB];
-  __shared__ __attribute__((aligned(16))) char vbuf[2][Cf::KB];
+  // one LDS array per buffer: with the loop unrolled by two every LDS read
+  // and every direct load names its buffer, so the compiler can see that the
+  // next block's loads do not touch the block being read and need not wait
+  __shared__ __attribute__((aligned(16))) char kb0[Cf::KB], kb1[Cf::KB];
+  __shared__ __attribute__((aligned(16))) char vb0[Cf::KB], vb1[Cf::KB];
   __shared__ int sel[1024];
   __shared__ int nvalid_sh, diag_sh;
 
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // involutions).  K rows past N re-read the last valid row; causality masks
   // them.  V^T blocks come zero-padded from transpose_v_blocks.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto load_block = [&](int j, int buf) {
+  auto load_block = [&](int j, char *kdst, char *vdst) {
     const uint16_t *ksrc = kbase + (size_t)j * BLK * D;
     const uint16_t *vsrc = vtbase + (size_t)j * D * BLK;
     const int last = min(BLK, N - j * BLK) - 1;
@@ -181,11 +184,11 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
       const int krow = p / Cf::KCH, kch = swz_k<Cf::KCH>(krow, p % Cf::KCH);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1))) *)(ksrc + (size_t)min(krow, last) * D + 8 * kch),
-          (void __attribute__((address_space(3))) *)(kbuf[buf] + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
+          (void __attribute__((address_space(3))) *)(kdst + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
       const int vrow = p / Cf::TCH, vch = swz_t<Cf::TCH>(vrow, p % Cf::TCH);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1))) *)(vsrc + (size_t)vrow * BLK + 8 * vch),
-          (void __attribute__((address_space(3))) *)(vbuf[buf] + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
+          (void __attribute__((address_space(3))) *)(vdst + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
     }
   };
   // this wave's direct loads done (vmcnt 0); the barrier that follows publishes them
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // for kt = 2p + t), softmax numerators against a per-row reference max that
   // moves (rescaling O and L) only when the block max exceeds it by more than
   // 2^8, then O^T += V^T P^T and L += 1 P^T.
-  auto step = [&](int buf, bool mask) {
+  auto step = [&](const char *kbuf, const char *vbuf, bool mask) {
     f32x4 S[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int row = 32 * (kt >> 1) + pair_key(kt & 1, lr);
-        const u32x4 A = lds_load<u32x4>(kbuf[buf], (row * Cf::KCH + swz_k<Cf::KCH>(row, 4 * s + lg)) * 16u);
+        const u32x4 A = lds_load<u32x4>(kbuf, (row * Cf::KCH + swz_k<Cf::KCH>(row, 4 * s + lg)) * 16u);
 #pragma unroll
         for (int a = 0; a < 2; ++a) S[kt][a] = mfma16x16x32(A, qf[a][s], S[kt][a]);
       }
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
 #pragma unroll
       for (int dv = 0; dv < Cf::ND; ++dv) {
         const int row = 16 * dv + lr;
-        const u32x4 A = lds_load<u32x4>(vbuf[buf], (row * Cf::TCH + swz_t<Cf::TCH>(row, 4 * pp + lg)) * 16u);
+        const u32x4 A = lds_load<u32x4>(vbuf, (row * Cf::TCH + swz_t<Cf::TCH>(row, 4 * pp + lg)) * 16u);
 #pragma unroll
         for (int a = 0; a < 2; ++a) Oacc[a][dv] = mfma16x16x32(A, Pf[a][pp], Oacc[a][dv]);
       }
@@ -269,16 +272,29 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   };
 
   if (nvalid > 0) {
-    load_block(sel[0], 0);
+    load_block(sel[0], kb0, vb0);
     wait_loads();
     __syncthreads();
-    for (int j = 0; j + 1 < nvalid; ++j) {
-      load_block(sel[j + 1], (j + 1) & 1);  // lands while block j is processed
-      step(j & 1, false);
+    int j = 0;
+    for (; j + 2 < nvalid; j += 2) {  // blocks j (buffer 0) and j+1 (buffer 1)
+      load_block(sel[j + 1], kb1, vb1);  // lands while block j is processed
+      step(kb0, vb0, false);
+      wait_loads();
+      __syncthreads();
+      load_block(sel[j + 2], kb0, vb0);
+      step(kb1, vb1, false);
       wait_loads();
       __syncthreads();
     }
-    step((nvalid - 1) & 1, has_diag);
+    if (j + 1 < nvalid) {  // two blocks left, the second one last
+      load_block(sel[j + 1], kb1, vb1);
+      step(kb0, vb0, false);
+      wait_loads();
+      __syncthreads();
+      step(kb1, vb1, has_diag);
+    } else {
+      step(kb0, vb0, has_diag);
+    }
   }
 
   if (!active) return;
