@@ -64,12 +64,15 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void *lds, uint32_t byte_off)
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Row swizzle of 16-byte chunks for row-major bf16 tiles in LDS that are read
-// both as plain 16-byte operand rows and with lds_read_tr: spreads 16 rows of
-// a 32-key pair (see pair_key) and the transposed reads of rows k0 + 8g + 4h
-// + r over all banks.  For those transposed reads it depends on g and r only.
+// Row swizzle of 16-byte chunks for row-major bf16 tiles of 256-byte rows in
+// LDS that are read both as plain 16-byte operand rows (16 rows of a 32-key
+// pair, see pair_key) and with lds_read_tr (rows k0 + 8g + 4h + r): row bits
+// 0, 1, 3 go to chunk bits 1, 2, 3.  Chunk bit 0 stays: candidate swizzles
+// measured with the bank-conflict counter on gfx950 show that XOR-ing it
+// costs extra cycles on 16-byte reads, and this map is conflict-free for both
+// access patterns.  For the transposed reads it depends on g and r only.
 __device__ __forceinline__ uint32_t fkv(uint32_t row) {
-  return ((row & 3u) << 1) | (((row >> 3) & 1u) << 3) | ((row >> 4) & 1u);
+  return ((row & 1u) << 1) | (((row >> 1) & 1u) << 2) | (((row >> 3) & 1u) << 3);
 }
 // Per-lane constants of a transposed fragment read (lane l = 16g + 4r + c):
 // byte offset of its row and 8-byte half, and the XOR applied to the tile's

@@ -34,9 +34,13 @@ namespace {
 
 constexpr int BLK = 64;  // tokens per KV / query block
 
+// V^T rows are 128 bytes (64 keys); a read takes 16 consecutive rows at one
+// chunk.  Row bits 0..2 XOR the chunk index: conflict-free on gfx950 by the
+// bank-conflict counter (a swizzle that also mixes row bit 3 into chunk bit 0
+// costs extra cycles).
 template <int NCH>
 __device__ __forceinline__ uint32_t swz_t(uint32_t row, uint32_t ch) {
-  return ch ^ ((row ^ (row >> 3)) & (NCH - 1));
+  return ch ^ (row & (NCH - 1));
 }
 template <int NCH>
 __device__ __forceinline__ uint32_t swz_k(uint32_t row, uint32_t ch) {
