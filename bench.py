@@ -32,6 +32,35 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM traffic of one sparse_attn_bf16 launch at the 256K workload, from two
+# rocprofv3 --pmc runs of `python bench.py --steps 1 --warmup 0
+# --no-cpu-baseline --no-decode` (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by what the same counter reads for a plain 1 GiB
+# device copy (FETCH_SIZE reads 0.5 GiB -> x2.0; WRITE_SIZE reads 1 GiB ->
+# x1.0); summary in profiles/sparse_attn_256K_hbm_traffic.md.  It holds only
+# for the kernel sources it was measured on: reported as null otherwise.
+TRAFFIC_MEASURED = {
+    "sources_sha256": "4737be3027f06e735dc761e0b461b8dc02a85d314964de36d5c6b870b81d33e3",
+    "fetch_kib": 8841841.1875, "fetch_scale": 2.0,
+    "write_kib": 2357108.0, "write_scale": 1.0,
+}
+TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
+
+
+def measured_traffic_bytes():
+    """Counter-measured HBM bytes per sparse_attn_bf16 launch, or None when the
+    kernel sources differ from the ones the counters were taken on."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    t = TRAFFIC_MEASURED
+    if h.hexdigest() != t["sources_sha256"]:
+        return None
+    return int(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -245,6 +274,9 @@ def main():
     flops = sparse_flops(idx, N, d, Hq // Hkv)
     group_flops = 3 * (32 * N * (2 * 128 * 128 + 4 * 128 * 128)) * 1.0 + flops  # algorithmic (causal) counts
     achieved = flops / (att_ms * 1e-3) / 1e12
+    traffic = measured_traffic_bytes() if N == 262144 else None
+    # unique bytes: Q read and O written once; K and V (as V^T) of the KV heads read once
+    alg_bytes = 2 * (Hq * N * d * 2) + 2 * (Hkv * N * d * 2)
     out = {
         "metric": "prefill tokens/s for 3:1 linear:sparse layer group at 256K; % MFMA/HBM peak",
         "value": round(N / (ms / 1000.0), 1),
@@ -265,7 +297,9 @@ def main():
         "group_mfma_frac": round(group_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
         "roofline": {"kernel": "sparse_attn_bf16 (+ its V^T block staging, <1%)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (counters, N=262144 only)",
+                     "algorithmic_bytes_per_launch": alg_bytes,
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4)},
     }
     if not args.no_decode:
