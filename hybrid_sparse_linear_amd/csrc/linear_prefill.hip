@@ -147,7 +147,8 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
                                                          int seg_len, int nseg) {
   using Cf = LinCfg<C, D>;
   __shared__ __attribute__((aligned(16))) char lds[Cf::LDS];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int nagg = nseg - 1;
   const int bh = blockIdx.x / nagg, seg = blockIdx.x % nagg;
   const int h = bh % H;
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
                                                       int H, int N, int seg_len, int nseg) {
   using Cf = LinCfg<C, D>;
   __shared__ __attribute__((aligned(16))) char lds[Cf::LDS];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const int h = bh % H;
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
@@ -311,12 +313,22 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) {
         const int qq = 32 * gq + 16 * tq + lr;
+        // decay factors read unconditionally (all 8 LDS reads in flight), then
+        // the causal mask as a select -- no branch around each read
+        float f[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[t][i] = pw[max(qq - (32 * p + 8 * g + 4 * t + i), 0)];
+            __asm__("" : "+v"(f[t][i]));  // keeps the read out of a branch
+          }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = 32 * p + 8 * g + 4 * t + i;
-            P[tq][t][i] = (j <= qq) ? P[tq][t][i] * pw[max(qq - j, 0)] : 0.f;
+            P[tq][t][i] = (j <= qq) ? P[tq][t][i] * f[t][i] : 0.f;
           }
         Bp[tq] = u32x4{pack_bf16x2(P[tq][0][0], P[tq][0][1]), pack_bf16x2(P[tq][0][2], P[tq][0][3]),
                        pack_bf16x2(P[tq][1][0], P[tq][1][1]), pack_bf16x2(P[tq][1][2], P[tq][1][3])};
