@@ -326,8 +326,26 @@ __global__ __launch_bounds__(NT) void select_rows(const float *__restrict__ scor
 __device__ __forceinline__ uint64_t pack_key(float score, int j) {
   return ((uint64_t)float_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
+// Value of lane l ^ m.  m is a constant after unrolling: m <= 8 are DPP moves
+// on the VALU (xor 4 = row half-mirror then quad permutation [3,2,1,0]; xor 8 =
+// row rotate by 8), m = 16 a ds_swizzle bit-mode exchange, m = 32 a bpermute.
+// The lane maps were checked on gfx950 with a probe.
+__device__ __forceinline__ uint32_t shfl_xor32(uint32_t v, int m) {
+  const int x = (int)v;
+  switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const int h = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, false);
+    }
+    case 8: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);
+    default: return (uint32_t)__shfl_xor(x, m, 64);
+  }
+}
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  const uint32_t lo = shfl_xor32((uint32_t)v, m), hi = shfl_xor32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
 // Descending bitonic sort of one key per lane across a wave.
