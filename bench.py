@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # x1.0); summary in profiles/sparse_attn_256K_hbm_traffic.md.  It holds only
 # for the kernel sources it was measured on: reported as null otherwise.
 TRAFFIC_MEASURED = {
-    "sources_sha256": "4737be3027f06e735dc761e0b461b8dc02a85d314964de36d5c6b870b81d33e3",
-    "fetch_kib": 8841841.1875, "fetch_scale": 2.0,
-    "write_kib": 2357108.0, "write_scale": 1.0,
+    "sources_sha256": "ba84bf7cf5c6ba8ef953bb28fa4f4bf06879bdc2387c76fbb743922813e10014",
+    "fetch_kib": 8873247.75, "fetch_scale": 2.0,
+    "write_kib": 2228052.875, "write_scale": 1.0,
 }
 TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
 
@@ -275,7 +275,7 @@ def main():
     group_flops = 3 * (32 * N * (2 * 128 * 128 + 4 * 128 * 128)) * 1.0 + flops  # algorithmic (causal) counts
     achieved = flops / (att_ms * 1e-3) / 1e12
     traffic = measured_traffic_bytes() if N == 262144 else None
-    # unique bytes: Q read and O written once; K and V (as V^T) of the KV heads read once
+    # unique bytes: Q read and O written once; K and V of the KV heads read once
     alg_bytes = 2 * (Hq * N * d * 2) + 2 * (Hkv * N * d * 2)
     out = {
         "metric": "prefill tokens/s for 3:1 linear:sparse layer group at 256K; % MFMA/HBM peak",
@@ -295,7 +295,7 @@ def main():
                                "top-64 + 1 initial + 2 local)" % N,
                    "tokens": N, "batch": 1},
         "group_mfma_frac": round(group_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-        "roofline": {"kernel": "sparse_attn_bf16 (+ its V^T block staging, <1%)", "bound": "mfma",
+        "roofline": {"kernel": "sparse_attn_bf16", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (counters, N=262144 only)",

@@ -18,8 +18,9 @@
 //   * S^T = K Q^T on MFMA 16x16x32 (A = K rows from LDS, B = Q rows held in
 //     registers), so each lane owns one query row and 16 keys per tile row:
 //     row max/sum need only two cross-lane steps per block.
-//   * O^T += V^T P^T with V pre-transposed per block in the workspace
-//     (transpose_v_blocks), so the V^T operand is a 16-byte LDS read.
+//   * O^T += V^T P^T with V staged row-major in LDS and its V^T operand
+//     fragments read with the gfx950 transposed LDS read (two
+//     ds_read_b64_tr_b16 per fragment): no transposed copy of V anywhere.
 //   * K and V^T blocks are double buffered in LDS; the next block's global
 //     loads are issued before the current block's MFMAs.
 //   * Workgroups of one (b, kv head, query block) land on the same XCD so the
@@ -34,49 +35,10 @@ namespace {
 
 constexpr int BLK = 64;  // tokens per KV / query block
 
-// V^T rows are 128 bytes (64 keys); a read takes 16 consecutive rows at one
-// chunk.  Row bits 0..2 XOR the chunk index: conflict-free on gfx950 by the
-// bank-conflict counter (a swizzle that also mixes row bit 3 into chunk bit 0
-// costs extra cycles).
-template <int NCH>
-__device__ __forceinline__ uint32_t swz_t(uint32_t row, uint32_t ch) {
-  return ch ^ (row & (NCH - 1));
-}
 template <int NCH>
 __device__ __forceinline__ uint32_t swz_k(uint32_t row, uint32_t ch) {
   if constexpr (NCH == 16) return ch ^ ((row & 3) | ((row >> 1) & 12));
   else return ch ^ (((row >> 1) & 1) | ((row >> 2) & 6));
-}
-
-// V [bh][N][D] -> Vt [bh][NB][D][64] (keys contiguous), zero past N.
-template <int D>
-__global__ __launch_bounds__(256) void transpose_v_blocks(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt,
-                                                          int N, int NB) {
-  const int bid = blockIdx.x;
-  const int bh = bid / NB, j = bid % NB;
-  const int tid = threadIdx.x;
-  constexpr int FG = D / 8;
-  if (tid >= 8 * FG) return;
-  const int tg = tid / FG, fg = tid % FG;
-  const uint16_t *src = v + ((size_t)bh * N + (size_t)j * BLK) * D;
-  u32x4 x[8], y[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = j * BLK + 8 * tg + e;
-    x[e] = (t < N) ? gload16(src + (size_t)(8 * tg + e) * D + 8 * fg) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int p = f >> 1;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const uint32_t a = x[2 * qq][p], b = x[2 * qq + 1][p];
-      y[f][qq] = (f & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-  uint16_t *dst = vt + ((size_t)bh * NB + j) * D * BLK;
-#pragma unroll
-  for (int f = 0; f < 8; ++f) gstore16(dst + (size_t)(8 * fg + f) * BLK + 8 * tg, y[f]);
 }
 
 template <int D>
@@ -84,8 +46,8 @@ struct SpCfg {
   static constexpr int NDS = D / 32;        // 32-deep feature steps
   static constexpr int ND = D / 16;         // 16-wide d_v tiles
   static constexpr int KCH = D / 8;         // 16-byte chunks per K row
-  static constexpr int TCH = BLK / 8;       // 16-byte chunks per V^T row (8)
-  static constexpr int KB = BLK * D * 2;    // bytes of one K block (== one V^T block)
+  static constexpr int ROWB = D * 2;        // bytes per K / V row
+  static constexpr int KB = BLK * D * 2;    // bytes of one K (or V) block
   static constexpr int NT = 512;            // threads per workgroup (8 waves)
   static constexpr int PER_T = KB / 16 / NT;  // 16-byte direct loads per thread per block
 };
@@ -96,7 +58,7 @@ struct SpCfg {
 // softmax overlaps the other's MFMAs.
 template <int D>
 __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                        const uint16_t *__restrict__ vt, const int32_t *__restrict__ idx,
+                                                        const uint16_t *__restrict__ v, const int32_t *__restrict__ idx,
                                                         uint16_t *__restrict__ o, int Hq, int Hkv, int N, int NQB,
                                                         int n_sel, int HG, int ntasks, float scale_log2) {
   using Cf = SpCfg<D>;
@@ -169,18 +131,19 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   const int nvalid = nvalid_sh;
   const bool has_diag = diag_sh != 0;
   const uint16_t *kbase = k + ((size_t)bkv * N) * D;
-  const int NB = (N + BLK - 1) / BLK;
-  const uint16_t *vtbase = vt + ((size_t)bkv * NB) * D * BLK;
+  const uint16_t *vbase = v + ((size_t)bkv * N) * D;
 
   // Direct global -> LDS loads (16 bytes per lane): the LDS slot of lane l in
   // wave w for step u is p = 512u + 64w + l, so each lane fetches the logical
   // chunk that the row swizzle maps to its slot (the XOR swizzles are
-  // involutions).  K rows past N re-read the last valid row; causality masks
-  // them.  V^T blocks come zero-padded from transpose_v_blocks.
+  // involutions).  K and V rows past N re-read the last valid row: they are
+  // keys of the diagonal block beyond every query, so causality masks them.
+  // V rows use the fkv swizzle of the transposed reads.
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);  // V^T fragment reads
   auto load_block = [&](int j, char *kdst, char *vdst) {
     const uint16_t *ksrc = kbase + (size_t)j * BLK * D;
-    const uint16_t *vsrc = vtbase + (size_t)j * D * BLK;
+    const uint16_t *vsrc = vbase + (size_t)j * BLK * D;
     const int last = min(BLK, N - j * BLK) - 1;
 #pragma unroll
     for (int u = 0; u < Cf::PER_T; ++u) {
@@ -189,9 +152,9 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1))) *)(ksrc + (size_t)min(krow, last) * D + 8 * kch),
           (void __attribute__((address_space(3))) *)(kdst + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
-      const int vrow = p / Cf::TCH, vch = swz_t<Cf::TCH>(vrow, p % Cf::TCH);
+      const int vch = (p % Cf::KCH) ^ (int)(fkv(krow) & (Cf::KCH - 1));
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(vsrc + (size_t)vrow * BLK + 8 * vch),
+          (const void __attribute__((address_space(1))) *)(vsrc + (size_t)min(krow, last) * D + 8 * vch),
           (void __attribute__((address_space(3))) *)(vdst + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
     }
   };
@@ -265,8 +228,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
     for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
       for (int dv = 0; dv < Cf::ND; ++dv) {
-        const int row = 16 * dv + lr;
-        const u32x4 A = lds_load<u32x4>(vbuf, (row * Cf::TCH + swz_t<Cf::TCH>(row, 4 * pp + lg)) * 16u);
+        const u32x4 A = tr_frag(vbuf, 32 * pp * Cf::ROWB, tr_off, tr_xor, dv, Cf::KCH, Cf::ROWB);
 #pragma unroll
         for (int a = 0; a < 2; ++a) Oacc[a][dv] = mfma16x16x32(A, Pf[a][pp], Oacc[a][dv]);
       }
@@ -383,10 +345,8 @@ __global__ __launch_bounds__(64) void sparse_attn_f32(const float *__restrict__ 
 }  // namespace
 
 size_t sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel) {
-  (void)Hq; (void)n_sel;
-  if (dtype != 1) return 0;
-  const size_t NB = (size_t)(N + block - 1) / block;
-  return (size_t)B * Hkv * NB * block * d * 2;  // V^T blocks
+  (void)dtype; (void)B; (void)Hq; (void)Hkv; (void)N; (void)d; (void)block; (void)n_sel;
+  return 0;  // every path works from the caller's tensors alone
 }
 
 hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st) {
@@ -402,26 +362,19 @@ hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st) {
                          a.n_sel, a.scale);
     return hipGetLastError();
   }
-  const int NB = NQB;
-  uint16_t *vt = static_cast<uint16_t *>(a.ws);
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 3) / 4;
   const int ntasks = a.B * a.Hkv * NQB;
   const int grid = ((ntasks + 7) / 8) * 8 * HG;
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  if (a.d == 128) {
-    hipLaunchKernelGGL(transpose_v_blocks<128>, dim3(a.B * a.Hkv * NB), dim3(256), 0, st, (const uint16_t *)a.v,
-                       vt, a.N, NB);
+  if (a.d == 128)
     hipLaunchKernelGGL(sparse_attn_bf16<128>, dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, vt, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HG,
-                       ntasks, scale_log2);
-  } else {
-    hipLaunchKernelGGL(transpose_v_blocks<64>, dim3(a.B * a.Hkv * NB), dim3(256), 0, st, (const uint16_t *)a.v, vt,
-                       a.N, NB);
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
+                       a.n_sel, HG, ntasks, scale_log2);
+  else
     hipLaunchKernelGGL(sparse_attn_bf16<64>, dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, vt, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HG,
-                       ntasks, scale_log2);
-  }
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
+                       a.n_sel, HG, ntasks, scale_log2);
   return hipGetLastError();
 }
 

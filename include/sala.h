@@ -152,7 +152,8 @@ size_t sala_sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, in
  *   block        64.   n_sel = idx row length (topk + n_init + n_local).
  *   scale        usually 1/sqrt(d).
  *   q, o         [B, Hq, N, d];  k, v  [B, Hkv, N, d];  idx [B, Hkv, NQB, n_sel].
- *   ws, ws_bytes at least sala_sparse_prefill_workspace(...) bytes.
+ *   ws, ws_bytes at least sala_sparse_prefill_workspace(...) bytes (0 in this
+ *                version: ws may be NULL).
  * ------------------------------------------------------------------------ */
 int sala_sparse_prefill(int dtype, int B, int Hq, int Hkv, int N, int d,
                         int block, int n_sel, float scale,

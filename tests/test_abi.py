@@ -111,7 +111,10 @@ def test_sparse_select_validation():
 def test_sparse_prefill_and_decode_validation():
     L = _lib.lib()
     f = L.sala_sparse_prefill
-    assert f(BF16, 1, 4, 2, 256, 128, 64, 7, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == WORKSPACE
+    # the sparse prefill needs no workspace (NULL is accepted); the remaining
+    # cases fail validation before any device work
+    assert L.sala_sparse_prefill_workspace(BF16, 1, 32, 2, 262144, 128, 64, 67) == 0
+    assert L.sala_sparse_prefill_workspace(F32, 1, 4, 2, 2048, 64, 64, 7) == 0
     assert f(BF16, 1, 4, 3, 256, 128, 64, 7, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == INVALID
     assert f(BF16, 1, 4, 2, 256, 128, 64, 0, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == UNSUPPORTED
     assert f(BF16, 1, 4, 2, 256, 128, 64, 7, ctypes.c_float(float("nan")), A, A, A, A, A, A, 1 << 30, NUL) == INVALID
