@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # x1.0); summary in profiles/sparse_attn_256K_hbm_traffic.md.  It holds only
 # for the kernel sources it was measured on: reported as null otherwise.
 TRAFFIC_MEASURED = {
-    "sources_sha256": "ba84bf7cf5c6ba8ef953bb28fa4f4bf06879bdc2387c76fbb743922813e10014",
-    "fetch_kib": 8873247.75, "fetch_scale": 2.0,
-    "write_kib": 2228052.875, "write_scale": 1.0,
+    "sources_sha256": "d0fa7a04c372a56d2707017f39be971e8f2002347e9d3ae699731637f818a957",
+    "fetch_kib": 8868454.9, "fetch_scale": 2.0,
+    "write_kib": 2228051.8, "write_scale": 1.0,
 }
 TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
 
@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=262144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling microkernels")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
     return ap.parse_args()
 
@@ -153,6 +155,60 @@ def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
                        f"at the end of the 256K context ({t_sel_row * 1e3:.1f} ms/row); restricted softmax for "
                        f"{len(rows)} query rows of 67 blocks ({t_att_row * 1e3:.2f} ms/row); scaled to 3 linear "
                        f"layers x 32 heads x N + 2 x 4096 selection rows + 32 x N attention rows")}
+
+
+def measure_ceilings(torch, sala):
+    """This GPU's practical ceilings from the two in-repo microkernels: an MFMA
+    loop (bf16 16x16x32) and a streaming copy of 1 GiB.  Best of a few reps."""
+    wgs, iters = 256 * 2, 20000
+    out = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            t.append(s.elapsed_time(e) * 1e-3)
+        return min(t)
+
+    t_mfma = best(lambda: sala.ceiling_mfma(wgs, iters, out))
+    t_copy = best(lambda: sala.ceiling_copy(src, dst))
+    mfma = wgs * 8 * iters * 8 * 16384 / t_mfma / 1e12
+    copy = 2 * src.numel() * 4 / t_copy / 1e9
+    del out, src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma, 1), "copy_gbs": round(copy, 1),
+            "method": "in-repo microkernels: 512 workgroups x 8 waves x 20000 rounds of 8 independent bf16 MFMA "
+                      "16x16x32; 1 GiB device copy with 16-byte loads/stores (read + write bytes); best of 5"}
+
+
+def bench_dense(torch, sala, sp, group_ms):
+    """The full-attention layer the sparse layer replaces: causal attention over
+    every earlier token at the same shapes, one timed launch after one warmup."""
+    q, k, v = sp["q"], sp["k"], sp["v"]
+    B, Hq, N, d = q.shape
+    o = torch.empty_like(q)
+    sala.dense_prefill(q, k, v, out=o)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    sala.dense_prefill(q, k, v, out=o)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    flops = 4 * d * Hq * B * N * (N + 1) / 2  # QK^T and PV over the causal half
+    return {"workload": "dense causal attention, Hq=32, Hkv=2, d=128, N=%d (bf16)" % N, "ms": round(ms, 2),
+            "tflop": round(flops / 1e12, 1), "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+            "group_speedup_vs_4_dense_layers": round(4 * ms / group_ms, 2),
+            "note": "attention ops only: the 3:1 group time against four full-attention layers at 256K"}
 
 
 def bench_decode(torch, sala, I, reps=20):
@@ -302,10 +358,15 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4)},
     }
+    if not args.no_dense:
+        out["dense_comparison"] = bench_dense(torch, sala, sp, ms)
     if not args.no_decode:
         del lin
         torch.cuda.empty_cache()
         out["decode"] = bench_decode(torch, sala, I)
+    if not args.no_ceilings:
+        out["ceilings"] = measure_ceilings(torch, sala)
+        out["roofline"]["frac_of_measured_ceiling"] = round(achieved / out["ceilings"]["mfma_bf16_tflops"], 4)
     if not args.no_cpu_baseline:
         lin1 = [I.workload2_linear(0, "cuda", N=8192, workload=4)]
         out["cpu_baseline"] = cpu_baseline(lin1, sp, idx, args.cpu_sample_seconds)

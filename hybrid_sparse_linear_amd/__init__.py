@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, without the ``sala_`` prefix):
   sparse_select    pooled block scores and top-k block selection
   sparse_prefill   softmax attention over the selected blocks
   sparse_decode    one query token against the selected cached blocks
+  dense_prefill    plain causal attention (the full-attention comparison)
+  ceiling_mfma / ceiling_copy   microkernels measuring this GPU's ceilings
   layer_group_prefill  three linear layers then one sparse layer, one stream
 """
 
@@ -23,7 +25,7 @@ import torch
 from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 
 __all__ = ["linear_prefill", "linear_decode", "sparse_select", "sparse_prefill", "sparse_decode",
-           "layer_group_prefill", "workspace_bytes", "SalaError"]
+           "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
 
 
 def _code(t):
@@ -178,6 +180,31 @@ def sparse_decode(q, k_cache, v_cache, idx, *, L=None, block=64, scale=None, out
     call("sala_sparse_decode", dt, B, Hq, Hkv, L, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k_cache),
          _ptr(v_cache), _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
     return o
+
+
+def dense_prefill(q, k, v, *, scale=None, out=None):
+    """Causal softmax attention of q [B, Hq, N, d] over every earlier token of k, v [B, Hkv, N, d] (bf16)."""
+    _dev(q, k, v, out)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    call("sala_dense_prefill", _code(q), B, Hq, Hkv, N, d, ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+         _stream())
+    return o
+
+
+def ceiling_mfma(workgroups, iters, out):
+    """Launch the MFMA ceiling microkernel (flops = workgroups*8*iters*8*16384)."""
+    _dev(out)
+    call("sala_ceiling_mfma", workgroups, iters, _ptr(out), _stream())
+
+
+def ceiling_copy(src, dst):
+    """Launch the streaming-copy ceiling microkernel over src.nbytes bytes."""
+    _dev(src, dst)
+    nbytes = src.numel() * src.element_size()
+    call("sala_ceiling_copy", _ptr(src), _ptr(dst), nbytes, _stream())
 
 
 def layer_group_prefill(linear_layers, sparse_layer, *, block=64, topk=64, n_init=1, n_local=2, chunk=None):

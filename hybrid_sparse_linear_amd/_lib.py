@@ -24,6 +24,9 @@ _SIGS = {
     "sala_sparse_prefill_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_sparse_decode": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_sparse_decode_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "sala_dense_prefill": (_i, [_i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p]),
+    "sala_ceiling_mfma": (_i, [_i, _i, _p, _p]),
+    "sala_ceiling_copy": (_i, [_p, _p, _z, _p]),
     "sala_status_string": (ctypes.c_char_p, [_i]),
     "sala_last_error": (ctypes.c_char_p, []),
     "sala_version": (ctypes.c_char_p, []),

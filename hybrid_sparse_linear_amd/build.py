@@ -24,6 +24,7 @@ SOURCES = [
     "sparse_select.hip",
     "sparse_prefill.hip",
     "sparse_decode.hip",
+    "ceilings.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

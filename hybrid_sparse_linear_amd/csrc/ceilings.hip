@@ -1,0 +1,55 @@
+// Two microkernels that measure this GPU's practical ceilings, reported next
+// to the published peaks: an MFMA loop (bf16 16x16x32, eight independent
+// accumulators per wave, 512-thread workgroups) and a streaming copy (16-byte
+// loads and stores, eight in flight per thread).  Not part of the attention
+// path.
+
+#include "sala_common.hpp"
+#include "sala_launch.hpp"
+
+namespace sala {
+namespace {
+
+__global__ __launch_bounds__(512) void mfma_loop(int iters, float *__restrict__ out) {
+  // operands depend on the lane so nothing folds
+  const u32x4 a = {threadIdx.x, 1u, 2u, 3u}, b = {3u, 2u, 1u, threadIdx.x};
+  f32x4 c[8] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = mfma16x16x32(a, b, c[u]);
+  }
+  float s = 0.f;
+  for (int u = 0; u < 8; ++u) s += c[u][0] + c[u][1] + c[u][2] + c[u][3];
+  // the stores only keep the loop alive: results are not needed
+  if (s == 1234.5f) out[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void copy_stream(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                   size_t n16) {
+  constexpr int U = 8;  // loads in flight per thread
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[i + u * stride] = x[u];
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_ceiling_mfma(int workgroups, int iters, float *out, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(512), 0, st, iters, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ceiling_copy(const void *src, void *dst, size_t bytes, hipStream_t st) {
+  hipLaunchKernelGGL(copy_stream, dim3(256 * 16), dim3(256), 0, st, static_cast<const u32x4 *>(src),
+                     static_cast<u32x4 *>(dst), bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace sala

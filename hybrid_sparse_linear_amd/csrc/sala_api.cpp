@@ -187,6 +187,38 @@ int sala_sparse_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, int blo
   return hip_status(sala::launch_sparse_prefill(a, static_cast<hipStream_t>(stream)), "sala_sparse_prefill launch");
 }
 
+int sala_dense_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, float scale, const void *q, const void *k,
+                       const void *v, void *o, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(dtype == SALA_BF16, SALA_ERR_UNSUPPORTED, "sala_dense_prefill supports SALA_BF16 only");
+  if ((s = check_sparse_common(B, Hq, Hkv, 64, 1, "n_sel"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(N >= 1, SALA_ERR_INVALID_ARG, "N must be >= 1");
+  REQUIRE(scale == scale, SALA_ERR_INVALID_ARG, "scale is NaN");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(o, "o");
+  sala::SparsePrefillArgs a{dtype, B, Hq, Hkv, N, d, 64, 1, scale, q, k, v, nullptr, o, nullptr};
+  return hip_status(sala::launch_dense_prefill(a, static_cast<hipStream_t>(stream)), "sala_dense_prefill launch");
+}
+
+int sala_ceiling_mfma(int workgroups, int iters, float *out, void *stream) {
+  REQUIRE(workgroups >= 1 && iters >= 1, SALA_ERR_INVALID_ARG, "workgroups and iters must be >= 1");
+  REQUIRE_PTR(out, "out");
+  return hip_status(sala::launch_ceiling_mfma(workgroups, iters, out, static_cast<hipStream_t>(stream)),
+                    "sala_ceiling_mfma launch");
+}
+
+int sala_ceiling_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  REQUIRE_PTR(src, "src");
+  REQUIRE_PTR(dst, "dst");
+  REQUIRE(bytes % 16 == 0, SALA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  return hip_status(sala::launch_ceiling_copy(src, dst, bytes, static_cast<hipStream_t>(stream)),
+                    "sala_ceiling_copy launch");
+}
+
 size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel) {
   if (B < 1 || Hkv < 1 || n_sel < 1 || (d != 64 && d != 128)) return 0;
   return sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel);

@@ -62,4 +62,12 @@ struct SparseDecodeArgs {
 size_t sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel);
 hipError_t launch_sparse_decode(const SparseDecodeArgs &a, hipStream_t st);
 
+// Dense causal attention (every block up to the query's own): the sparse
+// kernel with the block list replaced by 0..i.
+hipError_t launch_dense_prefill(const SparsePrefillArgs &a, hipStream_t st);
+
+// Measured-ceiling microkernels (not on the attention path).
+hipError_t launch_ceiling_mfma(int workgroups, int iters, float *out, hipStream_t st);
+hipError_t launch_ceiling_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
+
 }  // namespace sala

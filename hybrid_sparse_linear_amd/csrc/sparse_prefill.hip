@@ -53,10 +53,13 @@ struct SpCfg {
 };
 
 // One workgroup = 8 waves = 4 query heads of a GQA group x 64 query tokens.
+// DENSE: plain causal attention -- the block list is 0..i (the diagonal block
+// i is last anyway) and idx is not read; query blocks run from the last (the
+// most work) to the first.
 // Wave w owns head 4*hg + (w & 3) and query tokens 32*(w >> 2) .. +31, i.e.
 // two 16-token query tiles, so two waves share each SIMD and one wave's
 // softmax overlaps the other's MFMAs.
-template <int D>
+template <int D, bool DENSE>
 __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                         const uint16_t *__restrict__ v, const int32_t *__restrict__ idx,
                                                         uint16_t *__restrict__ o, int Hq, int Hkv, int N, int NQB,
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   const int task = (slot / HG) * 8 + (x & 7);
   const int hg = slot % HG;
   if (task >= ntasks) return;
-  const int i = task % NQB;
+  const int i = DENSE ? NQB - 1 - task % NQB : task % NQB;
   const int bkv = task / NQB;  // b * Hkv + kvh
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int G = Hq / Hkv;
@@ -90,7 +93,12 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // Block list: entries before the first negative, blocks after the query
   // block dropped, the query's own (diagonal) block moved last so that only
   // the final step needs the causal mask.
-  if (tid == 0) {
+  if (DENSE) {
+    if (tid == 0) {
+      nvalid_sh = i + 1;
+      diag_sh = 1;
+    }
+  } else if (tid == 0) {
     const int32_t *row = idx + ((size_t)bkv * NQB + i) * n_sel;
     int n = 0, has_diag = 0;
     for (int e = 0; e < n_sel; ++e) {
@@ -140,6 +148,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // keys of the diagonal block beyond every query, so causality masks them.
   // V rows use the fkv swizzle of the transposed reads.
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto blk = [&](int e) { return DENSE ? e : sel[e]; };  // e-th block to process
   const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);  // V^T fragment reads
   auto load_block = [&](int j, char *kdst, char *vdst) {
     const uint16_t *ksrc = kbase + (size_t)j * BLK * D;
@@ -238,22 +247,22 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   };
 
   if (nvalid > 0) {
-    load_block(sel[0], kb0, vb0);
+    load_block(blk(0), kb0, vb0);
     wait_loads();
     __syncthreads();
     int j = 0;
     for (; j + 2 < nvalid; j += 2) {  // blocks j (buffer 0) and j+1 (buffer 1)
-      load_block(sel[j + 1], kb1, vb1);  // lands while block j is processed
+      load_block(blk(j + 1), kb1, vb1);  // lands while block j is processed
       step(kb0, vb0, false);
       wait_loads();
       __syncthreads();
-      load_block(sel[j + 2], kb0, vb0);
+      load_block(blk(j + 2), kb0, vb0);
       step(kb1, vb1, false);
       wait_loads();
       __syncthreads();
     }
     if (j + 1 < nvalid) {  // two blocks left, the second one last
-      load_block(sel[j + 1], kb1, vb1);
+      load_block(blk(j + 1), kb1, vb1);
       step(kb0, vb0, false);
       wait_loads();
       __syncthreads();
@@ -342,6 +351,24 @@ __global__ __launch_bounds__(64) void sparse_attn_f32(const float *__restrict__ 
   }
 }
 
+template <bool DENSE>
+void launch_bf16(const SparsePrefillArgs &a, hipStream_t st) {
+  const int NQB = (a.N + BLK - 1) / BLK;
+  const int G = a.Hq / a.Hkv;
+  const int HG = (G + 3) / 4;
+  const int ntasks = a.B * a.Hkv * NQB;
+  const int grid = ((ntasks + 7) / 8) * 8 * HG;
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  if (a.d == 128)
+    hipLaunchKernelGGL((sparse_attn_bf16<128, DENSE>), dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
+                       a.n_sel, HG, ntasks, scale_log2);
+  else
+    hipLaunchKernelGGL((sparse_attn_bf16<64, DENSE>), dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
+                       a.n_sel, HG, ntasks, scale_log2);
+}
+
 }  // namespace
 
 size_t sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel) {
@@ -362,19 +389,12 @@ hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st) {
                          a.n_sel, a.scale);
     return hipGetLastError();
   }
-  const int G = a.Hq / a.Hkv;
-  const int HG = (G + 3) / 4;
-  const int ntasks = a.B * a.Hkv * NQB;
-  const int grid = ((ntasks + 7) / 8) * 8 * HG;
-  const float scale_log2 = a.scale * 1.4426950408889634f;
-  if (a.d == 128)
-    hipLaunchKernelGGL(sparse_attn_bf16<128>, dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
-                       a.n_sel, HG, ntasks, scale_log2);
-  else
-    hipLaunchKernelGGL(sparse_attn_bf16<64>, dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
-                       a.n_sel, HG, ntasks, scale_log2);
+  launch_bf16<false>(a, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_prefill(const SparsePrefillArgs &a, hipStream_t st) {
+  launch_bf16<true>(a, st);
   return hipGetLastError();
 }
 

@@ -164,6 +164,22 @@ size_t sala_sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, i
                                      int block, int n_sel);
 
 /* ------------------------------------------------------------------------
+ * sala_dense_prefill -- plain causal softmax attention over every earlier
+ * token (exact attention, the FlashAttention related-list entry): the
+ * full-attention layer the sparse layer replaces, for the layer-level
+ * comparison with the hybrid group (MiniCPM-SALA abstract: speed against
+ * full attention at 256K tokens).  The same kernel as sala_sparse_prefill
+ * with every block 0..i of query block i selected.
+ *
+ *   o_t = sum_{s <= t} softmax_s(scale * q_t . k_s) v_s, GQA as above.
+ *   dtype        SALA_BF16 only (SALA_ERR_UNSUPPORTED otherwise).
+ *   q, o         [B, Hq, N, d];  k, v  [B, Hkv, N, d];  d in {64, 128}.
+ * No workspace.
+ * ------------------------------------------------------------------------ */
+int sala_dense_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, float scale,
+                       const void *q, const void *k, const void *v, void *o, void *stream);
+
+/* ------------------------------------------------------------------------
  * sala_sparse_decode -- one query token per (b, hq) at position L-1 attends
  * to every cached token (< L) of the blocks listed in idx[b, hq/G].
  *
@@ -179,6 +195,21 @@ int sala_sparse_decode(int dtype, int B, int Hq, int Hkv, int L, int d,
 
 size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d,
                                     int block, int n_sel);
+
+/* ------------------------------------------------------------------------
+ * Measured ceilings (not on the attention path; used by the benchmark to
+ * report results against this GPU's practical peaks as well as the
+ * published ones).
+ *
+ * sala_ceiling_mfma: `workgroups` x 512 threads each run `iters` rounds of
+ *   8 independent bf16 MFMA 16x16x32 operations (16384 flops each per wave);
+ *   out [workgroups * 512] fp32 is only written on an impossible checksum.
+ *   Flops per launch: workgroups * 8 * iters * 8 * 16384.
+ * sala_ceiling_copy: copies `bytes` (a multiple of 16, both pointers 16-byte
+ *   aligned) from src to dst with 16-byte vector loads and stores.
+ * ------------------------------------------------------------------------ */
+int sala_ceiling_mfma(int workgroups, int iters, float *out, void *stream);
+int sala_ceiling_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
 const char *sala_status_string(int status);  /* static string, never NULL      */

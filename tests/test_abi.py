@@ -123,3 +123,18 @@ def test_sparse_prefill_and_decode_validation():
     assert g(BF16, 1, 128, 2, 4096, 128, 64, 67, ctypes.c_float(0.1), A, A, A, A, A, A, 1 << 30, NUL) == UNSUPPORTED
     assert g(BF16, 1, 32, 2, 4096, 128, 64, 67, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == WORKSPACE
     assert L.sala_sparse_decode_workspace(BF16, 4, 32, 2, 1 << 20, 128, 64, 67) > 0
+
+
+def test_dense_prefill_and_ceiling_validation():
+    L = _lib.lib()
+    f = L.sala_dense_prefill
+    assert f(F32, 1, 4, 2, 256, 128, ctypes.c_float(0.1), A, A, A, A, NUL) == UNSUPPORTED
+    assert f(BF16, 1, 4, 3, 256, 128, ctypes.c_float(0.1), A, A, A, A, NUL) == INVALID
+    assert f(BF16, 1, 4, 2, 256, 96, ctypes.c_float(0.1), A, A, A, A, NUL) == UNSUPPORTED
+    assert f(BF16, 1, 4, 2, 0, 128, ctypes.c_float(0.1), A, A, A, A, NUL) == INVALID
+    assert f(BF16, 1, 4, 2, 256, 128, ctypes.c_float(float("nan")), A, A, A, A, NUL) == INVALID
+    assert f(BF16, 1, 4, 2, 256, 128, ctypes.c_float(0.1), A, NUL, A, A, NUL) == INVALID
+    assert L.sala_ceiling_mfma(0, 10, A, NUL) == INVALID
+    assert L.sala_ceiling_mfma(4, 10, NUL, NUL) == INVALID
+    assert L.sala_ceiling_copy(A, A, 17, NUL) == INVALID
+    assert L.sala_ceiling_copy(NUL, A, 16, NUL) == INVALID

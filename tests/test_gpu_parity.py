@@ -274,6 +274,49 @@ def test_sparse_prefill_all_blocks_is_dense_causal():
     assert_close(o, ro, I.BF16, "dense")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 8, 2, 64 * 10 + 17, 128), (2, 4, 1, 300, 64), (1, 12, 2, 64 * 6, 128)],
+                         ids=["Hq8Hkv2N657d128", "B2Hq4Hkv1N300d64", "Hq12Hkv2N384d128"])
+def test_dense_prefill(B, Hq, Hkv, N, d):
+    """Dense causal attention (the full-attention comparison) against the
+    oracle's textbook causal softmax; ragged tail, d 64 and 128, G = 4, 4, 6."""
+    say("dense_prefill", B, Hq, Hkv, N, d)
+    x = I.sparse_inputs(B, Hq, Hkv, N, d, I.BF16, 140, 0, 1.0)
+    o = sala.dense_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]))
+    torch.cuda.synchronize()
+    ro = OS.dense_causal_attention(host64(x["q"]), host64(x["k"]), host64(x["v"]))
+    assert_close(o, ro, I.BF16, "dense")
+
+
+def test_dense_prefill_equals_sparse_with_every_block():
+    """With every block 0..i selected, the sparse kernel visits the same blocks
+    in the same order as the dense one: the outputs are bit-identical."""
+    say("dense == sparse(all blocks)")
+    B, Hq, Hkv, N, d = 1, 8, 2, 64 * 20 + 5, 128
+    x = I.sparse_inputs(B, Hq, Hkv, N, d, I.BF16, 141, 0, 1.0)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    nqb = (N + 63) // 64
+    row = torch.full((nqb, nqb), -1, dtype=torch.int32)
+    for i in range(nqb):
+        row[i, :i + 1] = torch.arange(i + 1, dtype=torch.int32)
+    idx = dev(row.expand(B, Hkv, nqb, nqb).contiguous())
+    o_sparse = sala.sparse_prefill(q, k, v, idx)
+    o_dense = sala.dense_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o_sparse, o_dense)
+
+
+def test_ceiling_microkernels():
+    """The measured-ceiling microkernels run and the copy is exact."""
+    say("ceilings")
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sala.ceiling_copy(src, dst)
+    out = torch.empty(64 * 512, dtype=torch.float32, device="cuda")
+    sala.ceiling_mfma(64, 10, out)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
 def test_sparse_end_to_end_gpu_idx():
     say("sparse end to end")
     B, Hq, Hkv, N, d, topk = 1, 16, 2, 64 * 48 + 33, 128, 8
