@@ -48,8 +48,9 @@ struct LinCfg {
   static constexpr uint32_t KN = 0;                    // K, natural [token][d_k], swizzled
   static constexpr uint32_t VN = KN + C * ROWB;        // V, natural [token][d_v], swizzled
   static constexpr uint32_t ST = VN + C * ROWB;        // bf16 S^T [d_v][d_k], swizzled
-  static constexpr uint32_t PW = ST + D * ROWB;        // lam^n, n = 0..C
-  static constexpr uint32_t RW = PW + (C + 4) * 4;     // lam^(m-1-j) for the chunk's rows, 0 past m
+  static constexpr int PWZ = 32;                        // zero entries below n = 0
+  static constexpr uint32_t PW = ST + D * ROWB;        // [PWZ zeros] lam^n, n = 0..C
+  static constexpr uint32_t RW = PW + (PWZ + C + 4) * 4;  // lam^(m-1-j) for the chunk's rows, 0 past m
   static constexpr uint32_t LDS = RW + C * 4;
   static_assert(DVW >= 1 && NSTG >= 1 && SDV >= 1, "unsupported chunk / head size");
   // wave -> (query pair, d_v part).  Waves w and w+4 share a SIMD; they get
@@ -154,9 +155,9 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
   const int h = bh % H;
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
-  float *pw = reinterpret_cast<float *>(lds + Cf::PW);
+  float *pw = reinterpret_cast<float *>(lds + Cf::PW) + Cf::PWZ;  // pw[n] = lam^n, 0 for n < 0
   float *rw = reinterpret_cast<float *>(lds + Cf::RW);
-  for (int n = tid; n <= C; n += Cf::NT) pw[n] = (float)pow((double)lam, (double)n);
+  for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);
   const uint16_t *kb = k + (size_t)bh * N * D;
   const uint16_t *vb = v + (size_t)bh * N * D;
   const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
@@ -222,9 +223,9 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   const int h = bh % H;
   const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
-  float *pw = reinterpret_cast<float *>(lds + Cf::PW);
+  float *pw = reinterpret_cast<float *>(lds + Cf::PW) + Cf::PWZ;  // pw[n] = lam^n, 0 for n < 0
   float *rw = reinterpret_cast<float *>(lds + Cf::RW);
-  for (int n = tid; n <= C; n += Cf::NT) pw[n] = (float)pow((double)lam, (double)n);
+  for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t *qb = q + head_off, *kb = k + head_off, *vb = v + head_off;
   uint16_t *ob = o + head_off;
@@ -313,23 +314,13 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) {
         const int qq = 32 * gq + 16 * tq + lr;
-        // decay factors read unconditionally (all 8 LDS reads in flight), then
-        // the causal mask as a select -- no branch around each read
-        float f[2][4];
+        // lam^(qq-j), zero for j > qq: the table's zero entries below n = 0
+        // do the causal mask (qq - j >= -31 within the diagonal pair)
+        const int nb = qq - 32 * p - 8 * g;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[t][i] = pw[max(qq - (32 * p + 8 * g + 4 * t + i), 0)];
-            __asm__("" : "+v"(f[t][i]));  // keeps the read out of a branch
-          }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = 32 * p + 8 * g + 4 * t + i;
-            P[tq][t][i] = (j <= qq) ? P[tq][t][i] * f[t][i] : 0.f;
-          }
+          for (int i = 0; i < 4; ++i) P[tq][t][i] *= pw[nb - 4 * t - i];
         Bp[tq] = u32x4{pack_bf16x2(P[tq][0][0], P[tq][0][1]), pack_bf16x2(P[tq][0][2], P[tq][0][3]),
                        pack_bf16x2(P[tq][1][0], P[tq][1][1]), pack_bf16x2(P[tq][1][2], P[tq][1][3])};
       }
