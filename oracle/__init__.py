@@ -28,9 +28,12 @@ Modules:
   sparse  -- block pooling, block scoring, top-k block selection with forced
              initial/local blocks, and softmax attention restricted to the
              selected token set (prefill and decode).
+  neighbours -- the linear layer's QK RMS normalisation, HyPE RoPE and output
+             gate, and the layer composed with them (prefill and decode).
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle_linear.py`` and ``tests/test_oracle_sparse.py`` against
+``tests/test_oracle_linear.py``, ``tests/test_oracle_sparse.py`` and
+``tests/test_oracle_neighbours.py`` against
 exact rational brute force, closed forms, special cases that reduce to a
 library routine, or invariants.  The *choice* of the method's unstated
 details (no feature map or normaliser in linear attention, the decay form,
@@ -39,4 +42,4 @@ readings are listed in the design notes and are pinned only by the
 internal invariants, not by any number on the pages.
 """
 
-from . import linear, sparse  # noqa: F401
+from . import linear, neighbours, sparse  # noqa: F401
