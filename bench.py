@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling microkernels")
+    ap.add_argument("--no-neighbours", action="store_true", help="skip the fused / unfused neighbour comparison")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
     return ap.parse_args()
 
@@ -209,6 +210,53 @@ def bench_dense(torch, sala, sp, group_ms):
             "frac_of_peak": round(flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
             "group_speedup_vs_4_dense_layers": round(4 * ms / group_ms, 2),
             "note": "attention ops only: the 3:1 group time against four full-attention layers at 256K"}
+
+
+def bench_neighbours(torch, sala, I, x, N, reps=3):
+    """One linear layer at the group shapes with its neighbours (QK RMS norm,
+    rotate-half RoPE, output gate): fused into the layer's kernels, against the
+    unfused pipeline of standalone kernels (norm+RoPE of q, of k, the plain
+    layer, the gate) and the plain layer alone.  Mean of `reps` after a warmup."""
+    nb = I.neighbour_inputs(1, 32, N, 128, 4, 0, "cuda")
+    q, k, v, dec, o, ws = x["q"], x["k"], x["v"], x["decay"], x["o"], x["ws"]
+    qh, kh = torch.empty_like(q), torch.empty_like(k)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    def fused():
+        sala.linear_prefill_fused(q, k, v, dec, gamma_q=nb["gamma_q"], gamma_k=nb["gamma_k"], rope_base=10000.0,
+                                  gate=nb["gate"], out=o, workspace=ws, want_state=False)
+
+    def unfused():
+        sala.qk_norm_rope(q, gamma=nb["gamma_q"], rope_base=10000.0, out=qh)
+        sala.qk_norm_rope(k, gamma=nb["gamma_k"], rope_base=10000.0, out=kh)
+        sala.linear_prefill(qh, kh, v, dec, out=o, workspace=ws, want_state=False)
+        sala.output_gate(o, nb["gate"], out=o)
+
+    def plain():
+        sala.linear_prefill(q, k, v, dec, out=o, workspace=ws, want_state=False)
+
+    t_f, t_u, t_p = timed(fused), timed(unfused), timed(plain)
+    tensor = 32 * N * 128 * 2
+    # q, k, v, gate read and o written; the aggregate pass reads k and v again (all but the last segment)
+    fused_bytes = 5 * tensor + 2 * tensor * 31 // 32
+    del qh, kh, nb
+    torch.cuda.empty_cache()
+    return {"workload": "one linear layer, H=32, d=128, N=%d, bf16: QK RMS norm + RoPE (base 1e4) + output gate" % N,
+            "fused_ms": round(t_f, 3), "unfused_ms": round(t_u, 3), "plain_layer_ms": round(t_p, 3),
+            "fused_speedup_vs_unfused": round(t_u / t_f, 3),
+            "fused_algorithmic_bytes": fused_bytes,
+            "fused_hbm_tbs": round(fused_bytes / (t_f * 1e-3) / 1e12, 3),
+            "fused_hbm_frac": round(fused_bytes / (t_f * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
 
 
 def bench_decode(torch, sala, I, reps=20):
@@ -360,6 +408,8 @@ def main():
     }
     if not args.no_dense:
         out["dense_comparison"] = bench_dense(torch, sala, sp, ms)
+    if not args.no_neighbours:
+        out["neighbours"] = bench_neighbours(torch, sala, I, lin[0], N)
     if not args.no_decode:
         del lin
         torch.cuda.empty_cache()

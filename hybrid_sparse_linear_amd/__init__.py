@@ -24,7 +24,9 @@ import torch
 
 from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 
-__all__ = ["linear_prefill", "linear_decode", "sparse_select", "sparse_prefill", "sparse_decode",
+__all__ = ["linear_prefill", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
+           "output_gate", "sparse_select",
+           "sparse_prefill", "sparse_decode",
            "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
 
 
@@ -112,6 +114,76 @@ def linear_decode(q, k, v, state, decay=None, *, out=None):
     call("sala_linear_decode", _code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay), _ptr(state),
          _stream())
     return o
+
+
+def linear_prefill_fused(q, k, v, decay=None, state=None, *, gamma_q=None, gamma_k=None, eps=1e-6,
+                         rope_base=10000.0, pos0=0, gate=None, chunk=None, out=None, state_out=None,
+                         workspace=None, want_state=True):
+    """The linear layer with QK RMS norm, rotate-half RoPE (positions pos0 ..) and the
+    output gate o * sigmoid(gate) applied inside its kernels (bf16).
+
+    gamma_q, gamma_k: [d] fp32 or None; rope_base 0 / None = no RoPE; gate: like q or None.
+    Returns (o, S_out or None) as linear_prefill.
+    """
+    _dev(q, k, v, decay, state, out, state_out, gamma_q, gamma_k, gate)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if gate is not None and (gate.shape != q.shape or gate.dtype != q.dtype):
+        raise ValueError("gate must match q in shape and dtype")
+    for gname, gt in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if gt is not None and (gt.shape != (d,) or gt.dtype != torch.float32):
+            raise ValueError(f"{gname} must be a float32 [{d}] tensor")
+    chunk = chunk or (64 if d == 64 else 128)
+    dt = _code(q)
+    o = torch.empty_like(q) if out is None else out
+    so = state_out
+    if so is None and want_state:
+        so = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    nb = lib().sala_linear_prefill_workspace(dt, B, H, N, d, chunk)
+    ws = _ws(nb, workspace, q)
+    call("sala_linear_prefill_fused", dt, B, H, N, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay),
+         _ptr(state), _ptr(so), _ptr(gamma_q), _ptr(gamma_k), float(eps), float(rope_base or 0.0), int(pos0),
+         _ptr(gate), _ptr(ws), nb, _stream())
+    return o, so
+
+
+def linear_decode_fused(q, k, v, state, decay=None, *, gamma_q=None, gamma_k=None, eps=1e-6, rope_base=10000.0,
+                        pos=None, gate=None, out=None):
+    """One decode token with the neighbours fused (see linear_prefill_fused); pos: int64 [B]
+    device tensor of positions (needed with RoPE).  state is updated in place; returns o."""
+    _dev(q, k, v, state, decay, out, gamma_q, gamma_k, pos, gate)
+    B, H, d = q.shape
+    if pos is not None and (pos.dtype != torch.int64 or pos.shape != (B,)):
+        raise ValueError("pos must be an int64 [B] tensor")
+    o = torch.empty_like(q) if out is None else out
+    call("sala_linear_decode_fused", _code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay),
+         _ptr(state), _ptr(gamma_q), _ptr(gamma_k), float(eps), float(rope_base or 0.0), _ptr(pos), _ptr(gate),
+         _stream())
+    return o
+
+
+def qk_norm_rope(x, *, gamma=None, eps=1e-6, rope_base=0.0, pos0=0, out=None):
+    """Standalone RMS norm (weight gamma [d] fp32 or None) then rotate-half RoPE at
+    positions pos0 .. (rope_base 0 = none) of x [B, H, N, d]; out may be x."""
+    _dev(x, gamma, out)
+    B, H, N, d = x.shape
+    if gamma is not None and (gamma.shape != (d,) or gamma.dtype != torch.float32):
+        raise ValueError(f"gamma must be a float32 [{d}] tensor")
+    o = torch.empty_like(x) if out is None else out
+    call("sala_qk_norm_rope", _code(x), B, H, N, d, _ptr(x), _ptr(o), _ptr(gamma), float(eps),
+         float(rope_base or 0.0), int(pos0), _stream())
+    return o
+
+
+def output_gate(o, gate, *, out=None):
+    """o * sigmoid(gate), elementwise (numel a multiple of 8); out may be o."""
+    _dev(o, gate, out)
+    if gate.shape != o.shape or gate.dtype != o.dtype:
+        raise ValueError("gate must match o in shape and dtype")
+    r = torch.empty_like(o) if out is None else out
+    call("sala_output_gate", _code(o), o.numel(), _ptr(o), _ptr(gate), _ptr(r), _stream())
+    return r
 
 
 def sparse_select(q, k=None, *, k_pooled=None, L=None, block=64, topk=64, n_init=1, n_local=2, idx_out=None,

@@ -12,12 +12,17 @@ SALA_BF16 = 1
 STATUS = {0: "SALA_OK", -1: "SALA_ERR_INVALID_ARG", -2: "SALA_ERR_UNSUPPORTED", -3: "SALA_ERR_WORKSPACE",
           -4: "SALA_ERR_HIP"}
 
-_i, _p, _f, _z = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+_i, _p, _f, _z, _ll = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t, ctypes.c_longlong
 
 _SIGS = {
     "sala_linear_prefill": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_linear_prefill_workspace": (_z, [_i, _i, _i, _i, _i, _i]),
     "sala_linear_decode": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "sala_linear_prefill_fused": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _f, _f, _ll,
+                                       _p, _p, _z, _p]),
+    "sala_linear_decode_fused": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _f, _f, _p, _p, _p]),
+    "sala_qk_norm_rope": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _f, _f, _ll, _p]),
+    "sala_output_gate": (_i, [_i, _z, _p, _p, _p, _p]),
     "sala_sparse_select": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_sparse_select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_sparse_prefill": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _z, _p]),

@@ -21,6 +21,7 @@ SOURCES = [
     "sala_api.cpp",
     "linear_prefill.hip",
     "linear_decode.hip",
+    "neighbours.hip",
     "sparse_select.hip",
     "sparse_prefill.hip",
     "sparse_decode.hip",

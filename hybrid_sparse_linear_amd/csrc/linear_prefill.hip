@@ -25,6 +25,8 @@
 // fp32 path: lin_recurrent_f32 runs the recurrence S_t = lam S_{t-1} + k_t v_t^T,
 // o_t = q_t S_t token by token with one thread per d_v column (small shapes).
 
+#include <type_traits>
+
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
 
@@ -139,15 +141,167 @@ __device__ __forceinline__ void state_update(const char *lds, int sdk, int sdv0,
   }
 }
 
-// ---------------------------------------------------------------- pass 1
+// ---------------------------------------------------------------- fused neighbours
+// QK RMS normalisation and HyPE RoPE applied to q and k as they are staged,
+// and the output gate applied to o as it is stored (MiniCPM-SALA, gist.science
+// (ja) 技術概要 section 2.2 and gist.science (de) section 2,
+// "Architektur-Hybridisierung": RoPE on the linear layers, QK normalisation,
+// an output gate after every attention block).  Forms: x / sqrt(mean(x^2) +
+// eps) * gamma over the head dimension; rotate-half RoPE, feature i turned
+// with feature i + D/2 by p * base^(-2i/D) at the absolute position p;
+// o * sigmoid(g).
+struct NbK {
+  const float *gq, *gk;   // RMS-norm weights [D] or nullptr
+  float eps, rope_base;   // rope_base <= 0: no RoPE
+  long long pos0;         // absolute position of token 0
+  const uint16_t *gate;   // [B, H, N, D] bf16 gate pre-activation or nullptr
+};
+
+// Fused staging: a thread owns 16-byte piece hc (features 8hc .. 8hc+7) and
+// piece hc + HC (features D/2 + 8hc ..) of rows tid/HC + RPF*u, so the
+// rotate-half partners of its features are its own and a row's sum of
+// squares is a sum over HC consecutive lanes.
 template <int C, int D>
+struct LinF {
+  static constexpr int HC = D / 16;
+  static constexpr int RPF = 512 / HC;
+  static constexpr int NSF = (C + RPF - 1) / RPF;
+  // tables after the plain layout: Q rows, gamma_q | gamma_k, theta_i / 2pi (fp64, fp32)
+  static constexpr uint32_t QN = (LinCfg<C, D>::LDS + 15u) & ~15u;
+  static constexpr uint32_t GAM = QN + C * LinCfg<C, D>::ROWB;
+  static constexpr uint32_t TRV = GAM + 2 * D * 4;
+  static constexpr uint32_t TRF = TRV + (D / 2) * 8;
+  static constexpr uint32_t LDS = TRF + (D / 2) * 4;
+};
+
+// xr: buffer resource over one head's [N, D] rows
+template <int C, int D>
+__device__ __forceinline__ void load_rows_f(__amdgpu_buffer_rsrc_t xr, int tid, int c0, int t_end,
+                                            u32x4 (&x)[LinF<C, D>::NSF][2]) {
+  using F = LinF<C, D>;
+  const uint32_t hc = tid % F::HC;
+#pragma unroll
+  for (int u = 0; u < F::NSF; ++u) {
+    const uint32_t t = min(c0 + tid / F::HC + F::RPF * u, t_end - 1);
+    x[u][0] = bload16(xr, (t * D + 8 * hc) * 2u);
+    x[u][1] = bload16(xr, (t * D + D / 2 + 8 * hc) * 2u);
+  }
+}
+// Rows -> LDS in the plain layout (fkv-swizzled 16-byte chunks); rows at or
+// past m are written as zero.
+template <int C, int D>
+__device__ __forceinline__ void store_rows_f(char *dst, int tid, int m, const u32x4 (&x)[LinF<C, D>::NSF][2]) {
+  using F = LinF<C, D>;
+  using Cf = LinCfg<C, D>;
+  const uint32_t hc = tid % F::HC;
+  const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < F::NSF; ++u) {
+    const uint32_t row = tid / F::HC + F::RPF * u;
+    if (F::RPF * F::NSF > C && row >= (uint32_t)C) continue;
+    const bool live = (int)row < m;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t ch = hc + F::HC * h;
+      lds_store(dst, row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u, live ? x[u][h] : zero);
+    }
+  }
+}
+// theta_i / 2pi for i < D/2 (fp64 and fp32) and the norm weights into LDS.
+template <int C, int D>
+__device__ __forceinline__ void nb_tables(char *lds, int tid, const NbK &nb) {
+  using F = LinF<C, D>;
+  float *gam = reinterpret_cast<float *>(lds + F::GAM);
+  if (tid < D) gam[tid] = nb.gq ? nb.gq[tid] : 1.f;
+  else if (tid < 2 * D) gam[tid] = nb.gk ? nb.gk[tid - D] : 1.f;
+  if (tid < D / 2 && nb.rope_base > 0.f) {
+    const double t = pow((double)nb.rope_base, -2.0 * tid / D) * 0.15915494309189535;  // / 2pi
+    reinterpret_cast<double *>(lds + F::TRV)[tid] = t;
+    reinterpret_cast<float *>(lds + F::TRF)[tid] = (float)t;
+  }
+}
+// Fraction of a turn of p0 * theta_i / 2pi for this thread's features (fp64).
+template <int C, int D>
+__device__ __forceinline__ void rope_base_turns(const char *lds, int hc, long long p0, float (&b)[8]) {
+  using F = LinF<C, D>;
+  const double *trv = reinterpret_cast<const double *>(lds + F::TRV);
+  const double p = (double)p0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double x = p * trv[8 * hc + e];
+    b[e] = (float)(x - floor(x));
+  }
+}
+// One row of q or k: lo = features 8hc .., hi = features D/2 + 8hc .., in place.
+// cos / sin of the angles of this thread's features at chunk row `row`:
+// turns = base turns of the chunk (fp64-reduced) + row * theta_i / 2pi.
+template <int C, int D>
+__device__ __forceinline__ void rope_cs(const char *lds, int hc, int row, const float (&b)[8], float (&c)[8],
+                                        float (&sn)[8]) {
+  const float *trf = reinterpret_cast<const float *>(lds + LinF<C, D>::TRF);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float turns = fmaf((float)row, trf[8 * hc + e], b[e]);
+    c[e] = __builtin_amdgcn_cosf(turns);
+    sn[e] = __builtin_amdgcn_sinf(turns);
+  }
+}
+template <int C, int D>
+__device__ __forceinline__ void nb_row(const char *lds, int hc, bool norm, int which, float eps, bool rope,
+                                       const float (&c)[8], const float (&sn)[8], u32x4 &lo, u32x4 &hi) {
+  using F = LinF<C, D>;
+  if (!norm && !rope) return;  // rows pass through unchanged
+  float a[8], z[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[2 * e] = bf16lo(lo[e]);
+    a[2 * e + 1] = bf16hi(lo[e]);
+    z[2 * e] = bf16lo(hi[e]);
+    z[2 * e + 1] = bf16hi(hi[e]);
+  }
+  if (norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(z[e], z[e], fmaf(a[e], a[e], ss));
+    ss = lane_group_sum<F::HC>(ss);
+    const float r = rsqrtf(fmaf(ss, 1.f / D, eps));
+    const char *gam = lds + F::GAM + which * D * 4;
+    const f32x4 ga0 = lds_load<f32x4>(gam, 32u * hc), ga1 = lds_load<f32x4>(gam, 32u * hc + 16u);
+    const f32x4 gz0 = lds_load<f32x4>(gam, (D / 2 + 8u * hc) * 4u), gz1 = lds_load<f32x4>(gam, (D / 2 + 8u * hc) * 4u + 16u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] *= r * ga0[e];
+      a[e + 4] *= r * ga1[e];
+      z[e] *= r * gz0[e];
+      z[e + 4] *= r * gz1[e];
+    }
+  }
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ya = fmaf(-z[e], sn[e], a[e] * c[e]), yz = fmaf(a[e], sn[e], z[e] * c[e]);
+      a[e] = ya;
+      z[e] = yz;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = pack_bf16x2(a[2 * e], a[2 * e + 1]);
+    hi[e] = pack_bf16x2(z[2 * e], z[2 * e + 1]);
+  }
+}
+
+// ---------------------------------------------------------------- pass 1
+// F: k is normalised and rotated as it is staged (the fused form).
+template <int C, int D, bool F>
 __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v,
                                                          const float *__restrict__ decay,
                                                          float *__restrict__ seg_state, int H, int N,
-                                                         int seg_len, int nseg) {
+                                                         int seg_len, int nseg, NbK nb) {
   using Cf = LinCfg<C, D>;
-  __shared__ __attribute__((aligned(16))) char lds[Cf::LDS];
+  using Fz = LinF<C, D>;
+  __shared__ __attribute__((aligned(16))) char lds[F ? Fz::LDS : Cf::LDS];
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int nagg = nseg - 1;
@@ -166,16 +320,48 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
   f32x4 Sacc[Cf::SDV];
 #pragma unroll
   for (int a = 0; a < Cf::SDV; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
-  load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
-  for (int c0 = t_begin; c0 < t_end; c0 += C) {
-    const int m = min(C, t_end - c0);
-    __syncthreads();
-    store_kv<C, D>(lds, tid, m, xk, xv);
-    if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
-    __syncthreads();
-    if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
-    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+  if constexpr (F) {
+    nb_tables<C, D>(lds, tid, nb);
+    const bool norm = nb.gk != nullptr, rope = nb.rope_base > 0.f;
+    const int hc = tid % Fz::HC;
+    const auto kr = buf_rsrc(kb, (uint32_t)N * D * 2u), vr = buf_rsrc(vb, (uint32_t)N * D * 2u);
+    u32x4 xk[Fz::NSF][2], xv[Fz::NSF][2];
+    load_rows_f<C, D>(kr, tid, t_begin, t_end, xk);
+    load_rows_f<C, D>(vr, tid, t_begin, t_end, xv);
+    for (int c0 = t_begin; c0 < t_end; c0 += C) {
+      const int m = min(C, t_end - c0);
+      __syncthreads();
+      float bt[8], cs[8], sn[8];
+      if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
+#pragma unroll
+      for (int u = 0; u < Fz::NSF; ++u) {
+        const int row = tid / Fz::HC + Fz::RPF * u;
+        if (rope) rope_cs<C, D>(lds, hc, row, bt, cs, sn);
+        nb_row<C, D>(lds, hc, norm, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
+        __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
+      }
+      store_rows_f<C, D>(lds + Cf::KN, tid, m, xk);
+      store_rows_f<C, D>(lds + Cf::VN, tid, m, xv);
+      if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
+      __syncthreads();
+      if (c0 + C < t_end) {
+        load_rows_f<C, D>(kr, tid, c0 + C, t_end, xk);
+        load_rows_f<C, D>(vr, tid, c0 + C, t_end, xv);
+      }
+      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+    }
+  } else {
+    u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
+    load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
+    for (int c0 = t_begin; c0 < t_end; c0 += C) {
+      const int m = min(C, t_end - c0);
+      __syncthreads();
+      store_kv<C, D>(lds, tid, m, xk, xv);
+      if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
+      __syncthreads();
+      if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
+      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+    }
   }
   float *out = seg_state + ((size_t)bh * nseg + seg) * D * D;
 #pragma unroll
@@ -206,7 +392,10 @@ __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_stat
 }
 
 // ---------------------------------------------------------------- pass 3
-template <int C, int D>
+// F: q and k are normalised and rotated as they are staged (q then also goes
+// through LDS), and the output is gated; the gated rows are stored after the
+// state update so that the gate loads are in flight during it.
+template <int C, int D, bool F>
 __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict__ q,
                                                       const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
@@ -214,9 +403,10 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
                                                       const float *__restrict__ decay,
                                                       const float *__restrict__ seg_state,
                                                       size_t seg_stride, float *__restrict__ state_out,
-                                                      int H, int N, int seg_len, int nseg) {
+                                                      int H, int N, int seg_len, int nseg, NbK nb) {
   using Cf = LinCfg<C, D>;
-  __shared__ __attribute__((aligned(16))) char lds[Cf::LDS];
+  using Fz = LinF<C, D>;
+  __shared__ __attribute__((aligned(16))) char lds[F ? Fz::LDS : Cf::LDS];
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
@@ -245,7 +435,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
 
   // Q fragments (B operands of Q^T): query tiles 2gq, 2gq+1 of the chunk;
   // rows past t_end load a clamped row whose outputs are never stored
-  u32x4 qf[2][Cf::NDS];
+  u32x4 qf[F ? 1 : 2][F ? 1 : Cf::NDS];
   auto load_q = [&](int c0) {
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
@@ -254,14 +444,81 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
       for (int s = 0; s < Cf::NDS; ++s) qf[tq][s] = gload16(qb + (size_t)t * D + 32 * s + 8 * g);
     }
   };
-  u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
-  load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
-  load_q(t_begin);
+  // Q fragment (tq, s): held in registers (plain form) or read from the
+  // staged, transformed Q rows in LDS at each use (F, which needs the VGPRs)
+  auto qfrag = [&](int tq, int s) -> u32x4 {
+    if constexpr (F) {
+      const uint32_t row = 32 * gq + 16 * tq + lr;
+      return lds_load<u32x4>(lds + Fz::QN, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
+    } else {
+      return qf[tq][s];
+    }
+  };
+  // this lane's output rows, gated by gv when given
+  auto store_out = [&](int c0, int m, const f32x4 (&Oacc)[Cf::DVW][2], const u32x2 (&gv)[2][Cf::DVW], bool gated) {
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) {
+      const int qq = 32 * gq + 16 * tq + lr;
+      if (qq < m) {
+        uint16_t *orow = ob + (size_t)(c0 + qq) * D;
+#pragma unroll
+        for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+          f32x4 x = Oacc[dvi][tq];
+          if (gated) {
+            x[0] *= sigmoid_fast(bf16lo(gv[tq][dvi][0]));
+            x[1] *= sigmoid_fast(bf16hi(gv[tq][dvi][0]));
+            x[2] *= sigmoid_fast(bf16lo(gv[tq][dvi][1]));
+            x[3] *= sigmoid_fast(bf16hi(gv[tq][dvi][1]));
+          }
+          *reinterpret_cast<u32x2 *>(orow + 16 * (dvb + dvi) + 4 * g) =
+              u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        }
+      }
+    }
+  };
+
+  // next chunk's 16-byte staging pieces: plain layout, or (F) rows x halves
+  using XT = std::conditional_t<F, u32x4[Fz::NSF][2], u32x4[Cf::NSTG]>;
+  XT xk, xv;
+  u32x4 xq[F ? Fz::NSF : 1][2];
+  bool norm_q = false, norm_k = false, rope = false;
+  const int hc = tid % Fz::HC;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto qr = buf_rsrc(qb, head_bytes), kr = buf_rsrc(kb, head_bytes), vr = buf_rsrc(vb, head_bytes);
+  const auto gr = buf_rsrc(nb.gate ? nb.gate + head_off : qb, head_bytes);
+  if constexpr (F) {
+    nb_tables<C, D>(lds, tid, nb);
+    norm_q = nb.gq != nullptr;
+    norm_k = nb.gk != nullptr;
+    rope = nb.rope_base > 0.f;
+    load_rows_f<C, D>(kr, tid, t_begin, t_end, xk);
+    load_rows_f<C, D>(vr, tid, t_begin, t_end, xv);
+    load_rows_f<C, D>(qr, tid, t_begin, t_end, xq);
+  } else {
+    load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
+    load_q(t_begin);
+  }
 
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    store_kv<C, D>(lds, tid, m, xk, xv);
+    if constexpr (F) {
+      float bt[8], cs[8], sn[8];
+      if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
+#pragma unroll
+      for (int u = 0; u < Fz::NSF; ++u) {
+        const int row = tid / Fz::HC + Fz::RPF * u;
+        if (rope) rope_cs<C, D>(lds, hc, row, bt, cs, sn);
+        nb_row<C, D>(lds, hc, norm_q, 0, nb.eps, rope, cs, sn, xq[u][0], xq[u][1]);
+        nb_row<C, D>(lds, hc, norm_k, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
+        __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
+      }
+      store_rows_f<C, D>(lds + Fz::QN, tid, m, xq);
+      store_rows_f<C, D>(lds + Cf::KN, tid, m, xk);
+      store_rows_f<C, D>(lds + Cf::VN, tid, m, xv);
+    } else {
+      store_kv<C, D>(lds, tid, m, xk, xv);
+    }
     // bf16 copy of S^T (rows d_v, columns d_k) for the Q S product
 #pragma unroll
     for (int a = 0; a < Cf::SDV; ++a) {
@@ -271,22 +528,29 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
     }
     if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
     __syncthreads();
-    if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
+    if (c0 + C < t_end) {
+      if constexpr (F) {
+        load_rows_f<C, D>(kr, tid, c0 + C, t_end, xk);
+        load_rows_f<C, D>(vr, tid, c0 + C, t_end, xv);
+      } else {
+        load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
+      }
+    }
 
     // (1) O^T = lam^(qq+1) * S^T Q^T for d_v tiles dvb .. and both query tiles
     f32x4 Oacc[Cf::DVW][2];
 #pragma unroll
-    for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-      const uint32_t row = 16 * (dvb + dvi) + lr;
+    for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi][0] = Oacc[dvi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < Cf::NDS; ++s) {
+    for (int s = 0; s < Cf::NDS; ++s) {
+      const u32x4 q0 = qfrag(0, s), q1 = qfrag(1, s);
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        const uint32_t row = 16 * (dvb + dvi) + lr;
         const u32x4 A = lds_load<u32x4>(lds + Cf::ST, row * Cf::ROWB + (((4 * s + g) ^ fst(row)) & (Cf::NCH - 1)) * 16u);
-        a0 = mfma16x16x32(A, qf[0][s], a0);
-        a1 = mfma16x16x32(A, qf[1][s], a1);
+        Oacc[dvi][0] = mfma16x16x32(A, q0, Oacc[dvi][0]);
+        Oacc[dvi][1] = mfma16x16x32(A, q1, Oacc[dvi][1]);
       }
-      Oacc[dvi][0] = a0;
-      Oacc[dvi][1] = a1;
     }
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
@@ -302,25 +566,27 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
 #pragma unroll
         for (int t = 0; t < 2; ++t) P[tq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < Cf::NDS; ++s)
+      for (int s = 0; s < Cf::NDS; ++s) {
+        const u32x4 q0 = qfrag(0, s), q1 = qfrag(1, s);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const uint32_t row = 32 * p + pair_key(t, lr);
           const u32x4 A = lds_load<u32x4>(lds + Cf::KN, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
-          P[0][t] = mfma16x16x32(A, qf[0][s], P[0][t]);
-          P[1][t] = mfma16x16x32(A, qf[1][s], P[1][t]);
+          P[0][t] = mfma16x16x32(A, q0, P[0][t]);
+          P[1][t] = mfma16x16x32(A, q1, P[1][t]);
         }
+      }
       u32x4 Bp[2];
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) {
         const int qq = 32 * gq + 16 * tq + lr;
         // lam^(qq-j), zero for j > qq: the table's zero entries below n = 0
         // do the causal mask (qq - j >= -31 within the diagonal pair)
-        const int nb = qq - 32 * p - 8 * g;
+        const int nb0 = qq - 32 * p - 8 * g;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) P[tq][t][i] *= pw[nb - 4 * t - i];
+          for (int i = 0; i < 4; ++i) P[tq][t][i] *= pw[nb0 - 4 * t - i];
         Bp[tq] = u32x4{pack_bf16x2(P[tq][0][0], P[tq][0][1]), pack_bf16x2(P[tq][0][2], P[tq][0][3]),
                        pack_bf16x2(P[tq][1][0], P[tq][1][1]), pack_bf16x2(P[tq][1][2], P[tq][1][3])};
       }
@@ -331,21 +597,29 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
         Oacc[dvi][1] = mfma16x16x32(A, Bp[1], Oacc[dvi][1]);
       }
     }
-    if (c0 + C < t_end) load_q(c0 + C);  // the Q fragments are free from here on
-    // (4) this lane's output rows
+    if constexpr (F) {
+      // gate values of this lane's outputs (clamped rows are never stored)
+      u32x2 gv[2][Cf::DVW] = {};
+      if (nb.gate) {
 #pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      const int qq = 32 * gq + 16 * tq + lr;
-      if (qq < m) {
-        uint16_t *orow = ob + (size_t)(c0 + qq) * D;
+        for (int tq = 0; tq < 2; ++tq) {
+          const uint32_t t = min(c0 + 32 * gq + 16 * tq + lr, t_end - 1);
 #pragma unroll
-        for (int dvi = 0; dvi < Cf::DVW; ++dvi)
-          *reinterpret_cast<u32x2 *>(orow + 16 * (dvb + dvi) + 4 * g) =
-              u32x2{pack_bf16x2(Oacc[dvi][tq][0], Oacc[dvi][tq][1]), pack_bf16x2(Oacc[dvi][tq][2], Oacc[dvi][tq][3])};
+          for (int dvi = 0; dvi < Cf::DVW; ++dvi) gv[tq][dvi] = bload8(gr, (t * D + 16 * (dvb + dvi) + 4 * g) * 2u);
+        }
       }
+      if (c0 + C < t_end) load_rows_f<C, D>(qr, tid, c0 + C, t_end, xq);
+      // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V, then (4) the gated output rows
+      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+      store_out(c0, m, Oacc, gv, nb.gate != nullptr);
+    } else {
+      if (c0 + C < t_end) load_q(c0 + C);  // the Q fragments are free from here on
+      // (4) this lane's output rows
+      const u32x2 nogate[2][Cf::DVW] = {};
+      store_out(c0, m, Oacc, nogate, false);
+      // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V
+      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
     }
-    // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V
-    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
   }
 
   if (state_out && seg == nseg - 1) {
@@ -411,8 +685,8 @@ void seg_plan(int BH, int N, int C, int *seg_len, int *nseg) {
   *nseg = (N + *seg_len - 1) / *seg_len;
 }
 
-template <int C, int D>
-hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+template <int C, int D, bool F>
+hipError_t run_bf16(const LinearPrefillArgs &a, const NbK &nb, hipStream_t st) {
   const int BH = a.B * a.H;
   int seg_len, nseg;
   seg_plan(BH, a.N, C, &seg_len, &nseg);
@@ -420,16 +694,25 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   const size_t DD = (size_t)D * D;
   const float *seg_state = a.state_in;  // nseg == 1: segment 0 starts from state_in
   if (nseg > 1) {
-    hipLaunchKernelGGL((lin_seg_aggregate<C, D>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg);
+    hipLaunchKernelGGL((lin_seg_aggregate<C, D, F>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws,
                        a.state_in, a.decay, a.H, (int)DD, a.N, seg_len, nseg);
     seg_state = ws;
   }
-  hipLaunchKernelGGL((lin_seg_output<C, D>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
+  hipLaunchKernelGGL((lin_seg_output<C, D, F>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, DD,
-                     a.state_out, a.H, a.N, seg_len, nseg);
+                     a.state_out, a.H, a.N, seg_len, nseg, nb);
   return hipGetLastError();
+}
+
+template <int C, int D>
+hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+  NbK nb{nullptr, nullptr, 0.f, 0.f, 0, nullptr};
+  if (!a.nb) return run_bf16<C, D, false>(a, nb, st);
+  nb = NbK{a.nb->gamma_q, a.nb->gamma_k, a.nb->eps, a.nb->rope_base, a.nb->pos0,
+           static_cast<const uint16_t *>(a.nb->gate)};
+  return run_bf16<C, D, true>(a, nb, st);
 }
 
 }  // namespace

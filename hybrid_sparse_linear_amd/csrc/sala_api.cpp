@@ -132,6 +132,92 @@ int sala_linear_decode(int dtype, int B, int H, int d, const void *q, const void
   return hip_status(sala::launch_linear_decode(a, static_cast<hipStream_t>(stream)), "sala_linear_decode launch");
 }
 
+namespace {
+int check_neighbours(const float *gamma_q, const float *gamma_k, float eps, float rope_base, const void *gate) {
+  OPT_PTR(gamma_q, "gamma_q");
+  OPT_PTR(gamma_k, "gamma_k");
+  OPT_PTR(gate, "gate");
+  REQUIRE(eps >= 0.f && eps < 1e30f, SALA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  REQUIRE(rope_base == 0.f || (rope_base > 1.f && rope_base < 1e30f), SALA_ERR_INVALID_ARG,
+          "rope_base must be 0 (no RoPE) or a finite base > 1");
+  return SALA_OK;
+}
+}  // namespace
+
+int sala_linear_prefill_fused(int dtype, int B, int H, int N, int d, int chunk, const void *q, const void *k,
+                              const void *v, void *o, const float *decay, const float *state_in, float *state_out,
+                              const float *gamma_q, const float *gamma_k, float eps, float rope_base, long long pos0,
+                              const void *gate, void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(dtype == SALA_BF16, SALA_ERR_UNSUPPORTED, "the fused linear prefill is bf16 only");
+  REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if ((s = check_d(d))) return s;
+  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: this build supports 64 and 128", chunk);
+  REQUIRE((long long)N * d * 2 < (1ll << 31), SALA_ERR_UNSUPPORTED, "one head's rows must stay under 2 GiB");
+  REQUIRE(pos0 >= 0 && pos0 < (1ll << 40), SALA_ERR_INVALID_ARG, "pos0 must be in [0, 2^40)");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(o, "o");
+  OPT_PTR(decay, "decay");
+  OPT_PTR(state_in, "state_in");
+  OPT_PTR(state_out, "state_out");
+  if ((s = check_neighbours(gamma_q, gamma_k, eps, rope_base, gate))) return s;
+  if ((s = check_ws(ws, ws_bytes, sala::linear_prefill_workspace(dtype, B, H, N, d, chunk)))) return s;
+  sala::LinearNeighbours nb{gamma_q, gamma_k, eps, rope_base, pos0, nullptr, gate};
+  sala::LinearPrefillArgs a{dtype, B, H, N, d, chunk, q, k, v, o, decay, state_in, state_out, ws, &nb};
+  return hip_status(sala::launch_linear_prefill(a, static_cast<hipStream_t>(stream)),
+                    "sala_linear_prefill_fused launch");
+}
+
+int sala_linear_decode_fused(int dtype, int B, int H, int d, const void *q, const void *k, const void *v, void *o,
+                             const float *decay, float *state, const float *gamma_q, const float *gamma_k, float eps,
+                             float rope_base, const long long *pos, const void *gate, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(B >= 1 && H >= 1, SALA_ERR_INVALID_ARG, "B, H must be >= 1");
+  if ((s = check_d(d))) return s;
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(state, "state");
+  OPT_PTR(decay, "decay");
+  if ((s = check_neighbours(gamma_q, gamma_k, eps, rope_base, gate))) return s;
+  REQUIRE(rope_base == 0.f || pos, SALA_ERR_INVALID_ARG, "pos must not be NULL when rope_base > 0");
+  OPT_PTR(pos, "pos");
+  sala::LinearNeighbours nb{gamma_q, gamma_k, eps, rope_base, 0, pos, gate};
+  sala::LinearDecodeArgs a{dtype, B, H, d, q, k, v, o, decay, state, &nb};
+  return hip_status(sala::launch_linear_decode(a, static_cast<hipStream_t>(stream)), "sala_linear_decode_fused launch");
+}
+
+int sala_qk_norm_rope(int dtype, int B, int H, int N, int d, const void *x, void *out, const float *gamma, float eps,
+                      float rope_base, long long pos0, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if ((s = check_d(d))) return s;
+  REQUIRE(pos0 >= 0 && pos0 < (1ll << 40), SALA_ERR_INVALID_ARG, "pos0 must be in [0, 2^40)");
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(out, "out");
+  if ((s = check_neighbours(gamma, nullptr, eps, rope_base, nullptr))) return s;
+  sala::QkNormRopeArgs a{dtype, B, H, N, d, x, out, gamma, eps, rope_base, pos0};
+  return hip_status(sala::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream)), "sala_qk_norm_rope launch");
+}
+
+int sala_output_gate(int dtype, size_t n, const void *o, const void *gate, void *out, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(n >= 1 && n % 8 == 0, SALA_ERR_INVALID_ARG, "n = %zu must be a positive multiple of 8", n);
+  REQUIRE(n / 8 < (1ull << 38), SALA_ERR_INVALID_ARG, "n too large");
+  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(gate, "gate");
+  REQUIRE_PTR(out, "out");
+  return hip_status(sala::launch_output_gate(dtype, n, o, gate, out, static_cast<hipStream_t>(stream)),
+                    "sala_output_gate launch");
+}
+
 size_t sala_sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk,
                                     int n_init, int n_local) {
   if (B < 1 || Hkv < 1 || L < 1 || block < 1 || (Nq != 1 && Nq != L)) return 0;

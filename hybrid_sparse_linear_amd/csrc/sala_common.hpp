@@ -104,6 +104,19 @@ __device__ __forceinline__ int pair_key(int t, int r) { return ((r >> 2) << 3) +
 __device__ __forceinline__ u32x4 gload16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void gstore16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// Buffer loads: a resource over [p, p + bytes) (bytes < 2^31) held in SGPRs
+// and a 32-bit byte offset per lane, so per-lane addresses cost one VGPR
+// instead of two; loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // ---------------------------------------------------------------- wave reductions (wave64)
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -114,6 +127,24 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// Sum over aligned groups of G consecutive lanes (G = 4 or 8), every lane of
+// a group receiving the group's sum: DPP quad permutations [1,0,3,2] and
+// [2,3,0,1], then (G = 8) the half-row mirror, which pairs each lane with one
+// of the other quad.
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(G == 4 || G == 8, "group of 4 or 8 lanes");
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  if constexpr (G == 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
+// 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
 // Order-preserving map fp32 -> uint32 (larger float => larger key); -0 maps as +0.

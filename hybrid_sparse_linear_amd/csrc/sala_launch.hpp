@@ -8,6 +8,19 @@
 
 namespace sala {
 
+// The linear layer's neighbours, applied inside its kernels: RMS norm of q
+// and k over the head dimension (weights gamma_q / gamma_k, nullptr = none),
+// rotate-half RoPE at absolute positions (rope_base <= 0: none) and the output
+// gate o * sigmoid(gate) (gate nullptr: none).
+struct LinearNeighbours {
+  const float *gamma_q, *gamma_k;
+  float eps;
+  float rope_base;
+  long long pos0;          // prefill: position of token 0
+  const long long *pos;    // decode: device array [B] of positions
+  const void *gate;        // same layout and dtype as o
+};
+
 struct LinearPrefillArgs {
   int dtype, B, H, N, d, chunk;
   const void *q, *k, *v;
@@ -15,9 +28,21 @@ struct LinearPrefillArgs {
   const float *decay, *state_in;
   float *state_out;
   void *ws;
+  const LinearNeighbours *nb;  // nullptr: the plain layer
 };
 size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk);
 hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st);
+
+struct QkNormRopeArgs {
+  int dtype, B, H, N, d;
+  const void *x;
+  void *out;
+  const float *gamma;
+  float eps, rope_base;
+  long long pos0;
+};
+hipError_t launch_qk_norm_rope(const QkNormRopeArgs &a, hipStream_t st);
+hipError_t launch_output_gate(int dtype, size_t n, const void *o, const void *g, void *out, hipStream_t st);
 
 struct LinearDecodeArgs {
   int dtype, B, H, d;
@@ -25,6 +50,7 @@ struct LinearDecodeArgs {
   void *o;
   const float *decay;
   float *state;
+  const LinearNeighbours *nb;  // nullptr: the plain step
 };
 hipError_t launch_linear_decode(const LinearDecodeArgs &a, hipStream_t st);
 

@@ -9,7 +9,8 @@ Recipe (every draw is fp32 from ``torch.randn`` with a seeded
 once to the target dtype with round-to-nearest-even):
 
   seed = 1000 * workload + 100 * layer + tensor id
-         tensor ids: q 0, k 1, v 2, shift direction 3, shifted-block set 4, state 5
+         tensor ids: q 0, k 1, v 2, shift direction 3, shifted-block set 4, state 5,
+                     gamma_q 6, gamma_k 7, gate 8
 
   workload 1  tiny group, fp32, B=1, H=4, d=64, N=2048, q/k/v ~ N(0,1)/8.
               Linear decay per head [1.0, 0.99, 1.0, 0.99], chunk 64.
@@ -70,6 +71,16 @@ def linear_inputs(B, H, N, d, dtype, workload, layer, std, device="cpu", decay=N
     k = normal((B, H, N, d), seed_of(workload, layer, 1), std, dtype, device)
     v = normal((B, H, N, d), seed_of(workload, layer, 2), std, dtype, device)
     return {"q": q, "k": k, "v": v, "decay": decay}
+
+
+def neighbour_inputs(B, H, N, d, workload, layer, device="cpu"):
+    """The linear layer's neighbour tensors: RMS-norm weights gamma_q, gamma_k [d]
+    (fp32, 1/sqrt(d) * (1 + 0.25 z), so normalised rows keep the workloads' input
+    scale) and a gate pre-activation [B, H, N, d] ~ N(0, 1) in bf16."""
+    gq = normal((d,), seed_of(workload, layer, 6), 0.25, F32, device).add_(1.0).mul_(1.0 / math.sqrt(d))
+    gk = normal((d,), seed_of(workload, layer, 7), 0.25, F32, device).add_(1.0).mul_(1.0 / math.sqrt(d))
+    gate = normal((B, H, N, d), seed_of(workload, layer, 8), 1.0, BF16, device)
+    return {"gamma_q": gq, "gamma_k": gk, "gate": gate}
 
 
 def sparse_inputs(B, Hq, Hkv, N, d, dtype, workload, layer, std=1.0, device="cpu",

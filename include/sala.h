@@ -102,6 +102,68 @@ int sala_linear_decode(int dtype, int B, int H, int d,
                        const float *decay, float *state, void *stream);
 
 /* ------------------------------------------------------------------------
+ * sala_linear_prefill_fused / sala_linear_decode_fused -- the linear layer
+ * with its neighbours applied inside the kernels, so q, k and o make no
+ * extra round trip through memory.  The pages add QK normalisation and an
+ * output gate after every attention block, and give the linear layers
+ * rotary position embedding (HyPE: none on the sparse layers)
+ * (MiniCPM-SALA, gist.science (ja) 技術概要 section 2.2; gist.science (de)
+ * section 2, "Architektur-Hybridisierung").  Forms used here:
+ *   x_hat  = x / sqrt(mean_i x_i^2 + eps) * gamma          (q with gamma_q,
+ *            k with gamma_k; NULL gamma: that vector is not normalised)
+ *   RoPE   rotate-half: feature i < d/2 is turned with feature i + d/2 by
+ *          p * rope_base^(-2i/d) at the token's absolute position p
+ *          (rope_base 0: no RoPE); applied after the normalisation
+ *   o      <- o * sigmoid(gate)  elementwise (gate NULL: no gate)
+ * then the decayed linear attention of sala_linear_prefill / _decode runs on
+ * the transformed q and k (v untouched).  The transformed q and k are
+ * rounded to bf16 once, as an unfused producer would store them.
+ *
+ * prefill: as sala_linear_prefill, bf16 only (SALA_ERR_UNSUPPORTED for fp32);
+ *   the tokens sit at positions pos0 .. pos0 + N - 1 (pos0 in [0, 2^40));
+ *   gate [B, H, N, d] bf16 or NULL; gamma_q, gamma_k [d] fp32 or NULL;
+ *   one head's rows N * d * 2 bytes must stay under 2 GiB.  Same workspace
+ *   as sala_linear_prefill (sala_linear_prefill_workspace).
+ * decode: as sala_linear_decode (bf16 or fp32); pos [B] int64 device array of
+ *   the token positions (required when rope_base > 0); gate [B, H, d] of dtype
+ *   or NULL.  The state is updated in place.
+ * Errors: eps negative or not finite, rope_base neither 0 nor a finite base
+ * > 1, misaligned optional pointers: SALA_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------ */
+int sala_linear_prefill_fused(int dtype, int B, int H, int N, int d, int chunk,
+                              const void *q, const void *k, const void *v, void *o,
+                              const float *decay, const float *state_in, float *state_out,
+                              const float *gamma_q, const float *gamma_k, float eps,
+                              float rope_base, long long pos0, const void *gate,
+                              void *ws, size_t ws_bytes, void *stream);
+
+int sala_linear_decode_fused(int dtype, int B, int H, int d,
+                             const void *q, const void *k, const void *v, void *o,
+                             const float *decay, float *state,
+                             const float *gamma_q, const float *gamma_k, float eps,
+                             float rope_base, const long long *pos, const void *gate,
+                             void *stream);
+
+/* ------------------------------------------------------------------------
+ * sala_qk_norm_rope -- the same neighbours as standalone streaming kernels,
+ * for the sparse layers (QK normalisation without RoPE, per HyPE) and for an
+ * unfused pipeline (MiniCPM-SALA, gist.science (ja) 技術概要 section 2.2;
+ * gist.science (de) section 2, "Architektur-Hybridisierung").
+ *   x, out  [B, H, N, d] of dtype (out may be x): per row, the RMS norm with
+ *           weight gamma [d] fp32 (NULL: none), then rotate-half RoPE at
+ *           position pos0 + t for token t (rope_base 0: none); same forms and
+ *           errors as the fused calls.
+ * sala_output_gate -- out = o * sigmoid(gate), elementwise over n elements of
+ *   dtype (n a positive multiple of 8; out may be o).
+ * ------------------------------------------------------------------------ */
+int sala_qk_norm_rope(int dtype, int B, int H, int N, int d, const void *x, void *out,
+                      const float *gamma, float eps, float rope_base, long long pos0,
+                      void *stream);
+
+int sala_output_gate(int dtype, size_t n, const void *o, const void *gate, void *out,
+                     void *stream);
+
+/* ------------------------------------------------------------------------
  * sala_sparse_select -- block selection for the sparse layer.
  *
  * The sparse layers use InfLLM-V2, which adds no parameters and reaches the

@@ -138,3 +138,65 @@ def test_dense_prefill_and_ceiling_validation():
     assert L.sala_ceiling_mfma(4, 10, NUL, NUL) == INVALID
     assert L.sala_ceiling_copy(A, A, 17, NUL) == INVALID
     assert L.sala_ceiling_copy(NUL, A, 16, NUL) == INVALID
+
+
+def lpf(**kw):
+    a = dict(dtype=BF16, B=1, H=2, N=256, d=128, chunk=128, q=A, k=A, v=A, o=A, decay=NUL, sin=NUL, sout=NUL,
+             gq=NUL, gk=NUL, eps=1e-6, base=10000.0, pos0=0, gate=NUL, ws=NUL, wsb=0)
+    a.update(kw)
+    return _lib.lib().sala_linear_prefill_fused(
+        a["dtype"], a["B"], a["H"], a["N"], a["d"], a["chunk"], a["q"], a["k"], a["v"], a["o"], a["decay"], a["sin"],
+        a["sout"], a["gq"], a["gk"], a["eps"], a["base"], a["pos0"], a["gate"], a["ws"], a["wsb"], NUL)
+
+
+def ldf(**kw):
+    a = dict(dtype=BF16, B=2, H=2, d=128, q=A, k=A, v=A, o=A, decay=NUL, state=A, gq=NUL, gk=NUL, eps=1e-6,
+             base=10000.0, pos=A, gate=NUL)
+    a.update(kw)
+    return _lib.lib().sala_linear_decode_fused(a["dtype"], a["B"], a["H"], a["d"], a["q"], a["k"], a["v"], a["o"],
+                                               a["decay"], a["state"], a["gq"], a["gk"], a["eps"], a["base"],
+                                               a["pos"], a["gate"], NUL)
+
+
+def test_fused_linear_validation():
+    assert lpf(dtype=F32) == UNSUPPORTED
+    assert lpf(dtype=5) == INVALID
+    assert lpf(N=0) == INVALID
+    assert lpf(d=80) == UNSUPPORTED
+    assert lpf(eps=-1.0) == INVALID
+    assert lpf(eps=float("nan")) == INVALID
+    assert lpf(base=0.5) == INVALID and b"rope_base" in _lib.lib().sala_last_error()
+    assert lpf(base=float("nan")) == INVALID
+    assert lpf(pos0=-1) == INVALID
+    assert lpf(gate=MIS) == INVALID
+    assert lpf(gq=MIS) == INVALID
+    assert lpf(N=16 * 1024 * 1024, H=1) == UNSUPPORTED  # one head's rows past 2 GiB
+    assert lpf(B=1, H=32, N=32768, ws=NUL, wsb=0) == WORKSPACE
+    assert ldf(dtype=3) == INVALID
+    assert ldf(pos=NUL) == INVALID and b"pos" in _lib.lib().sala_last_error()
+    assert ldf(state=NUL) == INVALID
+    assert ldf(base=1.0) == INVALID
+    assert ldf(gk=MIS) == INVALID
+    assert ldf(d=32) == UNSUPPORTED
+
+
+def test_standalone_neighbour_validation():
+    L = _lib.lib()
+    nr = lambda **kw: L.sala_qk_norm_rope(kw.get("dtype", BF16), kw.get("B", 1), kw.get("H", 2), kw.get("N", 10),
+                                          kw.get("d", 128), kw.get("x", A), kw.get("out", A), kw.get("gamma", NUL),
+                                          kw.get("eps", 1e-6), kw.get("base", 10000.0), kw.get("pos0", 0), NUL)
+    assert nr(dtype=9) == INVALID
+    assert nr(N=0) == INVALID
+    assert nr(d=100) == UNSUPPORTED
+    assert nr(x=NUL) == INVALID
+    assert nr(out=MIS) == INVALID
+    assert nr(gamma=MIS) == INVALID
+    assert nr(base=-3.0) == INVALID
+    assert nr(pos0=-5) == INVALID
+    og = lambda **kw: L.sala_output_gate(kw.get("dtype", BF16), kw.get("n", 64), kw.get("o", A), kw.get("g", A),
+                                         kw.get("out", A), NUL)
+    assert og(n=0) == INVALID
+    assert og(n=12) == INVALID and b"multiple of 8" in L.sala_last_error()
+    assert og(g=NUL) == INVALID
+    assert og(out=MIS) == INVALID
+    assert og(dtype=2) == INVALID
