@@ -316,12 +316,63 @@ def bench_decode(torch, sala, I, reps=20):
     times.sort()
     us = times[len(times) // 2]
     nbytes = 3 * (2 * 4 * 32 * 128 * 128 * 4) + 4 * 2 * 16384 * 128 * 4 + 4 * 2 * 67 * 64 * 128 * 2 * 2
-    return {"workload": "decode step at L=1048576, B=4: 3 linear decode (H=32, d=128 fp32 state) + select over "
-                        "16384 pooled blocks + attention over 64+1+2 blocks (Hq=32, Hkv=2)",
-            "us_per_step_median": round(us, 2), "algorithmic_bytes": nbytes,
-            "hbm_frac": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
-            "timing": "HIP events around one replay of the captured step (HIP graph), median of 20 reps, "
-                      "1 GiB read between reps", "graph_replay_matches_eager": replay_ok}
+    out = {"workload": "decode step at L=1048576, B=4: 3 linear decode (H=32, d=128 fp32 state) + select over "
+                       "16384 pooled blocks + attention over 64+1+2 blocks (Hq=32, Hkv=2)",
+           "us_per_step_median": round(us, 2), "algorithmic_bytes": nbytes,
+           "hbm_frac": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+           "timing": "HIP events around one replay of the captured step (HIP graph), median of 20 reps, "
+                     "1 GiB read between reps", "graph_replay_matches_eager": replay_ok}
+
+    # The same step as a generation loop runs it: the linear layers with QK norm,
+    # RoPE at position L-1 and the gate fused in, and the sparse layer appending
+    # the token's k, v to the cache and updating its block's pooled key first.
+    nb = I.neighbour_inputs(4, 32, 1, 128, 5, 0, "cuda")
+    gate = nb["gate"][:, :, 0].contiguous()
+    pos = torch.full((4,), L - 1, dtype=torch.int64, device="cuda")
+    k_new = sp["k_cache"][:, :, L - 1].clone()
+    v_new = sp["v_cache"][:, :, L - 1].clone()
+    idx1 = torch.empty((4, 2, 67), dtype=torch.int32, device="cuda")
+    o2 = torch.empty_like(q)
+    ws_step = torch.empty(sala.workspace_bytes("sparse_decode_step", dtype=1, B=4, Hq=32, Hkv=2, capacity=L, d=128,
+                                               block=64, topk=64, n_init=1, n_local=2), dtype=torch.uint8,
+                          device="cuda")
+
+    def gen_step():
+        for x in lin:
+            sala.linear_decode_fused(x["q"], x["k"], x["v"], x["state"], x["decay"], gamma_q=nb["gamma_q"],
+                                     gamma_k=nb["gamma_k"], rope_base=10000.0, pos=pos, gate=gate, out=x["o"])
+        sala.sparse_decode_step(q, k_new, v_new, sp["k_cache"], sp["v_cache"], kp, L - 1, idx_out=idx1, out=o2,
+                                workspace=ws_step)
+
+    for _ in range(3):
+        gen_step()
+    torch.cuda.synchronize()
+    gen_ok = bool(torch.equal(o2, o_eager))  # the appended token equals the cache's last row
+    graph2 = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gen_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph2):
+        gen_step()
+    graph2.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        sink.add_(flush.sum())
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        graph2.replay()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) * 1000.0)
+    times.sort()
+    out["generation_step"] = {
+        "workload": "the same step inside a generation loop: fused linear decode (QK RMS norm, RoPE at L-1, gate) "
+                    "x3 + sala_sparse_decode_step (append k, v at L-1, pooled-key update, select, attend)",
+        "us_per_step_median": round(times[len(times) // 2], 2), "matches_plain_step": gen_ok}
+    return out
 
 
 def main():

@@ -25,7 +25,7 @@ import torch
 from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 
 __all__ = ["linear_prefill", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
-           "output_gate", "sparse_select",
+           "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_select",
            "sparse_prefill", "sparse_decode",
            "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
 
@@ -80,6 +80,13 @@ def workspace_bytes(op, **kw):
     if op == "sparse_decode":
         return L.sala_sparse_decode_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["L"], kw["d"],
                                               kw["block"], kw["n_sel"])
+    if op == "sparse_prefill_chunk":
+        return L.sala_sparse_prefill_chunk_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["capacity"],
+                                                     kw["d"], kw["n"], kw["block"], kw["topk"], kw["n_init"],
+                                                     kw["n_local"])
+    if op == "sparse_decode_step":
+        return L.sala_sparse_decode_step_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["capacity"],
+                                                   kw["d"], kw["block"], kw["topk"], kw["n_init"], kw["n_local"])
     raise ValueError(op)
 
 
@@ -252,6 +259,62 @@ def sparse_decode(q, k_cache, v_cache, idx, *, L=None, block=64, scale=None, out
     call("sala_sparse_decode", dt, B, Hq, Hkv, L, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k_cache),
          _ptr(v_cache), _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
     return o
+
+
+def _cache_dims(k_cache, v_cache, k_pooled, block):
+    B, Hkv, cap, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must share shape and dtype")
+    if k_pooled.dtype != torch.float32 or tuple(k_pooled.shape) != (B, Hkv, (cap + block - 1) // block, d):
+        raise ValueError("k_pooled must be float32 [B, Hkv, ceil(capacity / block), d]")
+    return B, Hkv, cap, d
+
+
+def sparse_prefill_chunk(q, k_new, v_new, k_cache, v_cache, k_pooled, pos0, *, block=64, topk=64, n_init=1,
+                         n_local=2, scale=None, idx_out=None, out=None, workspace=None):
+    """Tokens pos0 .. pos0+n-1 of a sequence whose earlier tokens sit in the caches:
+    q [B, Hq, n, d], k_new, v_new [B, Hkv, n, d] are written into k_cache, v_cache
+    [B, Hkv, capacity, d]; k_pooled [B, Hkv, ceil(capacity/64), d] fp32 is updated.
+    Returns (o [B, Hq, n, d], idx [B, Hkv, ceil(n/64), n_sel])."""
+    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out)
+    B, Hkv, cap, d = _cache_dims(k_cache, v_cache, k_pooled, block)
+    Hq, n = q.shape[1], q.shape[2]
+    if k_new.shape != (B, Hkv, n, d) or v_new.shape != (B, Hkv, n, d):
+        raise ValueError("k_new, v_new must be [B, Hkv, n, d]")
+    n_sel = topk + n_init + n_local
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _code(q)
+    o = torch.empty_like(q) if out is None else out
+    idx = idx_out if idx_out is not None else torch.empty((B, Hkv, (n + block - 1) // block, n_sel),
+                                                         dtype=torch.int32, device=q.device)
+    nb = lib().sala_sparse_prefill_chunk_workspace(dt, B, Hq, Hkv, cap, d, n, block, topk, n_init, n_local)
+    ws = _ws(nb, workspace, q)
+    call("sala_sparse_prefill_chunk", dt, B, Hq, Hkv, cap, d, int(pos0), n, block, topk, n_init, n_local,
+         ctypes.c_float(scale), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_pooled),
+         _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
+    return o, idx
+
+
+def sparse_decode_step(q, k_new, v_new, k_cache, v_cache, k_pooled, pos, *, block=64, topk=64, n_init=1,
+                       n_local=2, scale=None, idx_out=None, out=None, workspace=None):
+    """One generated token at position pos: q [B, Hq, d], k_new, v_new [B, Hkv, d] are
+    appended to the caches (see sparse_prefill_chunk).  Returns (o [B, Hq, d], idx [B, Hkv, n_sel])."""
+    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out)
+    B, Hkv, cap, d = _cache_dims(k_cache, v_cache, k_pooled, block)
+    Hq = q.shape[1]
+    if k_new.shape != (B, Hkv, d) or v_new.shape != (B, Hkv, d):
+        raise ValueError("k_new, v_new must be [B, Hkv, d]")
+    n_sel = topk + n_init + n_local
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _code(q)
+    o = torch.empty_like(q) if out is None else out
+    idx = idx_out if idx_out is not None else torch.empty((B, Hkv, n_sel), dtype=torch.int32, device=q.device)
+    nb = lib().sala_sparse_decode_step_workspace(dt, B, Hq, Hkv, cap, d, block, topk, n_init, n_local)
+    ws = _ws(nb, workspace, q)
+    call("sala_sparse_decode_step", dt, B, Hq, Hkv, cap, d, int(pos), block, topk, n_init, n_local,
+         ctypes.c_float(scale), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_pooled),
+         _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
+    return o, idx
 
 
 def dense_prefill(q, k, v, *, scale=None, out=None):

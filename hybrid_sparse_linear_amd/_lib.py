@@ -23,6 +23,12 @@ _SIGS = {
     "sala_linear_decode_fused": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _f, _f, _p, _p, _p]),
     "sala_qk_norm_rope": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _f, _f, _ll, _p]),
     "sala_output_gate": (_i, [_i, _z, _p, _p, _p, _p]),
+    "sala_sparse_prefill_chunk_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "sala_sparse_prefill_chunk": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p,
+                                       _p, _p, _p, _z, _p]),
+    "sala_sparse_decode_step_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "sala_sparse_decode_step": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p,
+                                     _p, _p, _z, _p]),
     "sala_sparse_select": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_sparse_select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_sparse_prefill": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _z, _p]),

@@ -331,4 +331,116 @@ int sala_sparse_decode(int dtype, int B, int Hq, int Hkv, int L, int d, int bloc
   return hip_status(sala::launch_sparse_decode(a, static_cast<hipStream_t>(stream)), "sala_sparse_decode launch");
 }
 
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t step_select_ws(int dtype, int B, int Hq, int Hkv, int d, int L, int block, int topk, int n_init, int n_local) {
+  return align256(sala::sparse_select_workspace(dtype, B, Hq, Hkv, d, 1, L, block, topk, n_init, n_local, false));
+}
+}  // namespace
+
+size_t sala_sparse_decode_step_workspace(int dtype, int B, int Hq, int Hkv, int capacity, int d, int block, int topk,
+                                         int n_init, int n_local) {
+  if (B < 1 || Hkv < 1 || Hq < 1 || capacity < 1 || block != 64 || (d != 64 && d != 128) || topk < 0 ||
+      n_init < 0 || n_local < 0 || topk + n_init + n_local < 1)
+    return 0;
+  const int n_sel = topk + n_init + n_local;
+  return step_select_ws(dtype, B, Hq, Hkv, d, capacity, block, topk, n_init, n_local) +
+         sala::sparse_decode_workspace(dtype, B, Hq, Hkv, capacity, d, block, n_sel);
+}
+
+int sala_sparse_decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block, int topk,
+                            int n_init, int n_local, float scale, const void *q, const void *k_new, const void *v_new,
+                            void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o, void *ws,
+                            size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_sparse_common(B, Hq, Hkv, block, topk, "topk"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(capacity >= 1, SALA_ERR_INVALID_ARG, "capacity must be >= 1");
+  REQUIRE(pos >= 0 && pos < capacity, SALA_ERR_INVALID_ARG, "pos = %d must be in [0, capacity = %d)", pos, capacity);
+  REQUIRE(n_init >= 0 && n_local >= 0, SALA_ERR_INVALID_ARG, "n_init and n_local must be >= 0");
+  const int n_sel = topk + n_init + n_local;
+  REQUIRE(n_sel >= 1, SALA_ERR_INVALID_ARG, "topk + n_init + n_local must be >= 1");
+  REQUIRE(n_sel <= 1024, SALA_ERR_UNSUPPORTED, "topk + n_init + n_local must be <= 1024");
+  REQUIRE(Hq / Hkv <= 32, SALA_ERR_UNSUPPORTED, "decode supports at most 32 query heads per KV head");
+  REQUIRE(scale == scale, SALA_ERR_INVALID_ARG, "scale is NaN");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k_new, "k_new");
+  REQUIRE_PTR(v_new, "v_new");
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(v_cache, "v_cache");
+  REQUIRE_PTR(k_pooled, "k_pooled");
+  REQUIRE_PTR(idx, "idx");
+  REQUIRE_PTR(o, "o");
+  const int L = pos + 1;
+  const size_t sel = step_select_ws(dtype, B, Hq, Hkv, d, L, block, topk, n_init, n_local);
+  const size_t need = sel + sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel);
+  if ((s = check_ws(ws, ws_bytes, need))) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = sala::launch_kv_append(dtype, B * Hkv, capacity, d, block, pos, k_new, v_new, k_cache, v_cache,
+                                        k_pooled, st);
+  if (e != hipSuccess) return hip_status(e, "sala_sparse_decode_step append");
+  sala::SparseSelectArgs sa{dtype, B, Hq, Hkv, d, 1, L, block, topk, n_init, n_local, q, nullptr, k_pooled, idx,
+                            nullptr, ws, capacity};
+  e = sala::launch_sparse_select(sa, st);
+  if (e != hipSuccess) return hip_status(e, "sala_sparse_decode_step select");
+  sala::SparseDecodeArgs da{dtype, B, Hq, Hkv, L, d, block, n_sel, scale, q, k_cache, v_cache, idx, o,
+                            static_cast<char *>(ws) + sel, capacity};
+  return hip_status(sala::launch_sparse_decode(da, st), "sala_sparse_decode_step attend");
+}
+
+size_t sala_sparse_prefill_chunk_workspace(int dtype, int B, int Hq, int Hkv, int capacity, int d, int n, int block,
+                                           int topk, int n_init, int n_local) {
+  if (n == 1) return sala_sparse_decode_step_workspace(dtype, B, Hq, Hkv, capacity, d, block, topk, n_init, n_local);
+  if (B < 1 || Hkv < 1 || Hq < 1 || capacity < 1 || n < 1 || n > capacity || block != 64 || (d != 64 && d != 128))
+    return 0;
+  return sala::sparse_select_workspace(dtype, B, Hq, Hkv, d, n, capacity, block, topk, n_init, n_local, false);
+}
+
+int sala_sparse_prefill_chunk(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos0, int n, int block,
+                              int topk, int n_init, int n_local, float scale, const void *q, const void *k_new,
+                              const void *v_new, void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o,
+                              void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  REQUIRE(n >= 1, SALA_ERR_INVALID_ARG, "n must be >= 1");
+  if (n == 1)
+    return sala_sparse_decode_step(dtype, B, Hq, Hkv, capacity, d, pos0, block, topk, n_init, n_local, scale, q,
+                                   k_new, v_new, k_cache, v_cache, k_pooled, idx, o, ws, ws_bytes, stream);
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_sparse_common(B, Hq, Hkv, block, topk, "topk"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(capacity >= 1, SALA_ERR_INVALID_ARG, "capacity must be >= 1");
+  REQUIRE(pos0 >= 0 && (long long)pos0 + n <= capacity, SALA_ERR_INVALID_ARG,
+          "tokens pos0 .. pos0 + n - 1 (%d .. %lld) must lie in [0, capacity = %d)", pos0, (long long)pos0 + n - 1,
+          capacity);
+  REQUIRE(pos0 % block == 0, SALA_ERR_UNSUPPORTED, "a chunk of n > 1 tokens must start on a block boundary (pos0 = %d)",
+          pos0);
+  REQUIRE(n_init >= 0 && n_local >= 0, SALA_ERR_INVALID_ARG, "n_init and n_local must be >= 0");
+  const int n_sel = topk + n_init + n_local;
+  REQUIRE(n_sel >= 1, SALA_ERR_INVALID_ARG, "topk + n_init + n_local must be >= 1");
+  REQUIRE(n_sel <= 1024, SALA_ERR_UNSUPPORTED, "topk + n_init + n_local must be <= 1024");
+  REQUIRE(scale == scale, SALA_ERR_INVALID_ARG, "scale is NaN");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k_new, "k_new");
+  REQUIRE_PTR(v_new, "v_new");
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(v_cache, "v_cache");
+  REQUIRE_PTR(k_pooled, "k_pooled");
+  REQUIRE_PTR(idx, "idx");
+  REQUIRE_PTR(o, "o");
+  const int L = pos0 + n;
+  const size_t need = sala::sparse_select_workspace(dtype, B, Hq, Hkv, d, n, L, block, topk, n_init, n_local, false);
+  if ((s = check_ws(ws, ws_bytes, need))) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = sala::launch_kv_write(dtype, B * Hkv, capacity, d, pos0, n, k_new, v_new, k_cache, v_cache, st);
+  if (e != hipSuccess) return hip_status(e, "sala_sparse_prefill_chunk write");
+  sala::SparseSelectArgs sa{dtype, B, Hq, Hkv, d, n, L, block, topk, n_init, n_local, q, k_cache, k_pooled, idx,
+                            nullptr, ws, capacity};
+  e = sala::launch_sparse_select(sa, st);
+  if (e != hipSuccess) return hip_status(e, "sala_sparse_prefill_chunk select");
+  sala::SparsePrefillArgs pa{dtype, B, Hq, Hkv, n, d, block, n_sel, scale, q, k_cache, v_cache, idx, o, nullptr,
+                             L, capacity};
+  return hip_status(sala::launch_sparse_prefill(pa, st), "sala_sparse_prefill_chunk attend");
+}
+
 }  // extern "C"

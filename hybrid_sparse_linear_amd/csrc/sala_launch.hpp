@@ -61,7 +61,15 @@ struct SparseSelectArgs {
   int32_t *idx;
   float *scores;  // user buffer or nullptr
   void *ws;
+  int Lc;         // decode without k: k_pooled rows hold ceil(Lc / block) blocks (0: L)
 };
+// Decode step: token pos written into caches of Lc tokens per (b, KV head),
+// and the pooled key of its block recomputed.
+hipError_t launch_kv_append(int dtype, int BH, int Lc, int d, int block, int pos, const void *k_new,
+                            const void *v_new, void *k_cache, void *v_cache, float *k_pooled, hipStream_t st);
+// Continued prefill: rows pos0 .. pos0+n-1 of both caches written from [B*Hkv, n, d].
+hipError_t launch_kv_write(int dtype, int BH, int Lc, int d, int pos0, int n, const void *k_new, const void *v_new,
+                           void *k_cache, void *v_cache, hipStream_t st);
 size_t sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq, int L, int block, int topk,
                                int n_init, int n_local, bool want_scores);
 hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st);
@@ -73,6 +81,7 @@ struct SparsePrefillArgs {
   const int32_t *idx;
   void *o;
   void *ws;
+  int L, Lc;  // continued prefill: N queries are the last of L keys held in rows of Lc tokens (0: N, L)
 };
 size_t sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel);
 hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st);
@@ -84,6 +93,7 @@ struct SparseDecodeArgs {
   const int32_t *idx;
   void *o;
   void *ws;
+  int Lc;  // cache rows hold Lc tokens (0: L)
 };
 size_t sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel);
 hipError_t launch_sparse_decode(const SparseDecodeArgs &a, hipStream_t st);

@@ -35,8 +35,8 @@ __device__ __forceinline__ void load_row16(const T *p, float *f) {  // 16 bytes 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_partial(const T *__restrict__ q, const T *__restrict__ kc,
                                                       const T *__restrict__ vc, const int32_t *__restrict__ idx,
-                                                      float *__restrict__ part, int Hq, int Hkv, int L, int n_sel,
-                                                      int nsplit, int bps, float scale_log2) {
+                                                      float *__restrict__ part, int Hq, int Hkv, int L, int Lc,
+                                                      int n_sel, int nsplit, int bps, float scale_log2) {
   constexpr int KS = D + 4;                         // padded K row (floats)
   constexpr int EPL = sizeof(T) == 2 ? 8 : 4;       // elements per 16-byte load
   constexpr int CPR = D / EPL;                      // 16-byte loads per row
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(256) void decode_partial(const T *__restrict__ q, c
 #pragma unroll
     for (int c = 0; c < CPL; ++c) oacc[a][c] = 0.f;
   }
-  const T *kbase = kc + (size_t)bkv * L * D;
-  const T *vbase = vc + (size_t)bkv * L * D;
+  const T *kbase = kc + (size_t)bkv * Lc * D;  // cache rows hold Lc tokens
+  const T *vbase = vc + (size_t)bkv * Lc * D;
 
   for (int e = e0; e < e1; ++e) {
     const int j = row[e];
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64) void decode_attend_mfma(const uint16_t *__restr
                                                          const uint16_t *__restrict__ kc,
                                                          const uint16_t *__restrict__ vc,
                                                          const int32_t *__restrict__ idx, float *__restrict__ part,
-                                                         int Hq, int Hkv, int L, int n_sel, float scale_log2) {
+                                                         int Hq, int Hkv, int L, int Lc, int n_sel, float scale_log2) {
   constexpr int NDS = D / 32, ND = D / 16, NCH = D / 8, ROWB = 2 * D;
   __shared__ __attribute__((aligned(16))) char vs[BLK * ROWB];
   const int bkv = blockIdx.x / n_sel, e = blockIdx.x % n_sel;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64) void decode_attend_mfma(const uint16_t *__restr
     return;
   }
   const int cnt = min(BLK, L - j * BLK);
-  const size_t base = (size_t)bkv * L + (size_t)j * BLK;
+  const size_t base = (size_t)bkv * Lc + (size_t)j * BLK;  // cache rows hold Lc tokens
   // V rows -> LDS by direct loads: slot p = 64u + l holds row p / NCH, chunk
   // p % NCH after the fkv swizzle, so the lane fetches the logical chunk that
   // maps there (the XOR is an involution).  Rows past cnt repeat row cnt-1;
@@ -347,14 +347,15 @@ void run(const SparseDecodeArgs &a, hipStream_t st) {
   if (sizeof(T) == 2 && a.Hq / a.Hkv <= 16) {
     hipLaunchKernelGGL((decode_attend_mfma<D>), dim3(a.B * a.Hkv * a.n_sel), dim3(64), 0, st, (const uint16_t *)a.q,
                        (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L,
-                       a.n_sel, a.scale * 1.4426950408889634f);
+                       a.Lc ? a.Lc : a.L, a.n_sel, a.scale * 1.4426950408889634f);
     hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(512), 0, st, part, (T *)a.o, a.n_sel);
     return;
   }
   int nsplit, bps;
   split_plan(a.B * a.Hkv, a.n_sel, &nsplit, &bps);
   hipLaunchKernelGGL((decode_partial<T, D>), dim3(a.B * a.Hkv * nsplit), dim3(256), 0, st, (const T *)a.q,
-                     (const T *)a.k_cache, (const T *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L, a.n_sel, nsplit, bps,
+                     (const T *)a.k_cache, (const T *)a.v_cache, a.idx, part, a.Hq, a.Hkv, a.L, a.Lc ? a.Lc : a.L,
+                     a.n_sel, nsplit, bps,
                      a.scale * 1.4426950408889634f);
   hipLaunchKernelGGL((decode_combine<T, D>), dim3(a.B * a.Hq), dim3(512), 0, st, part, (T *)a.o, nsplit);
 }

@@ -62,8 +62,9 @@ struct SpCfg {
 template <int D, bool DENSE>
 __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                         const uint16_t *__restrict__ v, const int32_t *__restrict__ idx,
-                                                        uint16_t *__restrict__ o, int Hq, int Hkv, int N, int NQB,
-                                                        int n_sel, int HG, int ntasks, float scale_log2) {
+                                                        uint16_t *__restrict__ o, int Hq, int Hkv, int Nq, int L,
+                                                        int Lc, int qb0, int NQB, int n_sel, int HG, int ntasks,
+                                                        float scale_log2) {
   using Cf = SpCfg<D>;
   // one LDS array per buffer: with the loop unrolled by two every LDS read
   // and every direct load names its buffer, so the compiler can see that the
@@ -79,7 +80,9 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   const int task = (slot / HG) * 8 + (x & 7);
   const int hg = slot % HG;
   if (task >= ntasks) return;
-  const int i = DENSE ? NQB - 1 - task % NQB : task % NQB;
+  // query block: i_loc among the Nq query rows, i = qb0 + i_loc among the L keys
+  const int i_loc = DENSE ? NQB - 1 - task % NQB : task % NQB;
+  const int i = qb0 + i_loc;
   const int bkv = task / NQB;  // b * Hkv + kvh
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int G = Hq / Hkv;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
       diag_sh = 1;
     }
   } else if (tid == 0) {
-    const int32_t *row = idx + ((size_t)bkv * NQB + i) * n_sel;
+    const int32_t *row = idx + ((size_t)bkv * NQB + i_loc) * n_sel;
     int n = 0, has_diag = 0;
     for (int e = 0; e < n_sel; ++e) {
       const int j = row[e];
@@ -112,15 +115,15 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
     diag_sh = has_diag;
   }
 
-  // Q fragments (B operand of K Q^T): lane holds Q[t = 64i + 16qt + lr][32s + 8lg .. +7]
-  const uint16_t *qb = q + ((size_t)(b * Hq + hq) * N) * D;
+  // Q fragments (B operand of K Q^T): lane holds Q[t = 64 i_loc + 16qt + lr][32s + 8lg .. +7]
+  const uint16_t *qb = q + ((size_t)(b * Hq + hq) * Nq) * D;
   u32x4 qf[2][Cf::NDS];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const int t = BLK * i + 16 * (qt0 + a) + lr;
+    const int t = BLK * i_loc + 16 * (qt0 + a) + lr;
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s)
-      qf[a][s] = (t < N) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
+      qf[a][s] = (t < Nq) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
   }
 
   f32x4 Oacc[2][Cf::ND];
@@ -138,13 +141,13 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   __syncthreads();
   const int nvalid = nvalid_sh;
   const bool has_diag = diag_sh != 0;
-  const uint16_t *kbase = k + ((size_t)bkv * N) * D;
-  const uint16_t *vbase = v + ((size_t)bkv * N) * D;
+  const uint16_t *kbase = k + ((size_t)bkv * Lc) * D;  // key rows hold Lc tokens, L of them valid
+  const uint16_t *vbase = v + ((size_t)bkv * Lc) * D;
 
   // Direct global -> LDS loads (16 bytes per lane): the LDS slot of lane l in
   // wave w for step u is p = 512u + 64w + l, so each lane fetches the logical
   // chunk that the row swizzle maps to its slot (the XOR swizzles are
-  // involutions).  K and V rows past N re-read the last valid row: they are
+  // involutions).  K and V rows past L re-read the last valid row: they are
   // keys of the diagonal block beyond every query, so causality masks them.
   // V rows use the fkv swizzle of the transposed reads.
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   auto load_block = [&](int j, char *kdst, char *vdst) {
     const uint16_t *ksrc = kbase + (size_t)j * BLK * D;
     const uint16_t *vsrc = vbase + (size_t)j * BLK * D;
-    const int last = min(BLK, N - j * BLK) - 1;
+    const int last = min(BLK, L - j * BLK) - 1;
 #pragma unroll
     for (int u = 0; u < Cf::PER_T; ++u) {
       const int p = Cf::NT * u + tid;
@@ -273,13 +276,13 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   }
 
   if (!active) return;
-  uint16_t *ob = o + ((size_t)(b * Hq + hq) * N) * D;
+  uint16_t *ob = o + ((size_t)(b * Hq + hq) * Nq) * D;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const float lt = Lacc[a][0];
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-    const int t = BLK * i + 16 * (qt0 + a) + lr;
-    if (t < N) {
+    const int t = BLK * i_loc + 16 * (qt0 + a) + lr;
+    if (t < Nq) {
 #pragma unroll
       for (int dv = 0; dv < Cf::ND; ++dv)
         *reinterpret_cast<u32x2 *>(ob + (size_t)t * D + 16 * dv + 4 * lg) =
@@ -293,28 +296,29 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
 template <int D>
 __global__ __launch_bounds__(64) void sparse_attn_f32(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const int32_t *__restrict__ idx,
-                                                      float *__restrict__ o, int Hq, int Hkv, int N, int NQB,
-                                                      int n_sel, float scale) {
+                                                      float *__restrict__ o, int Hq, int Hkv, int Nq, int L, int Lc,
+                                                      int qb0, int NQB, int n_sel, float scale) {
   __shared__ float qs[BLK][D + 1];
   __shared__ float ks[BLK][D];
   __shared__ float vs[BLK][D];
   const int bid = blockIdx.x;
-  const int i = bid % NQB, bh = bid / NQB;  // bh = b * Hq + hq
+  const int i_loc = bid % NQB, bh = bid / NQB;  // bh = b * Hq + hq
+  const int i = qb0 + i_loc;                     // the query block among the L keys
   const int b = bh / Hq, hq = bh % Hq, G = Hq / Hkv, kvh = hq / G;
   const int tid = threadIdx.x;
-  const int t = BLK * i + tid;
-  const float *qb = q + (size_t)bh * N * D;
-  const float *kb = k + (size_t)(b * Hkv + kvh) * N * D;
-  const float *vb = v + (size_t)(b * Hkv + kvh) * N * D;
+  const int t = BLK * i_loc + tid;
+  const float *qb = q + (size_t)bh * Nq * D;
+  const float *kb = k + (size_t)(b * Hkv + kvh) * Lc * D;
+  const float *vb = v + (size_t)(b * Hkv + kvh) * Lc * D;
   for (int e = tid; e < BLK * D; e += 64) {
     const int r = e / D, c = e % D;
-    qs[r][c] = (BLK * i + r < N) ? qb[(size_t)(BLK * i + r) * D + c] : 0.f;
+    qs[r][c] = (BLK * i_loc + r < Nq) ? qb[(size_t)(BLK * i_loc + r) * D + c] : 0.f;
   }
   float acc[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) acc[c] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-  const int32_t *row = idx + ((size_t)(b * Hkv + kvh) * NQB + i) * n_sel;
+  const int32_t *row = idx + ((size_t)(b * Hkv + kvh) * NQB + i_loc) * n_sel;
   for (int e = 0; e < n_sel; ++e) {
     const int j = row[e];
     if (j < 0) break;
@@ -322,14 +326,14 @@ __global__ __launch_bounds__(64) void sparse_attn_f32(const float *__restrict__ 
     __syncthreads();
     for (int x = tid; x < BLK * D; x += 64) {
       const int r = x / D, c = x % D;
-      const bool ok = BLK * j + r < N;
+      const bool ok = BLK * j + r < L;
       ks[r][c] = ok ? kb[(size_t)(BLK * j + r) * D + c] : 0.f;
       vs[r][c] = ok ? vb[(size_t)(BLK * j + r) * D + c] : 0.f;
     }
     __syncthreads();
     const int kmax = (j == i) ? tid : BLK - 1;  // causal inside the diagonal block
     for (int kk = 0; kk <= kmax; ++kk) {
-      if (BLK * j + kk >= N) break;
+      if (BLK * j + kk >= L) break;
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < D; ++c) s = fmaf(qs[tid][c], ks[kk][c], s);
@@ -343,17 +347,28 @@ __global__ __launch_bounds__(64) void sparse_attn_f32(const float *__restrict__ 
       m = mnew;
     }
   }
-  if (t < N) {
+  if (t < Nq) {
     const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-    float *orow = o + ((size_t)bh * N + t) * D;
+    float *orow = o + ((size_t)bh * Nq + t) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) orow[c] = acc[c] * inv;
   }
 }
 
+// a.N query rows; keys: a.L valid (0: N) in rows of a.Lc tokens (0: L); the
+// queries are the last N of the L tokens (L - N a multiple of BLK).
+struct KeyGeom {
+  int L, Lc, qb0;
+};
+KeyGeom key_geom(const SparsePrefillArgs &a) {
+  const int L = a.L ? a.L : a.N;
+  return KeyGeom{L, a.Lc ? a.Lc : L, (L - a.N) / BLK};
+}
+
 template <bool DENSE>
 void launch_bf16(const SparsePrefillArgs &a, hipStream_t st) {
   const int NQB = (a.N + BLK - 1) / BLK;
+  const KeyGeom kg = key_geom(a);
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 3) / 4;
   const int ntasks = a.B * a.Hkv * NQB;
@@ -361,12 +376,12 @@ void launch_bf16(const SparsePrefillArgs &a, hipStream_t st) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   if (a.d == 128)
     hipLaunchKernelGGL((sparse_attn_bf16<128, DENSE>), dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
-                       a.n_sel, HG, ntasks, scale_log2);
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, kg.L,
+                       kg.Lc, kg.qb0, NQB, a.n_sel, HG, ntasks, scale_log2);
   else
     hipLaunchKernelGGL((sparse_attn_bf16<64, DENSE>), dim3(grid), dim3(512), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, NQB,
-                       a.n_sel, HG, ntasks, scale_log2);
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.idx, (uint16_t *)a.o, a.Hq, a.Hkv, a.N, kg.L,
+                       kg.Lc, kg.qb0, NQB, a.n_sel, HG, ntasks, scale_log2);
 }
 
 }  // namespace
@@ -378,15 +393,16 @@ size_t sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, int d,
 
 hipError_t launch_sparse_prefill(const SparsePrefillArgs &a, hipStream_t st) {
   const int NQB = (a.N + BLK - 1) / BLK;
+  const KeyGeom kg = key_geom(a);
   if (a.dtype == 0) {
     if (a.d == 64)
       hipLaunchKernelGGL(sparse_attn_f32<64>, dim3(a.B * a.Hq * NQB), dim3(64), 0, st, (const float *)a.q,
-                         (const float *)a.k, (const float *)a.v, a.idx, (float *)a.o, a.Hq, a.Hkv, a.N, NQB,
-                         a.n_sel, a.scale);
+                         (const float *)a.k, (const float *)a.v, a.idx, (float *)a.o, a.Hq, a.Hkv, a.N, kg.L, kg.Lc,
+                         kg.qb0, NQB, a.n_sel, a.scale);
     else
       hipLaunchKernelGGL(sparse_attn_f32<128>, dim3(a.B * a.Hq * NQB), dim3(64), 0, st, (const float *)a.q,
-                         (const float *)a.k, (const float *)a.v, a.idx, (float *)a.o, a.Hq, a.Hkv, a.N, NQB,
-                         a.n_sel, a.scale);
+                         (const float *)a.k, (const float *)a.v, a.idx, (float *)a.o, a.Hq, a.Hkv, a.N, kg.L, kg.Lc,
+                         kg.qb0, NQB, a.n_sel, a.scale);
     return hipGetLastError();
   }
   launch_bf16<false>(a, st);

@@ -73,19 +73,21 @@ __device__ void mean_rows(RowPtr src, int nrows, int d, float *dst, float *red /
   }
 }
 
-// grid.x = B*Hkv*NBk (key blocks, when k != null) + B*Hkv*NQB (query blocks, prefill)
+// grid.x = B*Hkv*NBp (key blocks kb0 .. kb0+NBp-1, when k != null) + B*Hkv*NQB
+// (query blocks, prefill).  k rows hold Lc tokens (L valid); kbar rows hold
+// NBs pooled blocks.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_rows(const T *__restrict__ q, const T *__restrict__ k,
                                                  float *__restrict__ kbar, float *__restrict__ qbar, int Hq,
-                                                 int Hkv, int Nq, int L, int d, int block, int n_kblocks_total,
-                                                 int NBk, int NQB) {
+                                                 int Hkv, int Nq, int L, int Lc, int d, int block, int n_kblocks_total,
+                                                 int NBp, int kb0, int NBs, int NQB) {
   __shared__ float red[256 * 8];
   const int bid = blockIdx.x;
   if (bid < n_kblocks_total) {
-    const int bh = bid / NBk, j = bid % NBk;
+    const int bh = bid / NBp, j = kb0 + bid % NBp;
     const int cnt = min(block, L - j * block);
-    const T *base = k + ((size_t)bh * L + (size_t)j * block) * d;
-    mean_rows<T>([&](int r) { return base + (size_t)r * d; }, cnt, d, kbar + ((size_t)bh * NBk + j) * d, red);
+    const T *base = k + ((size_t)bh * Lc + (size_t)j * block) * d;
+    mean_rows<T>([&](int r) { return base + (size_t)r * d; }, cnt, d, kbar + ((size_t)bh * NBs + j) * d, red);
   } else {
     const int id = bid - n_kblocks_total;
     const int bh = id / NQB, i = id % NQB;  // bh = b*Hkv + h
@@ -97,19 +99,53 @@ __global__ __launch_bounds__(256) void pool_rows(const T *__restrict__ q, const 
   }
 }
 
-// scores[bh][i][j] = (qbar_i . kbar_j) * inv_sqrt_d for the 64x64 tiles with J <= I.
+// Decode step: token pos of every (b, KV head) is written into the caches
+// (rows of Lc tokens), and the pooled key of its block becomes the mean of the
+// block's tokens 0 .. pos (the new one taken from k_new), summed in the same
+// order as pool_rows, so it equals a full re-pool of the cache bit for bit.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append(const T *__restrict__ k_new, const T *__restrict__ v_new,
+                                                 T *__restrict__ kc, T *__restrict__ vc, float *__restrict__ kbar,
+                                                 int Lc, int NBs, int d, int block, int pos) {
+  __shared__ float red[256 * 8];
+  constexpr int E = Elem<T>::PER16;
+  const int bh = blockIdx.x, tid = threadIdx.x, cpr = d / E;
+  const T *kn = k_new + (size_t)bh * d;
+  const T *vn = v_new + (size_t)bh * d;
+  T *krow = kc + ((size_t)bh * Lc + pos) * d;
+  T *vrow = vc + ((size_t)bh * Lc + pos) * d;
+  if (tid < cpr) gstore16(krow + tid * E, gload16(kn + tid * E));
+  else if (tid < 2 * cpr) gstore16(vrow + (tid - cpr) * E, gload16(vn + (tid - cpr) * E));
+  const int j = pos / block, first = j * block, cnt = pos - first + 1;
+  const T *base = kc + ((size_t)bh * Lc + first) * d;
+  mean_rows<T>([&](int r) { return r == cnt - 1 ? kn : base + (size_t)r * d; }, cnt, d,
+               kbar + ((size_t)bh * NBs + j) * d, red);
+}
+
+// scores[bh][i][j] = (qbar_i . kbar_j) * inv_sqrt_d for the 64x64 tiles of
+// query blocks i (local; global qb0 + i) against key blocks j that are not
+// entirely after them.  nTk == 0: qb0 == 0 and a triangular grid of tiles
+// J <= I; otherwise a rectangular grid of nTk key tiles per query tile whose
+// tiles past the diagonal exit at once.  kbar rows hold NBs pooled blocks.
 __global__ __launch_bounds__(256) void score_tiles(const float *__restrict__ qbar, const float *__restrict__ kbar,
-                                                   float *__restrict__ scores, int NQB, int NB, int d,
-                                                   float inv_sqrt_d) {
+                                                   float *__restrict__ scores, int NQB, int NB, int NBs, int qb0,
+                                                   int nTk, int d, float inv_sqrt_d) {
   __shared__ float qs[64][129];
   __shared__ float ks[64][129];
   const int T = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  int I = (int)((sqrtf(8.f * (float)T + 1.f) - 1.f) * 0.5f);
-  while ((I + 1) * (I + 2) / 2 <= T) ++I;
-  while (I * (I + 1) / 2 > T) --I;
-  const int J = T - I * (I + 1) / 2;
+  int I, J;
+  if (nTk == 0) {
+    I = (int)((sqrtf(8.f * (float)T + 1.f) - 1.f) * 0.5f);
+    while ((I + 1) * (I + 2) / 2 <= T) ++I;
+    while (I * (I + 1) / 2 > T) --I;
+    J = T - I * (I + 1) / 2;
+  } else {
+    I = T / nTk;
+    J = T % nTk;
+    if (64 * J > qb0 + 64 * I + 63) return;  // every key block after every query block of the tile
+  }
   const float *qb = qbar + ((size_t)bh * NQB + 64 * I) * d;
-  const float *kb = kbar + ((size_t)bh * NB + 64 * J) * d;
+  const float *kb = kbar + ((size_t)bh * NBs + 64 * J) * d;
   for (int e = tid; e < 64 * d; e += 256) {
     const int r = e / d, c = e % d;
     qs[r][c] = (64 * I + r < NQB) ? qb[(size_t)r * d + c] : 0.f;
@@ -146,8 +182,8 @@ __global__ __launch_bounds__(256) void score_tiles(const float *__restrict__ qba
 // blocks per workgroup.  8 lanes per key block, 128-byte coalesced reads.
 template <typename T>
 __global__ __launch_bounds__(256) void score_decode(const T *__restrict__ q, const float *__restrict__ kbar,
-                                                    float *__restrict__ scores, int Hq, int Hkv, int NB, int d,
-                                                    float inv_sqrt_d) {
+                                                    float *__restrict__ scores, int Hq, int Hkv, int NB, int NBs,
+                                                    int d, float inv_sqrt_d) {
   __shared__ float qm[128];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv, tid = threadIdx.x;
   if (tid < d) {
@@ -166,7 +202,7 @@ __global__ __launch_bounds__(256) void score_decode(const T *__restrict__ q, con
   for (int vv = 0; vv < nv; ++vv)
 #pragma unroll
     for (int e = 0; e < 4; ++e) qr[4 * vv + e] = qm[32 * vv + 4 * l8 + e];
-  const float *kb = kbar + (size_t)bh * NB * d;
+  const float *kb = kbar + (size_t)bh * NBs * d;  // NBs: pooled blocks per row of kbar (capacity)
   for (int u = 0; u < 8; ++u) {
     const int j = blockIdx.x * 256 + grp + 32 * u;
     float acc = 0.f;
@@ -214,7 +250,7 @@ __device__ int block_excl_scan(int v, int *tmp, int &total) {
 template <int NT, int MAXC>
 __global__ __launch_bounds__(NT) void select_rows(const float *__restrict__ scores, int32_t *__restrict__ idx,
                                                   int rows_per_bh, int NB, int L, int block, int topk,
-                                                  int n_init, int n_local, int fixed_i) {
+                                                  int n_init, int n_local, int fixed_i, int qb0) {
   __shared__ uint32_t keys[MAXC];
   __shared__ int hist[256];
   __shared__ int tmp[NT / 64 + 1];
@@ -223,7 +259,7 @@ __global__ __launch_bounds__(NT) void select_rows(const float *__restrict__ scor
   const int tid = threadIdx.x;
   const int row = blockIdx.x;  // bh * rows_per_bh + r
   const int bh = row / rows_per_bh, r = row % rows_per_bh;
-  const int i = (fixed_i >= 0) ? fixed_i : r;
+  const int i = (fixed_i >= 0) ? fixed_i : qb0 + r;  // global query block
   const int width = topk + n_init + n_local;
   const float *srow = scores + ((size_t)bh * rows_per_bh + r) * NB;
   int32_t *out = idx + (size_t)row * width;
@@ -378,8 +414,8 @@ __device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, const uint64_t *b
 template <typename T, int d>
 __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ q, const float *__restrict__ kbar,
                                                           float *__restrict__ scores, uint64_t *__restrict__ tops,
-                                                          int Hq, int Hkv, int NB, float inv_sqrt_d, int lo,
-                                                          int hi) {
+                                                          int Hq, int Hkv, int NB, int NBs, float inv_sqrt_d,
+                                                          int lo, int hi) {
   __shared__ float qm[128];
   __shared__ float qpart[256];
   __shared__ float sc[256];
@@ -388,7 +424,7 @@ __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ 
   const int lane = tid & 63, w = tid >> 6;
   const int grp = tid >> 3, l8 = tid & 7;
   constexpr int nv = d / 32;  // float4 pieces per lane per pooled key
-  const float *kb = kbar + (size_t)bh * NB * d;
+  const float *kb = kbar + (size_t)bh * NBs * d;  // NBs: pooled blocks per row of kbar (capacity)
   // block of local slot (u, grp): the u-th loads of all workgroups of a row
   // cover one contiguous run of 32 * gridDim.x blocks, so the HBM channels see
   // an even spread at every moment.  Any partition keeps the two levels exact.
@@ -545,10 +581,57 @@ size_t sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, int Nq,
   return bytes;
 }
 
+// Rows pos0 .. pos0+n-1 of both caches (rows of Lc tokens) from k_new, v_new [BH, n, d].
+template <typename T>
+__global__ __launch_bounds__(256) void kv_write_rows(const T *__restrict__ k_new, const T *__restrict__ v_new,
+                                                     T *__restrict__ kc, T *__restrict__ vc, int Lc, int n, int d,
+                                                     int pos0, long long pieces) {
+  constexpr int E = Elem<T>::PER16;
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= pieces) return;
+  const int cpr = d / E;
+  const long long row = x / cpr;  // bh * n + r
+  const int c = (int)(x % cpr), r = (int)(row % n);
+  const long long bh = row / n;
+  const size_t dst = ((size_t)bh * Lc + pos0 + r) * d + (size_t)c * E;
+  const size_t src = (size_t)row * d + (size_t)c * E;
+  gstore16(kc + dst, gload16(k_new + src));
+  gstore16(vc + dst, gload16(v_new + src));
+}
+
+hipError_t launch_kv_write(int dtype, int BH, int Lc, int d, int pos0, int n, const void *k_new, const void *v_new,
+                           void *k_cache, void *v_cache, hipStream_t st) {
+  const long long pieces = (long long)BH * n * (d / (dtype == 1 ? 8 : 4));
+  const dim3 grid((unsigned)((pieces + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(kv_write_rows<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, (uint16_t *)k_cache, (uint16_t *)v_cache, Lc, n, d, pos0, pieces);
+  else
+    hipLaunchKernelGGL(kv_write_rows<float>, grid, dim3(256), 0, st, (const float *)k_new, (const float *)v_new,
+                       (float *)k_cache, (float *)v_cache, Lc, n, d, pos0, pieces);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(int dtype, int BH, int Lc, int d, int block, int pos, const void *k_new,
+                            const void *v_new, void *k_cache, void *v_cache, float *k_pooled, hipStream_t st) {
+  const int NBs = (Lc + block - 1) / block;
+  if (dtype == 1)
+    hipLaunchKernelGGL(kv_append<uint16_t>, dim3(BH), dim3(256), 0, st, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, (uint16_t *)k_cache, (uint16_t *)v_cache, k_pooled, Lc, NBs, d, block,
+                       pos);
+  else
+    hipLaunchKernelGGL(kv_append<float>, dim3(BH), dim3(256), 0, st, (const float *)k_new, (const float *)v_new,
+                       (float *)k_cache, (float *)v_cache, k_pooled, Lc, NBs, d, block, pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
   const int NB = (a.L + a.block - 1) / a.block;
+  const int Lc = a.Lc ? a.Lc : a.L;                // k and k_pooled rows are laid out for Lc tokens
+  const int NBs = (Lc + a.block - 1) / a.block;
   const bool decode = (a.Nq == 1);
   const int NQB = decode ? 1 : (a.Nq + a.block - 1) / a.block;
+  const int qb0 = decode ? 0 : (a.L - a.Nq) / a.block;  // first query block of a continued prefill
   const int BH = a.B * a.Hkv;
   char *ws = static_cast<char *>(a.ws);
   float *qbar = nullptr;
@@ -556,23 +639,33 @@ hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
   float *scores = a.scores ? a.scores : reinterpret_cast<float *>(ws);
   const float inv_sqrt_d = 1.0f / sqrtf((float)a.d);
 
-  const int nk = a.k ? BH * NB : 0;
+  // key blocks to pool: all of them, or (continued prefill) those the query chunk fills
+  const int kb0 = decode ? 0 : qb0;
+  const int NBp = NB - kb0;
+  const int nk = a.k ? BH * NBp : 0;
   const int nq = decode ? 0 : BH * NQB;
   if (nk + nq > 0) {
     if (a.dtype == 1)
       hipLaunchKernelGGL(pool_rows<uint16_t>, dim3(nk + nq), dim3(256), 0, st, (const uint16_t *)a.q,
-                         (const uint16_t *)a.k, a.k_pooled, qbar, a.Hq, a.Hkv, a.Nq, a.L, a.d, a.block, nk, NB,
-                         NQB);
+                         (const uint16_t *)a.k, a.k_pooled, qbar, a.Hq, a.Hkv, a.Nq, a.L, Lc, a.d, a.block, nk, NBp,
+                         kb0, NBs, NQB);
     else
       hipLaunchKernelGGL(pool_rows<float>, dim3(nk + nq), dim3(256), 0, st, (const float *)a.q,
-                         (const float *)a.k, a.k_pooled, qbar, a.Hq, a.Hkv, a.Nq, a.L, a.d, a.block, nk, NB, NQB);
+                         (const float *)a.k, a.k_pooled, qbar, a.Hq, a.Hkv, a.Nq, a.L, Lc, a.d, a.block, nk, NBp,
+                         kb0, NBs, NQB);
   }
   if (!decode) {
-    const int nT = (NQB + 63) / 64;
-    hipLaunchKernelGGL(score_tiles, dim3(nT * (nT + 1) / 2, BH), dim3(256), 0, st, qbar, a.k_pooled, scores, NQB,
-                       NB, a.d, inv_sqrt_d);
+    const int nTq = (NQB + 63) / 64;
+    if (qb0 == 0) {
+      hipLaunchKernelGGL(score_tiles, dim3(nTq * (nTq + 1) / 2, BH), dim3(256), 0, st, qbar, a.k_pooled, scores,
+                         NQB, NB, NBs, 0, 0, a.d, inv_sqrt_d);
+    } else {
+      const int nTk = (NB + 63) / 64;
+      hipLaunchKernelGGL(score_tiles, dim3(nTq * nTk, BH), dim3(256), 0, st, qbar, a.k_pooled, scores, NQB, NB,
+                         NBs, qb0, nTk, a.d, inv_sqrt_d);
+    }
     hipLaunchKernelGGL((select_rows<256, 8192>), dim3(BH * NQB), dim3(256), 0, st, scores, a.idx, NQB, NB, a.L,
-                       a.block, a.topk, a.n_init, a.n_local, -1);
+                       a.block, a.topk, a.n_init, a.n_local, -1, qb0);
   } else if (a.topk <= 64 && (NB + 255) / 256 * 64 <= 4096) {
     // two exact levels: local top-64 per 256 blocks, then threshold + rank per row
     const int nchunk = (NB + 255) / 256;
@@ -582,7 +675,7 @@ hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
     const int ncand = max(0, hi - lo + 1);
 #define SALA_SCORE_TOP64(T, DD)                                                                                  \
   hipLaunchKernelGGL((score_decode_top64<T, DD>), dim3(nchunk, BH), dim3(256), 0, st, (const T *)a.q, a.k_pooled,   \
-                     a.scores, tops, a.Hq, a.Hkv, NB, inv_sqrt_d, lo, hi)
+                     a.scores, tops, a.Hq, a.Hkv, NB, NBs, inv_sqrt_d, lo, hi)
     if (a.dtype == 1 && a.d == 128) SALA_SCORE_TOP64(uint16_t, 128);
     else if (a.dtype == 1) SALA_SCORE_TOP64(uint16_t, 64);
     else if (a.d == 128) SALA_SCORE_TOP64(float, 128);
@@ -593,12 +686,12 @@ hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
   } else {
     if (a.dtype == 1)
       hipLaunchKernelGGL(score_decode<uint16_t>, dim3((NB + 255) / 256, BH), dim3(256), 0, st,
-                         (const uint16_t *)a.q, a.k_pooled, scores, a.Hq, a.Hkv, NB, a.d, inv_sqrt_d);
+                         (const uint16_t *)a.q, a.k_pooled, scores, a.Hq, a.Hkv, NB, NBs, a.d, inv_sqrt_d);
     else
       hipLaunchKernelGGL(score_decode<float>, dim3((NB + 255) / 256, BH), dim3(256), 0, st, (const float *)a.q,
-                         a.k_pooled, scores, a.Hq, a.Hkv, NB, a.d, inv_sqrt_d);
+                         a.k_pooled, scores, a.Hq, a.Hkv, NB, NBs, a.d, inv_sqrt_d);
     hipLaunchKernelGGL((select_rows<1024, 16384>), dim3(BH), dim3(1024), 0, st, scores, a.idx, 1, NB, a.L,
-                       a.block, a.topk, a.n_init, a.n_local, (a.L - 1) / a.block);
+                       a.block, a.topk, a.n_init, a.n_local, (a.L - 1) / a.block, 0);
   }
   return hipGetLastError();
 }

@@ -164,6 +164,55 @@ int sala_output_gate(int dtype, size_t n, const void *o, const void *gate, void 
                      void *stream);
 
 /* ------------------------------------------------------------------------
+ * The sparse layer in a generation loop over a KV cache kept at a fixed
+ * capacity: sparse layers keep the whole KV cache ("dense storage") and
+ * reach all of it with sparse compute (MiniCPM-SALA, gist.science (ja)
+ * 技術概要 section 1 and 2.1); the model decodes contexts of up to 1M tokens
+ * on one GPU (same page, section 4.3).
+ *
+ * Layout shared by both calls:
+ *   k_cache, v_cache  [B, Hkv, capacity, d] of dtype; row t holds token t.
+ *   k_pooled          [B, Hkv, ceil(capacity / block), d] fp32; entry j holds
+ *                     the mean of block j's tokens written so far.
+ * Before a call that writes tokens from position p on, rows 0 .. p-1 hold the
+ * earlier tokens and k_pooled holds their blocks (as earlier calls left them).
+ * Selection and attention follow sala_sparse_select / sala_sparse_prefill /
+ * sala_sparse_decode for the keys 0 .. (last written token).
+ *
+ * sala_sparse_prefill_chunk -- n tokens at positions pos0 .. pos0 + n - 1:
+ *   q [B, Hq, n, d], k_new, v_new [B, Hkv, n, d] (the chunk's keys and
+ *   values, written into the caches); the pooled keys of the blocks the chunk
+ *   fills are recomputed; every query block of the chunk selects among all
+ *   cached blocks; o [B, Hq, n, d]; idx [B, Hkv, ceil(n / block), n_sel].
+ *   n > 1 needs pos0 % block == 0 (SALA_ERR_UNSUPPORTED otherwise); n == 1 is
+ *   one decode step.  pos0 + n <= capacity.  A first chunk (pos0 = 0) is an
+ *   ordinary prefill that also fills the caches.
+ * sala_sparse_decode_step -- one token at position pos (0 <= pos < capacity):
+ *   q [B, Hq, d], k_new, v_new [B, Hkv, d]; writes the token, recomputes the
+ *   pooled key of block pos / block, selects for the query at pos (L = pos+1)
+ *   and attends; o [B, Hq, d]; idx [B, Hkv, n_sel].
+ * Workspaces: at least the *_workspace value for the same arguments (sized
+ * for the whole capacity, so one buffer serves a whole generation loop).
+ * Results equal sala_sparse_select + sala_sparse_prefill (or
+ * sala_sparse_decode) run on the first pos0 + n (pos + 1) tokens bit for bit.
+ * ------------------------------------------------------------------------ */
+size_t sala_sparse_prefill_chunk_workspace(int dtype, int B, int Hq, int Hkv, int capacity, int d, int n,
+                                           int block, int topk, int n_init, int n_local);
+int sala_sparse_prefill_chunk(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos0, int n,
+                              int block, int topk, int n_init, int n_local, float scale,
+                              const void *q, const void *k_new, const void *v_new,
+                              void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o,
+                              void *ws, size_t ws_bytes, void *stream);
+
+size_t sala_sparse_decode_step_workspace(int dtype, int B, int Hq, int Hkv, int capacity, int d, int block,
+                                         int topk, int n_init, int n_local);
+int sala_sparse_decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block,
+                            int topk, int n_init, int n_local, float scale,
+                            const void *q, const void *k_new, const void *v_new,
+                            void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * sala_sparse_select -- block selection for the sparse layer.
  *
  * The sparse layers use InfLLM-V2, which adds no parameters and reaches the

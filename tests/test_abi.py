@@ -200,3 +200,38 @@ def test_standalone_neighbour_validation():
     assert og(g=NUL) == INVALID
     assert og(out=MIS) == INVALID
     assert og(dtype=2) == INVALID
+
+
+def test_generation_loop_validation():
+    L = _lib.lib()
+
+    def chunk(**kw):
+        a = dict(dtype=BF16, B=1, Hq=4, Hkv=2, cap=1000, d=128, pos0=64, n=100, block=64, topk=4, ni=1, nl=2,
+                 scale=0.1, ws=NUL, wsb=0)
+        a.update(kw)
+        return L.sala_sparse_prefill_chunk(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["cap"], a["d"], a["pos0"], a["n"],
+                                           a["block"], a["topk"], a["ni"], a["nl"], a["scale"], A, A, A, A, A, A, A, A,
+                                           a["ws"], a["wsb"], NUL)
+
+    def step(**kw):
+        a = dict(dtype=BF16, B=1, Hq=4, Hkv=2, cap=1000, d=128, pos=500, block=64, topk=4, ni=1, nl=2, scale=0.1,
+                 ws=NUL, wsb=0, k_cache=A)
+        a.update(kw)
+        return L.sala_sparse_decode_step(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["cap"], a["d"], a["pos"], a["block"],
+                                         a["topk"], a["ni"], a["nl"], a["scale"], A, A, A, a["k_cache"], A, A, A, A,
+                                         a["ws"], a["wsb"], NUL)
+
+    assert chunk(n=0) == INVALID
+    assert chunk(pos0=70) == UNSUPPORTED and b"block boundary" in L.sala_last_error()
+    assert chunk(pos0=960, n=100) == INVALID  # past the capacity
+    assert chunk(Hq=3) == INVALID
+    assert chunk(scale=float("nan")) == INVALID
+    assert chunk() == WORKSPACE
+    assert L.sala_sparse_prefill_chunk_workspace(BF16, 1, 4, 2, 1000, 128, 100, 64, 4, 1, 2) > 0
+    assert chunk(ws=A, wsb=1) == WORKSPACE
+    assert step(pos=1000) == INVALID and b"capacity" in L.sala_last_error()
+    assert step(pos=-1) == INVALID
+    assert step(k_cache=MIS) == INVALID
+    assert step(d=48) == UNSUPPORTED
+    assert step() == WORKSPACE
+    assert L.sala_sparse_decode_step_workspace(BF16, 1, 4, 2, 1000, 128, 64, 4, 1, 2) > 0
