@@ -116,6 +116,11 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// 16 bytes per lane from buffer offset off straight into LDS: lane l's bytes
+// land at lds + 16 l (lds wave-uniform).
+__device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)lds, 16, off, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------- wave reductions (wave64)
 __device__ __forceinline__ float wave_max(float v) {
@@ -140,6 +145,24 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
   if constexpr (G == 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
   return x;
+}
+
+// Max / sum over the four 16-lane rows of a wave, at each position within a
+// row, every lane receiving the result: v_permlane16_swap pairs rows 0-1 and
+// 2-3, v_permlane32_swap the two halves (VALU lane exchanges, no LDS round
+// trip).  With both operands the same register each swap returns the pair's
+// two rows, so combining its two results reduces over the pair.
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each).

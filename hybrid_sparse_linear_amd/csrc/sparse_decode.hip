@@ -238,8 +238,7 @@ __global__ __launch_bounds__(64) void decode_attend_mfma(const uint16_t *__restr
         S[pp][t][i] = x;
         mx = fmaxf(mx, x);
       }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = row4_max(mx);
   float ls = 0.f;
   u32x4 Bp[2];
 #pragma unroll
@@ -255,8 +254,7 @@ __global__ __launch_bounds__(64) void decode_attend_mfma(const uint16_t *__restr
     Bp[pp] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
                    pack_bf16x2(p[1][2], p[1][3])};
   }
-  ls += __shfl_xor(ls, 16, 64);
-  ls += __shfl_xor(ls, 32, 64);
+  ls = row4_sum(ls);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the V rows are in LDS
   const uint32_t lane_off = tr_lane_off(l, ROWB), lane_xor = tr_lane_xor(l);
   // every lane takes part in the MFMAs; only heads < G store

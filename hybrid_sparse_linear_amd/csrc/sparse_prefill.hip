@@ -144,30 +144,33 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   const uint16_t *kbase = k + ((size_t)bkv * Lc) * D;  // key rows hold Lc tokens, L of them valid
   const uint16_t *vbase = v + ((size_t)bkv * Lc) * D;
 
-  // Direct global -> LDS loads (16 bytes per lane): the LDS slot of lane l in
+  // Direct buffer -> LDS loads (16 bytes per lane): the LDS slot of lane l in
   // wave w for step u is p = 512u + 64w + l, so each lane fetches the logical
   // chunk that the row swizzle maps to its slot (the XOR swizzles are
-  // involutions).  K and V rows past L re-read the last valid row: they are
-  // keys of the diagonal block beyond every query, so causality masks them.
-  // V rows use the fkv swizzle of the transposed reads.
+  // involutions).  V rows use the fkv swizzle of the transposed reads.  The
+  // lane offsets within a block are fixed; each block gets a buffer resource
+  // (SGPRs) over its valid rows, so rows past L read as zero: they are keys of
+  // the diagonal block beyond every query, which causality masks.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto blk = [&](int e) { return DENSE ? e : sel[e]; };  // e-th block to process
   const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);  // V^T fragment reads
+  uint32_t koff[Cf::PER_T], voff[Cf::PER_T];
+#pragma unroll
+  for (int u = 0; u < Cf::PER_T; ++u) {
+    const int p = Cf::NT * u + tid;
+    const int krow = p / Cf::KCH;
+    koff[u] = (uint32_t)(krow * D + 8 * (int)swz_k<Cf::KCH>(krow, p % Cf::KCH)) * 2u;
+    voff[u] = (uint32_t)(krow * D + 8 * ((p % Cf::KCH) ^ (int)(fkv(krow) & (Cf::KCH - 1)))) * 2u;
+  }
   auto load_block = [&](int j, char *kdst, char *vdst) {
-    const uint16_t *ksrc = kbase + (size_t)j * BLK * D;
-    const uint16_t *vsrc = vbase + (size_t)j * BLK * D;
-    const int last = min(BLK, L - j * BLK) - 1;
+    j = __builtin_amdgcn_readfirstlane(j);  // uniform (one block list per workgroup): the resources stay scalar
+    const uint32_t valid = (uint32_t)min(BLK, L - j * BLK) * D * 2u;
+    const auto kr = buf_rsrc(kbase + (size_t)j * BLK * D, valid);
+    const auto vr = buf_rsrc(vbase + (size_t)j * BLK * D, valid);
 #pragma unroll
     for (int u = 0; u < Cf::PER_T; ++u) {
-      const int p = Cf::NT * u + tid;
-      const int krow = p / Cf::KCH, kch = swz_k<Cf::KCH>(krow, p % Cf::KCH);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(ksrc + (size_t)min(krow, last) * D + 8 * kch),
-          (void __attribute__((address_space(3))) *)(kdst + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
-      const int vch = (p % Cf::KCH) ^ (int)(fkv(krow) & (Cf::KCH - 1));
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(vsrc + (size_t)min(krow, last) * D + 8 * vch),
-          (void __attribute__((address_space(3))) *)(vdst + (Cf::NT * u + 64 * wu) * 16), 16, 0, 0);
+      bload16_lds(kr, kdst + (Cf::NT * u + 64 * wu) * 16, koff[u]);
+      bload16_lds(vr, vdst + (Cf::NT * u + 64 * wu) * 16, voff[u]);
     }
   };
   // this wave's direct loads done (vmcnt 0); the barrier that follows publishes them
@@ -207,8 +210,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
           }
           mx = fmaxf(mx, S[kt][a][e]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = row4_max(mx);
       mb[a] = mx * scale_log2;
     }
     if (__any((mb[0] > mref[0] + 8.0f) || (mb[1] > mref[1] + 8.0f))) {

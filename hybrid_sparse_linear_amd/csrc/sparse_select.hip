@@ -362,12 +362,15 @@ __global__ __launch_bounds__(NT) void select_rows(const float *__restrict__ scor
 __device__ __forceinline__ uint64_t pack_key(float score, int j) {
   return ((uint64_t)float_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
-// Value of lane l ^ m.  m is a constant after unrolling: m <= 8 are DPP moves
-// on the VALU (xor 4 = row half-mirror then quad permutation [3,2,1,0]; xor 8 =
-// row rotate by 8), m = 16 a ds_swizzle bit-mode exchange, m = 32 a bpermute.
-// The lane maps were checked on gfx950 with a probe.
+// Value of lane l ^ m.  m is a constant after unrolling, and every case is a
+// VALU lane exchange: m <= 8 are DPP moves (xor 4 = row half-mirror then quad
+// permutation [3,2,1,0]; xor 8 = row rotate by 8); m = 16 and 32 take the
+// partner's row from v_permlane16_swap / v_permlane32_swap, which (with both
+// operands v) return the lower and the upper row of each row pair.  The lane
+// maps were checked on gfx950 with probes.
 __device__ __forceinline__ uint32_t shfl_xor32(uint32_t v, int m) {
   const int x = (int)v;
+  const int lane = __lane_id();
   switch (m) {
     case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
     case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
@@ -376,8 +379,14 @@ __device__ __forceinline__ uint32_t shfl_xor32(uint32_t v, int m) {
       return (uint32_t)__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, false);
     }
     case 8: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
-    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);
-    default: return (uint32_t)__shfl_xor(x, m, 64);
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16) ? p[0] : p[1];
+    }
+    default: {  // 32
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32) ? p[0] : p[1];
+    }
   }
 }
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
