@@ -71,10 +71,8 @@ struct LinCfg {
 
 // K and V rows live in LDS in their natural layout with 16-byte chunks XOR-
 // swizzled by row (fkv): conflict-free for the plain 16-byte reads of 16 rows
-// of one key pair and for the transposed reads (lds_read_tr).
-// S^T rows are read 16 consecutive rows at one chunk: row bits 0..2 go to
-// chunk bits 1..3 (conflict-free by the same measurement as fkv).
-__device__ __forceinline__ uint32_t fst(uint32_t row) { return (row & 7u) << 1; }
+// of one key pair and for the transposed reads (lds_read_tr).  S^T rows are
+// read 16 consecutive rows at one chunk and use fst.
 
 template <int C, int D>
 __device__ __forceinline__ u32x4 tr_frag(const char *lds, uint32_t base_k0, uint32_t lane_tr, uint32_t xtr,

@@ -77,6 +77,10 @@ __device__ __forceinline__ uint32_t fkv(uint32_t row) {
 // Per-lane constants of a transposed fragment read (lane l = 16g + 4r + c):
 // byte offset of its row and 8-byte half, and the XOR applied to the tile's
 // chunk index.
+// Chunk swizzle for tiles read as 16 consecutive rows at one 16-byte chunk
+// (plain reads): row bits 0..2 go to chunk bits 1..3 (conflict-free by the
+// same measurement as fkv).
+__device__ __forceinline__ uint32_t fst(uint32_t row) { return (row & 7u) << 1; }
 __device__ __forceinline__ uint32_t tr_lane_off(int l, int rowb) {
   return (8 * (l >> 4) + ((l & 15) >> 2)) * rowb + (l & 1) * 8;
 }
