@@ -25,8 +25,6 @@
 // fp32 path: lin_recurrent_f32 runs the recurrence S_t = lam S_{t-1} + k_t v_t^T,
 // o_t = q_t S_t token by token with one thread per d_v column (small shapes).
 
-#include <type_traits>
-
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
 
@@ -41,9 +39,9 @@ struct LinCfg {
   static constexpr int ND = D / 16;            // 16-wide feature tiles
   static constexpr int NDS = D / 32;           // 32-deep steps over features
   static constexpr int NKS = C / 32;           // 32-deep steps over chunk tokens
-  static constexpr int NQP = C / 32;           // pairs of 16-query tiles per chunk
-  static constexpr int WPP = 8 / NQP;          // waves sharing one query pair (split over d_v)
-  static constexpr int DVW = ND / WPP;         // output d_v tiles per wave
+  static constexpr int NQT = C / 16;           // 16-query tiles per chunk
+  static constexpr int WPQ = 8 / NQT;          // waves sharing one query tile (split over d_v)
+  static constexpr int DVW = ND / WPQ;         // output d_v tiles per wave
   static constexpr int SDV = ND * ND / 8;      // state tiles per wave (one d_k tile, SDV d_v tiles)
   static constexpr int RPP = NT / NCH;         // K/V rows staged per pass of the workgroup
   static constexpr int NSTG = C / RPP;         // staging passes (16-byte K and V pieces per thread)
@@ -55,16 +53,17 @@ struct LinCfg {
   static constexpr uint32_t RW = PW + (PWZ + C + 4) * 4;  // lam^(m-1-j) for the chunk's rows, 0 past m
   static constexpr uint32_t LDS = RW + C * 4;
   static_assert(DVW >= 1 && NSTG >= 1 && SDV >= 1, "unsupported chunk / head size");
-  // wave -> (query pair, d_v part).  Waves w and w+4 share a SIMD; they get
-  // query pairs from opposite ends of the chunk so the causal work per SIMD
-  // is even.
-  __device__ static void qrole(int w, int &gq, int &part) {
+  // wave -> (query tile, d_v part).  Waves w and w+4 share a SIMD; they get
+  // query tiles from opposite ends of the chunk, so the causal work (tile qt
+  // meets key pairs 0 .. qt/2) is even per SIMD, and no two waves compute the
+  // same decay-masked K Q^T tile.
+  __device__ static void qrole(int w, int &qt, int &part) {
     if (w < 4) {
-      gq = w % NQP;
-      part = w / NQP;
+      qt = w;
+      part = 0;
     } else {
-      gq = NQP - 1 - (w - 4) % NQP;
-      part = WPP / 2 + (w - 4) / NQP;
+      qt = NQT - 1 - (w - 4);
+      part = WPQ - 1;
     }
   }
 };
@@ -390,10 +389,14 @@ __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_stat
 }
 
 // ---------------------------------------------------------------- pass 3
-// F: q and k are normalised and rotated as they are staged (q then also goes
-// through LDS), and the output is gated; the gated rows are stored after the
-// state update so that the gate loads are in flight during it.
-template <int C, int D, bool F>
+// q, k and v of a chunk are staged through LDS in rows (a thread owns two
+// 16-byte pieces of a row); q and k are normalised and rotated there when the
+// neighbours ask for it, and the output is gated when a gate is given.  The
+// output rows are stored after the state update so that gate loads are in
+// flight during it.  (Loading q straight into MFMA fragments reads each row
+// in 64-byte pieces; the row-wise staging is faster even with nothing to
+// apply.)
+template <int C, int D>
 __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict__ q,
                                                       const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
                                                       int H, int N, int seg_len, int nseg, NbK nb) {
   using Cf = LinCfg<C, D>;
   using Fz = LinF<C, D>;
-  __shared__ __attribute__((aligned(16))) char lds[F ? Fz::LDS : Cf::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[Fz::LDS];
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
@@ -417,8 +420,8 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t *qb = q + head_off, *kb = k + head_off, *vb = v + head_off;
   uint16_t *ob = o + head_off;
-  int gq, part;
-  Cf::qrole(w, gq, part);
+  int qt, part;
+  Cf::qrole(w, qt, part);
   const int dvb = part * Cf::DVW;  // first output d_v tile of this wave
   const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
   const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
@@ -431,76 +434,47 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
     for (int i = 0; i < 4; ++i)
       Sacc[a][i] = sin ? sin[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] : 0.f;
 
-  // Q fragments (B operands of Q^T): query tiles 2gq, 2gq+1 of the chunk;
-  // rows past t_end load a clamped row whose outputs are never stored
-  u32x4 qf[F ? 1 : 2][F ? 1 : Cf::NDS];
-  auto load_q = [&](int c0) {
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      const int t = min(c0 + 32 * gq + 16 * tq + lr, t_end - 1);
-#pragma unroll
-      for (int s = 0; s < Cf::NDS; ++s) qf[tq][s] = gload16(qb + (size_t)t * D + 32 * s + 8 * g);
-    }
+  // Q fragment s (B operand of Q^T, query tile qt): read from the staged Q
+  // rows in LDS at each use
+  const int qq = 16 * qt + lr;  // this lane's query row in the chunk
+  auto qfrag = [&](int s) -> u32x4 {
+    return lds_load<u32x4>(lds + Fz::QN, qq * Cf::ROWB + (((4 * s + g) ^ fkv(qq)) & (Cf::NCH - 1)) * 16u);
   };
-  // Q fragment (tq, s): held in registers (plain form) or read from the
-  // staged, transformed Q rows in LDS at each use (F, which needs the VGPRs)
-  auto qfrag = [&](int tq, int s) -> u32x4 {
-    if constexpr (F) {
-      const uint32_t row = 32 * gq + 16 * tq + lr;
-      return lds_load<u32x4>(lds + Fz::QN, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
-    } else {
-      return qf[tq][s];
-    }
-  };
-  // this lane's output rows, gated by gv when given
-  auto store_out = [&](int c0, int m, const f32x4 (&Oacc)[Cf::DVW][2], const u32x2 (&gv)[2][Cf::DVW], bool gated) {
+  // this lane's output row, gated by gv when given
+  auto store_out = [&](int c0, int m, const f32x4 (&Oacc)[Cf::DVW], const u32x2 (&gv)[Cf::DVW], bool gated) {
+    if (qq < m) {
+      uint16_t *orow = ob + (size_t)(c0 + qq) * D;
 #pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      const int qq = 32 * gq + 16 * tq + lr;
-      if (qq < m) {
-        uint16_t *orow = ob + (size_t)(c0 + qq) * D;
-#pragma unroll
-        for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
-          f32x4 x = Oacc[dvi][tq];
-          if (gated) {
-            x[0] *= sigmoid_fast(bf16lo(gv[tq][dvi][0]));
-            x[1] *= sigmoid_fast(bf16hi(gv[tq][dvi][0]));
-            x[2] *= sigmoid_fast(bf16lo(gv[tq][dvi][1]));
-            x[3] *= sigmoid_fast(bf16hi(gv[tq][dvi][1]));
-          }
-          *reinterpret_cast<u32x2 *>(orow + 16 * (dvb + dvi) + 4 * g) =
-              u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        f32x4 x = Oacc[dvi];
+        if (gated) {
+          x[0] *= sigmoid_fast(bf16lo(gv[dvi][0]));
+          x[1] *= sigmoid_fast(bf16hi(gv[dvi][0]));
+          x[2] *= sigmoid_fast(bf16lo(gv[dvi][1]));
+          x[3] *= sigmoid_fast(bf16hi(gv[dvi][1]));
         }
+        *reinterpret_cast<u32x2 *>(orow + 16 * (dvb + dvi) + 4 * g) =
+            u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
       }
     }
   };
 
-  // next chunk's 16-byte staging pieces: plain layout, or (F) rows x halves
-  using XT = std::conditional_t<F, u32x4[Fz::NSF][2], u32x4[Cf::NSTG]>;
-  XT xk, xv;
-  u32x4 xq[F ? Fz::NSF : 1][2];
-  bool norm_q = false, norm_k = false, rope = false;
+  // next chunk's 16-byte staging pieces (rows x halves)
+  u32x4 xk[Fz::NSF][2], xv[Fz::NSF][2], xq[Fz::NSF][2];
   const int hc = tid % Fz::HC;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto qr = buf_rsrc(qb, head_bytes), kr = buf_rsrc(kb, head_bytes), vr = buf_rsrc(vb, head_bytes);
   const auto gr = buf_rsrc(nb.gate ? nb.gate + head_off : qb, head_bytes);
-  if constexpr (F) {
-    nb_tables<C, D>(lds, tid, nb);
-    norm_q = nb.gq != nullptr;
-    norm_k = nb.gk != nullptr;
-    rope = nb.rope_base > 0.f;
-    load_rows_f<C, D>(kr, tid, t_begin, t_end, xk);
-    load_rows_f<C, D>(vr, tid, t_begin, t_end, xv);
-    load_rows_f<C, D>(qr, tid, t_begin, t_end, xq);
-  } else {
-    load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
-    load_q(t_begin);
-  }
+  nb_tables<C, D>(lds, tid, nb);
+  const bool norm_q = nb.gq != nullptr, norm_k = nb.gk != nullptr, rope = nb.rope_base > 0.f;
+  load_rows_f<C, D>(kr, tid, t_begin, t_end, xk);
+  load_rows_f<C, D>(vr, tid, t_begin, t_end, xv);
+  load_rows_f<C, D>(qr, tid, t_begin, t_end, xq);
 
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
     __syncthreads();
-    if constexpr (F) {
+    {
       float bt[8], cs[8], sn[8];
       if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
 #pragma unroll
@@ -514,8 +488,6 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
       store_rows_f<C, D>(lds + Fz::QN, tid, m, xq);
       store_rows_f<C, D>(lds + Cf::KN, tid, m, xk);
       store_rows_f<C, D>(lds + Cf::VN, tid, m, xv);
-    } else {
-      store_kv<C, D>(lds, tid, m, xk, xv);
     }
     // bf16 copy of S^T (rows d_v, columns d_k) for the Q S product
 #pragma unroll
@@ -527,97 +499,68 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
     if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
     __syncthreads();
     if (c0 + C < t_end) {
-      if constexpr (F) {
-        load_rows_f<C, D>(kr, tid, c0 + C, t_end, xk);
-        load_rows_f<C, D>(vr, tid, c0 + C, t_end, xv);
-      } else {
-        load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
-      }
+      load_rows_f<C, D>(kr, tid, c0 + C, t_end, xk);
+      load_rows_f<C, D>(vr, tid, c0 + C, t_end, xv);
     }
 
-    // (1) O^T = lam^(qq+1) * S^T Q^T for d_v tiles dvb .. and both query tiles
-    f32x4 Oacc[Cf::DVW][2];
+    // (1) O^T = lam^(qq+1) * S^T Q^T for d_v tiles dvb .. of this wave's query tile
+    f32x4 Oacc[Cf::DVW];
 #pragma unroll
-    for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi][0] = Oacc[dvi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s) {
-      const u32x4 q0 = qfrag(0, s), q1 = qfrag(1, s);
+      const u32x4 q0 = qfrag(s);
 #pragma unroll
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
         const uint32_t row = 16 * (dvb + dvi) + lr;
         const u32x4 A = lds_load<u32x4>(lds + Cf::ST, row * Cf::ROWB + (((4 * s + g) ^ fst(row)) & (Cf::NCH - 1)) * 16u);
-        Oacc[dvi][0] = mfma16x16x32(A, q0, Oacc[dvi][0]);
-        Oacc[dvi][1] = mfma16x16x32(A, q1, Oacc[dvi][1]);
+        Oacc[dvi] = mfma16x16x32(A, q0, Oacc[dvi]);
       }
     }
+    {
+      const float f = pw[qq + 1];
 #pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      const float f = pw[32 * gq + 16 * tq + lr + 1];
-#pragma unroll
-      for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi][tq] *= f;
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi] *= f;
     }
     // (2)+(3) P^T = decay-masked K Q^T over the causal key pairs; O^T += V^T P^T
-    for (int p = 0; p <= gq; ++p) {
-      f32x4 P[2][2];
-#pragma unroll
-      for (int tq = 0; tq < 2; ++tq)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) P[tq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p <= qt / 2; ++p) {
+      f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int s = 0; s < Cf::NDS; ++s) {
-        const u32x4 q0 = qfrag(0, s), q1 = qfrag(1, s);
+        const u32x4 q0 = qfrag(s);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const uint32_t row = 32 * p + pair_key(t, lr);
           const u32x4 A = lds_load<u32x4>(lds + Cf::KN, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
-          P[0][t] = mfma16x16x32(A, q0, P[0][t]);
-          P[1][t] = mfma16x16x32(A, q1, P[1][t]);
+          P[t] = mfma16x16x32(A, q0, P[t]);
         }
       }
-      u32x4 Bp[2];
+      // lam^(qq-j), zero for j > qq: the table's zero entries below n = 0
+      // do the causal mask (qq - j >= -31 within the diagonal pair)
+      const int nb0 = qq - 32 * p - 8 * g;
 #pragma unroll
-      for (int tq = 0; tq < 2; ++tq) {
-        const int qq = 32 * gq + 16 * tq + lr;
-        // lam^(qq-j), zero for j > qq: the table's zero entries below n = 0
-        // do the causal mask (qq - j >= -31 within the diagonal pair)
-        const int nb0 = qq - 32 * p - 8 * g;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) P[tq][t][i] *= pw[nb0 - 4 * t - i];
-        Bp[tq] = u32x4{pack_bf16x2(P[tq][0][0], P[tq][0][1]), pack_bf16x2(P[tq][0][2], P[tq][0][3]),
-                       pack_bf16x2(P[tq][1][0], P[tq][1][1]), pack_bf16x2(P[tq][1][2], P[tq][1][3])};
-      }
+        for (int i = 0; i < 4; ++i) P[t][i] *= pw[nb0 - 4 * t - i];
+      const u32x4 Bp = u32x4{pack_bf16x2(P[0][0], P[0][1]), pack_bf16x2(P[0][2], P[0][3]),
+                             pack_bf16x2(P[1][0], P[1][1]), pack_bf16x2(P[1][2], P[1][3])};
 #pragma unroll
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
         const u32x4 A = tr_frag<C, D>(lds, Cf::VN + 32 * p * Cf::ROWB, lane_tr, xtr, dvb + dvi);
-        Oacc[dvi][0] = mfma16x16x32(A, Bp[0], Oacc[dvi][0]);
-        Oacc[dvi][1] = mfma16x16x32(A, Bp[1], Oacc[dvi][1]);
+        Oacc[dvi] = mfma16x16x32(A, Bp, Oacc[dvi]);
       }
     }
-    if constexpr (F) {
-      // gate values of this lane's outputs (clamped rows are never stored)
-      u32x2 gv[2][Cf::DVW] = {};
-      if (nb.gate) {
+    // gate values of this lane's outputs (a clamped row is never stored)
+    u32x2 gv[Cf::DVW] = {};
+    if (nb.gate) {
+      const uint32_t t = min(c0 + qq, t_end - 1);
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-          const uint32_t t = min(c0 + 32 * gq + 16 * tq + lr, t_end - 1);
-#pragma unroll
-          for (int dvi = 0; dvi < Cf::DVW; ++dvi) gv[tq][dvi] = bload8(gr, (t * D + 16 * (dvb + dvi) + 4 * g) * 2u);
-        }
-      }
-      if (c0 + C < t_end) load_rows_f<C, D>(qr, tid, c0 + C, t_end, xq);
-      // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V, then (4) the gated output rows
-      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
-      store_out(c0, m, Oacc, gv, nb.gate != nullptr);
-    } else {
-      if (c0 + C < t_end) load_q(c0 + C);  // the Q fragments are free from here on
-      // (4) this lane's output rows
-      const u32x2 nogate[2][Cf::DVW] = {};
-      store_out(c0, m, Oacc, nogate, false);
-      // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V
-      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) gv[dvi] = bload8(gr, (t * D + 16 * (dvb + dvi) + 4 * g) * 2u);
     }
+    if (c0 + C < t_end) load_rows_f<C, D>(qr, tid, c0 + C, t_end, xq);
+    // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V, then (4) the (gated) output row
+    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+    store_out(c0, m, Oacc, gv, nb.gate != nullptr);
   }
 
   if (state_out && seg == nseg - 1) {
@@ -683,8 +626,13 @@ void seg_plan(int BH, int N, int C, int *seg_len, int *nseg) {
   *nseg = (N + *seg_len - 1) / *seg_len;
 }
 
-template <int C, int D, bool F>
-hipError_t run_bf16(const LinearPrefillArgs &a, const NbK &nb, hipStream_t st) {
+template <int C, int D>
+hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+  NbK nb{nullptr, nullptr, 0.f, 0.f, 0, nullptr};
+  if (a.nb)
+    nb = NbK{a.nb->gamma_q, a.nb->gamma_k, a.nb->eps, a.nb->rope_base, a.nb->pos0,
+             static_cast<const uint16_t *>(a.nb->gate)};
+  const bool k_transformed = nb.gk != nullptr || nb.rope_base > 0.f;
   const int BH = a.B * a.H;
   int seg_len, nseg;
   seg_plan(BH, a.N, C, &seg_len, &nseg);
@@ -692,25 +640,20 @@ hipError_t run_bf16(const LinearPrefillArgs &a, const NbK &nb, hipStream_t st) {
   const size_t DD = (size_t)D * D;
   const float *seg_state = a.state_in;  // nseg == 1: segment 0 starts from state_in
   if (nseg > 1) {
-    hipLaunchKernelGGL((lin_seg_aggregate<C, D, F>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
+    if (k_transformed)
+      hipLaunchKernelGGL((lin_seg_aggregate<C, D, true>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
+                         (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
+    else
+      hipLaunchKernelGGL((lin_seg_aggregate<C, D, false>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
+                         (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws,
                        a.state_in, a.decay, a.H, (int)DD, a.N, seg_len, nseg);
     seg_state = ws;
   }
-  hipLaunchKernelGGL((lin_seg_output<C, D, F>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
+  hipLaunchKernelGGL((lin_seg_output<C, D>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, DD,
                      a.state_out, a.H, a.N, seg_len, nseg, nb);
   return hipGetLastError();
-}
-
-template <int C, int D>
-hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
-  NbK nb{nullptr, nullptr, 0.f, 0.f, 0, nullptr};
-  if (!a.nb) return run_bf16<C, D, false>(a, nb, st);
-  nb = NbK{a.nb->gamma_q, a.nb->gamma_k, a.nb->eps, a.nb->rope_base, a.nb->pos0,
-           static_cast<const uint16_t *>(a.nb->gate)};
-  return run_bf16<C, D, true>(a, nb, st);
 }
 
 }  // namespace
