@@ -128,3 +128,36 @@ def test_decode_step_at_1M_equals_plain_decode():
     assert torch.equal(kp, kp_f)
     assert torch.equal(idx, idx_f[:, :, 0])
     assert torch.equal(o, o_f)
+
+
+def test_generation_loop_fp32():
+    B, Hq, Hkv, d = 1, 4, 2, 64
+    topk, n_init, n_local = 2, 1, 1
+    T, cap = 64 * 4 + 3, 64 * 5
+    say("generation loop fp32", B, Hq, Hkv, d, T, cap)
+    x = I.sparse_inputs(B, Hq, Hkv, T, d, I.F32, 98, 1, 1.0 / 8.0, "cpu", shift_frac=0.3)
+    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.float32, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((B, Hkv, (cap + 63) // 64, d), dtype=torch.float32, device="cuda")
+    kw = dict(topk=topk, n_init=n_init, n_local=n_local)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o, idx = sala.sparse_prefill_chunk(sl(q, 0, 192), sl(k, 0, 192), sl(v, 0, 192), kc, vc, kp, 0, **kw)
+    idx_f, _ = sala.sparse_select(sl(q, 0, 192), sl(k, 0, 192), **kw)
+    o_f = sala.sparse_prefill(sl(q, 0, 192), sl(k, 0, 192), sl(v, 0, 192), idx_f)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_f) and torch.equal(o, o_f)
+    qh, kh, vh = host64(q[:, :, :192]), host64(k[:, :, :192]), host64(v[:, :, :192])
+    # attention over the GPU's selection (its indices equal the one-shot call's, which the
+    # selection tests pin to the oracle)
+    assert_close(o, OS.sparse_attention_prefill(qh, kh, vh, idx.cpu().numpy()), I.F32, "fp32 chunk vs oracle")
+    for t in range(192, T):
+        L = t + 1
+        o, idx = sala.sparse_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                                         kc, vc, kp, t, **kw)
+        idx_f, _ = sala.sparse_select(q[:, :, t:t + 1].contiguous(), sl(k, 0, L), **kw)
+        o_f = sala.sparse_decode(q[:, :, t].contiguous(), sl(k, 0, L), sl(v, 0, L), idx_f[:, :, 0].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_f[:, :, 0]) and torch.equal(o, o_f), f"fp32 step {t}"
+    ro = OS.sparse_attention_decode(host64(q[:, :, T - 1]), host64(k), host64(v), idx.cpu().numpy(), T)
+    assert_close(o, ro, I.F32, "fp32 last step vs oracle")
