@@ -187,7 +187,8 @@ def measure_ceilings(torch, sala):
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": round(mfma, 1), "copy_gbs": round(copy, 1),
             "method": "in-repo microkernels: 512 workgroups x 8 waves x 20000 rounds of 8 independent bf16 MFMA "
-                      "16x16x32; 1 GiB device copy with 16-byte loads/stores (read + write bytes); best of 5"}
+                      "16x16x32; 1 GiB device copy, one contiguous 16 KiB run per workgroup with nontemporal 16-byte "
+                      "loads/stores (read + write bytes); best of 5"}
 
 
 def bench_dense(torch, sala, sp, group_ms):
