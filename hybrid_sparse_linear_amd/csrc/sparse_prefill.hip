@@ -115,26 +115,37 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
     diag_sh = has_diag;
   }
 
-  // Q fragments (B operand of K Q^T): lane holds Q[t = 64 i_loc + 16qt + lr][32s + 8lg .. +7]
+  // Q fragments (B operand of K Q^T): lane holds Q[t = 64 i_loc + 16qt + lr][32s + 8lg .. +7],
+  // multiplied by scale * log2(e) and rounded to bf16 once, so that the MFMA
+  // yields exponents in log2 units directly (the rounding moves a score by
+  // about 2^-9 of its size, below the rounding of P to bf16)
   const uint16_t *qb = q + ((size_t)(b * Hq + hq) * Nq) * D;
   u32x4 qf[2][Cf::NDS];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int t = BLK * i_loc + 16 * (qt0 + a) + lr;
 #pragma unroll
-    for (int s = 0; s < Cf::NDS; ++s)
-      qf[a][s] = (t < Nq) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < Cf::NDS; ++s) {
+      u32x4 x = (t < Nq) ? gload16(qb + (size_t)t * D + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = pack_bf16x2(bf16lo(x[e]) * scale_log2, bf16hi(x[e]) * scale_log2);
+      qf[a][s] = x;
+    }
   }
 
   f32x4 Oacc[2][Cf::ND];
   f32x4 Lacc[2];  // row sums of P, accumulated on MFMA against a tile of ones
-  float mref[2];  // per-row reference max (log2 units) used by the exponentials
+  // Per-row reference (log2 units) of the exponentials, kept as -ref in all
+  // four elements: it is the accumulator the score MFMAs start from, so the
+  // tile comes out as score - ref.  The first block sets it.
+  f32x4 negm[2];
+  bool first = true;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
 #pragma unroll
     for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] = f32x4{0.f, 0.f, 0.f, 0.f};
     Lacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mref[a] = -INFINITY;
+    negm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
@@ -176,16 +187,17 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // this wave's direct loads done (vmcnt 0); the barrier that follows publishes them
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  // One block: S^T = K Q^T (tiles [kt][a], lane holds keys 32p + 8lg + 4t + e
-  // for kt = 2p + t), softmax numerators against a per-row reference max that
-  // moves (rescaling O and L) only when the block max exceeds it by more than
-  // 2^8, then O^T += V^T P^T and L += 1 P^T.
+  // One block: S^T = K Q^T - ref (tiles [kt][a], lane holds keys
+  // 32p + 8lg + 4t + e for kt = 2p + t), softmax numerators exp2(S) against
+  // the per-row reference, which moves up (rescaling O and L) only when the
+  // block max exceeds it by more than 8 (a factor 2^8), then O^T += V^T P^T
+  // and L += 1 P^T.
   auto step = [&](const char *kbuf, const char *vbuf, bool mask) {
     f32x4 S[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) S[kt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < 2; ++a) S[kt][a] = negm[a];
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s) {
 #pragma unroll
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
         for (int a = 0; a < 2; ++a) S[kt][a] = mfma16x16x32(A, qf[a][s], S[kt][a]);
       }
     }
-    float mb[2];
+    float mb[2];  // block max over the row, relative to the reference
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       float mx = -INFINITY;
@@ -210,19 +222,23 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
           }
           mx = fmaxf(mx, S[kt][a][e]);
         }
-      mx = row4_max(mx);
-      mb[a] = mx * scale_log2;
+      mb[a] = row4_max(mx);
     }
-    if (__any((mb[0] > mref[0] + 8.0f) || (mb[1] > mref[1] + 8.0f))) {
+    if (__any(first || (mb[0] > 8.0f) || (mb[1] > 8.0f))) {
+      // move the reference up by d >= 0 (on the first block: to the block
+      // max; every row has an unmasked key there, so the max is finite)
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const float mnew = fmaxf(mref[a], mb[a]);
-        const float alpha = __builtin_amdgcn_exp2f(mref[a] - mnew);
-        mref[a] = mnew;
+        const float d = first ? mb[a] : fmaxf(mb[a], 0.f);
+        const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
         for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] *= alpha;
         Lacc[a] *= alpha;
+        negm[a] -= d;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) S[kt][a] -= d;
       }
+      first = false;
     }
     u32x4 Pf[2][2];
 #pragma unroll
@@ -231,7 +247,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[kt][e] = __builtin_amdgcn_exp2f(fmaf(S[kt][a][e], scale_log2, -mref[a]));
+        for (int e = 0; e < 4; ++e) p[kt][e] = __builtin_amdgcn_exp2f(S[kt][a][e]);
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
         Pf[a][pp] = u32x4{pack_bf16x2(p[2 * pp][0], p[2 * pp][1]), pack_bf16x2(p[2 * pp][2], p[2 * pp][3]),
