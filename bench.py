@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # x1.0); summary in profiles/sparse_attn_256K_hbm_traffic.md.  It holds only
 # for the kernel sources it was measured on: reported as null otherwise.
 TRAFFIC_MEASURED = {
-    "sources_sha256": "a63c42e7647a67b2709fe5c7830bb74f9eecc5ec4447d2e19e13606215ee672e",
-    "fetch_kib": 8945101.5, "fetch_scale": 2.0,
-    "write_kib": 2552116.625, "write_scale": 1.0,
+    "sources_sha256": "06adb2f0685656d975941f856b3cb883a11204768aede60a810cf04ac991244e",
+    "fetch_kib": 9051647.0625, "fetch_scale": 2.0,
+    "write_kib": 3007610.25, "write_scale": 1.0,
 }
 TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
 
