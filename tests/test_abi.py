@@ -125,6 +125,22 @@ def test_sparse_prefill_and_decode_validation():
     assert L.sala_sparse_decode_workspace(BF16, 4, 32, 2, 1 << 20, 128, 64, 67) > 0
 
 
+def test_empty_inputs_are_rejected():
+    # a zero batch, head count or length is an argument error at every entry
+    # point, reported before any device work
+    L = _lib.lib()
+    assert lp(N=0) == INVALID and lp(H=0) == INVALID
+    assert L.sala_linear_decode(BF16, 0, 2, 128, A, A, A, A, NUL, A, NUL) == INVALID
+    assert L.sala_linear_decode(BF16, 1, 0, 128, A, A, A, A, NUL, A, NUL) == INVALID
+    assert ss(L=0, Nq=0) == INVALID and ss(B=0) == INVALID and ss(Hkv=0) == INVALID
+    f = L.sala_sparse_prefill
+    assert f(BF16, 0, 4, 2, 256, 128, 64, 7, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == INVALID
+    assert f(BF16, 1, 4, 2, 0, 128, 64, 7, ctypes.c_float(0.1), A, A, A, A, A, NUL, 0, NUL) == INVALID
+    g = L.sala_sparse_decode
+    assert g(BF16, 1, 32, 2, 0, 128, 64, 67, ctypes.c_float(0.1), A, A, A, A, A, A, 1 << 30, NUL) == INVALID
+    assert g(BF16, 0, 32, 2, 4096, 128, 64, 67, ctypes.c_float(0.1), A, A, A, A, A, A, 1 << 30, NUL) == INVALID
+
+
 def test_dense_prefill_and_ceiling_validation():
     L = _lib.lib()
     f = L.sala_dense_prefill
