@@ -47,6 +47,40 @@ TRAFFIC_MEASURED = {
 TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
 
 
+class ClockSampler:
+    """Samples the GPU shader clock (MHz, through torch.cuda.clock_rate) from
+    a host thread while the timed steps run.  The published peaks are quoted
+    at 2400 MHz; the median of the busy samples (>= 500 MHz, the lowest busy
+    level) is the clock the kernels actually ran at, or None when the clock
+    cannot be read."""
+
+    def __init__(self, torch, period_s=0.05):
+        import threading
+        self.torch, self.period, self.samples = torch, period_s, []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            try:
+                self.samples.append(int(self.torch.cuda.clock_rate(0)))
+            except Exception:
+                return
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+
+    def mhz(self):
+        busy = sorted(c for c in self.samples if c >= 500)
+        return busy[len(busy) // 2] if busy else None
+
+
 def measured_traffic_bytes():
     """Counter-measured HBM bytes per sparse_attn_bf16 launch, or None when the
     kernel sources differ from the ones the counters were taken on."""
@@ -420,11 +454,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(record=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with ClockSampler(torch) as clock:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(record=True)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    sclk = clock.mhz()
     ms = elapsed * 1000.0 / args.steps
     att_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
     flops = sparse_flops(idx, N, d, Hq // Hkv)
@@ -456,7 +492,9 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (counters, N=262144 only)",
                      "algorithmic_bytes_per_launch": alg_bytes,
-                     "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4)},
+                     "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4),
+                     "sclk_mhz": sclk,
+                     "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4)},
     }
     if not args.no_dense:
         out["dense_comparison"] = bench_dense(torch, sala, sp, ms)
