@@ -164,7 +164,22 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // the diagonal block beyond every query, which causality masks.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto blk = [&](int e) { return DENSE ? e : sel[e]; };  // e-th block to process
-  const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);  // V^T fragment reads
+  // Per-lane LDS byte offsets of the operand reads, computed once.  K: the
+  // four rows a lane reads per block (keys r0, r0 + 4, r0 + 32, r0 + 36 with
+  // r0 = pair_key(0, lr)) differ only in row bits 2 and 5, which the swizzle
+  // does not use, so one offset per 32-deep feature step s serves all four and
+  // the row difference is a constant.  V^T: one offset per d_v tile; the key
+  // half is a constant.
+  uint32_t koffs[Cf::NDS], voffs[Cf::ND];
+  {
+    const int r0 = pair_key(0, lr);
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s) koffs[s] = (uint32_t)(r0 * Cf::KCH + swz_k<Cf::KCH>(r0, 4 * s + lg)) * 16u;
+    const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);
+#pragma unroll
+    for (int dv = 0; dv < Cf::ND; ++dv)
+      voffs[dv] = tr_off + (((uint32_t)(2 * dv) ^ tr_xor) & (uint32_t)(Cf::KCH - 1)) * 16u;
+  }
   uint32_t koff[Cf::PER_T], voff[Cf::PER_T];
 #pragma unroll
   for (int u = 0; u < Cf::PER_T; ++u) {
@@ -194,16 +209,27 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // and L += 1 P^T.
   auto step = [&](const char *kbuf, const char *vbuf, bool mask) {
     f32x4 S[4][2];
+    if (mask) {  // the diagonal block: keys after the query start from -inf, which the MFMAs keep
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) S[kt][a] = negm[a];
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + e;
+            S[kt][a][e] = (key > 16 * (qt0 + a) + lr) ? -INFINITY : negm[a][e];
+          }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) S[kt][a] = negm[a];
+    }
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const int row = 32 * (kt >> 1) + pair_key(kt & 1, lr);
-        const u32x4 A = lds_load<u32x4>(kbuf, (row * Cf::KCH + swz_k<Cf::KCH>(row, 4 * s + lg)) * 16u);
+        const u32x4 A = lds_load<u32x4>(kbuf + (32 * (kt >> 1) + 4 * (kt & 1)) * Cf::ROWB, koffs[s]);
 #pragma unroll
         for (int a = 0; a < 2; ++a) S[kt][a] = mfma16x16x32(A, qf[a][s], S[kt][a]);
       }
@@ -215,13 +241,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (mask) {
-            const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + e;
-            if (key > 16 * (qt0 + a) + lr) S[kt][a][e] = -INFINITY;
-          }
-          mx = fmaxf(mx, S[kt][a][e]);
-        }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kt][a][e]);
       mb[a] = row4_max(mx);
     }
     if (__any(first || (mb[0] > 8.0f) || (mb[1] > 8.0f))) {
@@ -258,7 +278,9 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
     for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
       for (int dv = 0; dv < Cf::ND; ++dv) {
-        const u32x4 A = tr_frag(vbuf, 32 * pp * Cf::ROWB, tr_off, tr_xor, dv, Cf::KCH, Cf::ROWB);
+        const char *vh = vbuf + 32 * pp * Cf::ROWB;
+        const u32x2 lo = lds_read_tr(vh, voffs[dv]), hi = lds_read_tr(vh + 4 * Cf::ROWB, voffs[dv]);
+        const u32x4 A = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int a = 0; a < 2; ++a) Oacc[a][dv] = mfma16x16x32(A, Pf[a][pp], Oacc[a][dv]);
       }
