@@ -169,6 +169,13 @@ __device__ __forceinline__ float row4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), __builtin_bit_cast(bf16x2v, 0x3F803F80u),
+                                         acc, false);
+}
+
 // 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));

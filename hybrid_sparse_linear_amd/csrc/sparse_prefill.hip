@@ -134,7 +134,10 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   }
 
   f32x4 Oacc[2][Cf::ND];
-  f32x4 Lacc[2];  // row sums of P, accumulated on MFMA against a tile of ones
+  // row sums of P: each lane sums its 16 keys of the row (the bf16 values the
+  // MFMAs use, two per dot product against (1, 1)); the four lanes of a row
+  // are added at the end
+  float lsum[2];
   // Per-row reference (log2 units) of the exponentials, kept as -ref in all
   // four elements: it is the accumulator the score MFMAs start from, so the
   // tile comes out as score - ref.  The first block sets it.
@@ -144,10 +147,9 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   for (int a = 0; a < 2; ++a) {
 #pragma unroll
     for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Lacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[a] = 0.f;
     negm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
   __syncthreads();
   const int nvalid = nvalid_sh;
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   // 32p + 8lg + 4t + e for kt = 2p + t), softmax numerators exp2(S) against
   // the per-row reference, which moves up (rescaling O and L) only when the
   // block max exceeds it by more than 8 (a factor 2^8), then O^T += V^T P^T
-  // and L += 1 P^T.
+  // and the lane's row-sum part grows by its 16 values of P.
   auto step = [&](const char *kbuf, const char *vbuf, bool mask) {
     f32x4 S[4][2];
     if (mask) {  // the diagonal block: keys after the query start from -inf, which the MFMAs keep
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
         const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
         for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] *= alpha;
-        Lacc[a] *= alpha;
+        lsum[a] *= alpha;
         negm[a] -= d;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) S[kt][a] -= d;
@@ -285,7 +287,9 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
         for (int a = 0; a < 2; ++a) Oacc[a][dv] = mfma16x16x32(A, Pf[a][pp], Oacc[a][dv]);
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a) Lacc[a] = mfma16x16x32(ones, Pf[a][pp], Lacc[a]);
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lsum[a] = dot2_bf16_ones(Pf[a][pp][e], lsum[a]);
     }
   };
 
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
   uint16_t *ob = o + ((size_t)(b * Hq + hq) * Nq) * D;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const float lt = Lacc[a][0];
+    const float lt = row4_sum(lsum[a]);
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
     const int t = BLK * i_loc + 16 * (qt0 + a) + lr;
     if (t < Nq) {
