@@ -236,22 +236,29 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
         for (int a = 0; a < 2; ++a) S[kt][a] = mfma16x16x32(A, qf[a][s], S[kt][a]);
       }
     }
-    float mb[2];  // block max over the row, relative to the reference
+    // Whether any score of the wave is more than 8 above its row's reference
+    // needs only this lane's max and a ballot; the row maxima themselves are
+    // formed only when the reference has to move.
+    float mx = -INFINITY;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      float mx = -INFINITY;
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kt][a][e]);
-      mb[a] = row4_max(mx);
-    }
-    if (__any(first || (mb[0] > 8.0f) || (mb[1] > 8.0f))) {
-      // move the reference up by d >= 0 (on the first block: to the block
-      // max; every row has an unmasked key there, so the max is finite)
+    if (__any(first || (mx > 8.0f))) {
+      // move the reference up by d >= 0, d the row's block max (on the first
+      // block the reference is set to it; every row has an unmasked key
+      // there, so the max is finite)
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const float d = first ? mb[a] : fmaxf(mb[a], 0.f);
+        float ma = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ma = fmaxf(ma, S[kt][a][e]);
+        ma = row4_max(ma);
+        const float d = first ? ma : fmaxf(ma, 0.f);
         const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
         for (int dv = 0; dv < Cf::ND; ++dv) Oacc[a][dv] *= alpha;
