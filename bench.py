@@ -56,11 +56,11 @@ class ClockSampler:
 
     def __init__(self, torch, period_s=0.05):
         import threading
-        self.torch, self.period, self.samples = torch, period_s, []
+        self.torch, self.period, self.samples, self.error = torch, period_s, [], None
         try:
             torch.cuda.clock_rate(0)  # the first query sets up amd-smi (slow); keep it out of the timed steps
-        except Exception:
-            pass
+        except Exception as e:
+            self.error = repr(e)[:200]
         self.stop = threading.Event()
         self.thread = threading.Thread(target=self._run, daemon=True)
 
@@ -68,7 +68,8 @@ class ClockSampler:
         while not self.stop.is_set():
             try:
                 self.samples.append(int(self.torch.cuda.clock_rate(0)))
-            except Exception:
+            except Exception as e:
+                self.error = repr(e)[:200]
                 return
             self.stop.wait(self.period)
 
@@ -458,13 +459,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    with ClockSampler(torch) as clock:
+    with ClockSampler(torch, period_s=0.02) as clock:
         t0 = time.perf_counter()
         for _ in range(args.steps):
             step(record=True)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-    sclk = clock.mhz()
+    group_sclk = clock.mhz()
+    # the sparse kernel's own clock: ten more launches with the sampler on
+    with ClockSampler(torch, period_s=0.02) as sclock:
+        for _ in range(10):
+            sala.sparse_prefill(sp["q"], sp["k"], sp["v"], idx, out=o_sp, workspace=ws_att)
+        torch.cuda.synchronize()
+    sclk = sclock.mhz()
     ms = elapsed * 1000.0 / args.steps
     att_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
     flops = sparse_flops(idx, N, d, Hq // Hkv)
@@ -497,7 +504,7 @@ def main():
                      "traffic_unit": "HBM bytes per launch (counters, N=262144 only)",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4),
-                     "sclk_mhz": sclk,
+                     "sclk_mhz": sclk, "group_step_sclk_mhz": group_sclk,
                      "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4)},
     }
     if not args.no_dense:
