@@ -418,7 +418,7 @@ def bench_decode(torch, sala, I, reps=20):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: libsala has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     import hybrid_sparse_linear_amd as sala

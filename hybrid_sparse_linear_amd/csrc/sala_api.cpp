@@ -45,7 +45,7 @@ int check_dtype(int dtype) {
 
 int check_d(int d) {
   if (d <= 0) return fail(SALA_ERR_INVALID_ARG, "d = %d must be positive", d);
-  if (d != 64 && d != 128) return fail(SALA_ERR_UNSUPPORTED, "d = %d: this build supports 64 and 128", d);
+  if (d != 64 && d != 128) return fail(SALA_ERR_UNSUPPORTED, "d = %d: libsala supports 64 and 128", d);
   return SALA_OK;
 }
 
@@ -67,7 +67,7 @@ int check_sparse_common(int B, int Hq, int Hkv, int block, int topk_or_nsel, con
   REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1, SALA_ERR_INVALID_ARG, "B, Hq, Hkv must be >= 1");
   REQUIRE(Hq % Hkv == 0, SALA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   REQUIRE(block >= 1, SALA_ERR_INVALID_ARG, "block must be >= 1");
-  REQUIRE(block == 64, SALA_ERR_UNSUPPORTED, "block = %d: this build supports 64", block);
+  REQUIRE(block == 64, SALA_ERR_UNSUPPORTED, "block = %d: libsala supports 64", block);
   REQUIRE(topk_or_nsel >= 0, SALA_ERR_INVALID_ARG, "%s must be >= 0", what);
   return SALA_OK;
 }
@@ -103,7 +103,7 @@ int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk, const 
   if ((s = check_dtype(dtype))) return s;
   REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
   if ((s = check_d(d))) return s;
-  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: this build supports 64 and 128", chunk);
+  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: libsala supports 64 and 128", chunk);
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(k, "k");
   REQUIRE_PTR(v, "v");
@@ -153,7 +153,7 @@ int sala_linear_prefill_fused(int dtype, int B, int H, int N, int d, int chunk, 
   REQUIRE(dtype == SALA_BF16, SALA_ERR_UNSUPPORTED, "the fused linear prefill is bf16 only");
   REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
   if ((s = check_d(d))) return s;
-  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: this build supports 64 and 128", chunk);
+  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: libsala supports 64 and 128", chunk);
   REQUIRE((long long)N * d * 2 < (1ll << 31), SALA_ERR_UNSUPPORTED, "one head's rows must stay under 2 GiB");
   REQUIRE(pos0 >= 0 && pos0 < (1ll << 40), SALA_ERR_INVALID_ARG, "pos0 must be in [0, 2^40)");
   REQUIRE_PTR(q, "q");

@@ -50,7 +50,7 @@ typedef enum {
 typedef enum {
   SALA_OK = 0,
   SALA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or shape     */
-  SALA_ERR_UNSUPPORTED = -2, /* valid request outside what this build covers   */
+  SALA_ERR_UNSUPPORTED = -2, /* valid request outside what libsala covers      */
   SALA_ERR_WORKSPACE = -3,   /* ws too small (query the *_workspace call)      */
   SALA_ERR_HIP = -4          /* a HIP launch/runtime call failed               */
 } sala_status;
