@@ -96,21 +96,26 @@ __device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, 
   }
 }
 // Registers -> K_lds / V_lds (natural layout, fkv-swizzled); chunk rows at or
-// past m are written as zero.
+// past m are written as zero (only the last chunk of a segment can be short,
+// so full chunks take a branch without the per-dword selects).
 template <int C, int D>
 __device__ __forceinline__ void store_kv(char *lds, int tid, int m, const u32x4 (&xk)[LinCfg<C, D>::NSTG],
                                          const u32x4 (&xv)[LinCfg<C, D>::NSTG]) {
   using Cf = LinCfg<C, D>;
   const uint32_t ch = tid % Cf::NCH;
   const u32x4 zero = {0, 0, 0, 0};
+  auto store = [&](bool whole) {
 #pragma unroll
-  for (int u = 0; u < Cf::NSTG; ++u) {
-    const uint32_t row = tid / Cf::NCH + Cf::RPP * u;
-    const uint32_t off = row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
-    const bool live = (int)row < m;
-    lds_store(lds + Cf::KN, off, live ? xk[u] : zero);
-    lds_store(lds + Cf::VN, off, live ? xv[u] : zero);
-  }
+    for (int u = 0; u < Cf::NSTG; ++u) {
+      const uint32_t row = tid / Cf::NCH + Cf::RPP * u;
+      const uint32_t off = row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
+      const bool live = whole || (int)row < m;
+      lds_store(lds + Cf::KN, off, live ? xk[u] : zero);
+      lds_store(lds + Cf::VN, off, live ? xv[u] : zero);
+    }
+  };
+  if (m >= C) store(true);
+  else store(false);
 }
 
 // State update for this wave's tiles (d_k tile sdk, d_v tiles sdv0 ..):
@@ -185,24 +190,28 @@ __device__ __forceinline__ void load_rows_f(__amdgpu_buffer_rsrc_t xr, int tid, 
   }
 }
 // Rows -> LDS in the plain layout (fkv-swizzled 16-byte chunks); rows at or
-// past m are written as zero.
+// past m are written as zero (full chunks skip the per-dword selects).
 template <int C, int D>
 __device__ __forceinline__ void store_rows_f(char *dst, int tid, int m, const u32x4 (&x)[LinF<C, D>::NSF][2]) {
   using F = LinF<C, D>;
   using Cf = LinCfg<C, D>;
   const uint32_t hc = tid % F::HC;
   const u32x4 zero = {0, 0, 0, 0};
+  auto store = [&](bool whole) {  // whole: a full chunk, no row past the end
 #pragma unroll
-  for (int u = 0; u < F::NSF; ++u) {
-    const uint32_t row = tid / F::HC + F::RPF * u;
-    if (F::RPF * F::NSF > C && row >= (uint32_t)C) continue;
-    const bool live = (int)row < m;
+    for (int u = 0; u < F::NSF; ++u) {
+      const uint32_t row = tid / F::HC + F::RPF * u;
+      if (F::RPF * F::NSF > C && row >= (uint32_t)C) continue;
+      const bool live = whole || (int)row < m;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t ch = hc + F::HC * h;
-      lds_store(dst, row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u, live ? x[u][h] : zero);
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t ch = hc + F::HC * h;
+        lds_store(dst, row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u, live ? x[u][h] : zero);
+      }
     }
-  }
+  };
+  if (m >= C) store(true);
+  else store(false);
 }
 // theta_i / 2pi for i < D/2 (fp64 and fp32) and the norm weights into LDS.
 template <int C, int D>
