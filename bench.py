@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # x1.0); summary in profiles/sparse_attn_256K_hbm_traffic.md.  It holds only
 # for the kernel sources it was measured on: reported as null otherwise.
 TRAFFIC_MEASURED = {
-    "sources_sha256": "ddda4a7135d3c9c4b2b4b3191434b5879b9a1f0d86b4a993d40b623df0e0f191",
+    "sources_sha256": "3165e02afc7b25a64d8db24136472ceda6fea0c1e0d56b6961c851c3e28aaaa6",
     "fetch_kib": 8795024.8125, "fetch_scale": 2.0,
     "write_kib": 2097153.59375, "write_scale": 1.0,
 }

@@ -11,18 +11,20 @@
 // staged on chip, an online softmax, no score matrix in HBM -- is used here.
 //
 // bf16 design (MI355X):
-//   * One workgroup = 4 waves = 4 query heads of one GQA group x the 64 tokens
-//     of one query block.  All heads of a group share the selected blocks, so
-//     every gathered 64-key block (16 KiB of K + 16 KiB of V at d = 128) feeds
-//     256 query rows from LDS.
+//   * One workgroup = 8 waves = 4 query heads of one GQA group x the 64 tokens
+//     of one query block (a wave: one head, two 16-token query tiles).  All
+//     heads of a group share the selected blocks, so every gathered 64-key
+//     block (16 KiB of K + 16 KiB of V at d = 128) feeds 256 query rows from
+//     LDS.
 //   * S^T = K Q^T on MFMA 16x16x32 (A = K rows from LDS, B = Q rows held in
-//     registers), so each lane owns one query row and 16 keys per tile row:
-//     row max/sum need only two cross-lane steps per block.
+//     registers, pre-scaled to log2 units), so each lane owns one query row
+//     and 16 keys per tile: a row max needs two cross-lane steps, taken only
+//     when the softmax reference has to move.
 //   * O^T += V^T P^T with V staged row-major in LDS and its V^T operand
 //     fragments read with the gfx950 transposed LDS read (two
 //     ds_read_b64_tr_b16 per fragment): no transposed copy of V anywhere.
-//   * K and V^T blocks are double buffered in LDS; the next block's global
-//     loads are issued before the current block's MFMAs.
+//   * K and V blocks are double buffered in LDS; the next block's direct
+//     buffer-to-LDS loads are issued before the current block's MFMAs.
 //   * Workgroups of one (b, kv head, query block) land on the same XCD so the
 //     gathered blocks are shared in that XCD's L2.
 // fp32 path: sparse_attn_f32, one thread per query token, fp32 FMA.
