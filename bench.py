@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # for the kernel sources it was measured on: reported as null otherwise.
 TRAFFIC_MEASURED = {
     "sources_sha256": "3165e02afc7b25a64d8db24136472ceda6fea0c1e0d56b6961c851c3e28aaaa6",
-    "fetch_kib": 8795024.8125, "fetch_scale": 2.0,
-    "write_kib": 2097153.59375, "write_scale": 1.0,
+    "fetch_kib": 8798300.1875, "fetch_scale": 2.0,
+    "write_kib": 2097153.78125, "write_scale": 1.0,
 }
 TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
 
