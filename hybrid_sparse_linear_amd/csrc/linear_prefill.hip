@@ -532,7 +532,12 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi] *= f;
     }
     // (2)+(3) P^T = decay-masked K Q^T over the causal key pairs; O^T += V^T P^T
-    for (int p = 0; p <= qt / 2; ++p) {
+    // unrolled over the chunk's key pairs (the bound is the wave's uniform
+    // query tile), so every LDS address below is a fixed register plus an
+    // immediate offset rather than a per-pair add
+#pragma unroll
+    for (int p = 0; p < (Cf::NQT + 1) / 2; ++p) {
+      if (p > qt / 2) break;
       f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int s = 0; s < Cf::NDS; ++s) {
