@@ -459,18 +459,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    with ClockSampler(torch, period_s=0.02) as clock:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step(record=True)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-    group_sclk = clock.mhz()
-    # the sparse kernel's own clock: ten more launches with the sampler on
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # the sparse kernel's own clock: back-to-back launches for at least 0.6 s
+    # (at least ten) with the sampler on
     with ClockSampler(torch, period_s=0.02) as sclock:
-        for _ in range(10):
+        t_clk, n_clk = time.perf_counter() + 0.6, 0
+        while n_clk < 10 or time.perf_counter() < t_clk:
             sala.sparse_prefill(sp["q"], sp["k"], sp["v"], idx, out=o_sp, workspace=ws_att)
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            n_clk += 1
     sclk = sclock.mhz()
     ms = elapsed * 1000.0 / args.steps
     att_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
@@ -504,7 +505,7 @@ def main():
                      "traffic_unit": "HBM bytes per launch (counters, N=262144 only)",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 4), "avg_launch_ms": round(att_ms, 4),
-                     "sclk_mhz": sclk, "group_step_sclk_mhz": group_sclk,
+                     "sclk_mhz": sclk, "sclk_samples": len(sclock.samples),
                      "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4)},
     }
     if not args.no_dense:
@@ -521,6 +522,8 @@ def main():
     if not args.no_cpu_baseline:
         lin1 = [I.workload2_linear(0, "cuda", N=8192, workload=4)]
         out["cpu_baseline"] = cpu_baseline(lin1, sp, idx, args.cpu_sample_seconds)
+    if out["roofline"]["sclk_mhz"] is None and sclock.error:
+        out["roofline"]["sclk_error"] = sclock.error
     print(json.dumps(out), flush=True)
 
 
