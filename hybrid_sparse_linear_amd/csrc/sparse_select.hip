@@ -130,8 +130,11 @@ __global__ __launch_bounds__(256) void kv_append(const T *__restrict__ k_new, co
 __global__ __launch_bounds__(256) void score_tiles(const float *__restrict__ qbar, const float *__restrict__ kbar,
                                                    float *__restrict__ scores, int NQB, int NB, int NBs, int qb0,
                                                    int nTk, int d, float inv_sqrt_d) {
-  __shared__ float qs[64][129];
-  __shared__ float ks[64][129];
+  // rows padded to 132 floats: 16-byte aligned for the float4 reads below, and
+  // 16 consecutive rows start 4 banks apart, so a wave's float4 reads of 16
+  // rows cover the 64 banks once
+  __shared__ __attribute__((aligned(16))) float qs[64][132];
+  __shared__ __attribute__((aligned(16))) float ks[64][132];
   const int T = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   int I, J;
   if (nTk == 0) {
@@ -146,24 +149,34 @@ __global__ __launch_bounds__(256) void score_tiles(const float *__restrict__ qba
   }
   const float *qb = qbar + ((size_t)bh * NQB + 64 * I) * d;
   const float *kb = kbar + ((size_t)bh * NBs + 64 * J) * d;
-  for (int e = tid; e < 64 * d; e += 256) {
-    const int r = e / d, c = e % d;
-    qs[r][c] = (64 * I + r < NQB) ? qb[(size_t)r * d + c] : 0.f;
-    ks[r][c] = (64 * J + r < NB) ? kb[(size_t)r * d + c] : 0.f;
+  const int d4 = d / 4;
+  for (int e = tid; e < 64 * d4; e += 256) {
+    const int r = e / d4, c = 4 * (e % d4);
+    const float4 zero = {0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<float4 *>(&qs[r][c]) =
+        (64 * I + r < NQB) ? *reinterpret_cast<const float4 *>(qb + (size_t)r * d + c) : zero;
+    *reinterpret_cast<float4 *>(&ks[r][c]) =
+        (64 * J + r < NB) ? *reinterpret_cast<const float4 *>(kb + (size_t)r * d + c) : zero;
   }
   __syncthreads();
   const int ty = tid / 16, tx = tid % 16;
   float acc[4][4] = {};
-  for (int kk = 0; kk < d; ++kk) {
-    float a[4], bb[4];
+  // four features per LDS read; each accumulator still sums kk = 0, 1, 2, ... in order
+  for (int kk = 0; kk < d; kk += 4) {
+    float4 a[4], bb[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = qs[ty + 16 * r][kk];
+    for (int r = 0; r < 4; ++r) a[r] = *reinterpret_cast<const float4 *>(&qs[ty + 16 * r][kk]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) bb[c] = ks[tx + 16 * c][kk];
+    for (int c = 0; c < 4; ++c) bb[c] = *reinterpret_cast<const float4 *>(&ks[tx + 16 * c][kk]);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], bb[c], acc[r][c]);
+      for (int c = 0; c < 4; ++c) {
+        acc[r][c] = fmaf(a[r].x, bb[c].x, acc[r][c]);
+        acc[r][c] = fmaf(a[r].y, bb[c].y, acc[r][c]);
+        acc[r][c] = fmaf(a[r].z, bb[c].z, acc[r][c]);
+        acc[r][c] = fmaf(a[r].w, bb[c].w, acc[r][c]);
+      }
   }
   float *out = scores + (size_t)bh * NQB * NB;
 #pragma unroll
