@@ -145,18 +145,24 @@ def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
     from oracle import sparse as OS
     torch.set_num_threads(cores)
 
-    N = lin_inputs[0]["q"].shape[2]
+    N = sp_inputs["q"].shape[2]
     H = lin_inputs[0]["q"].shape[1]
-    # linear: chunked form on one head over a sample of tokens (cost is linear in tokens)
-    n_lin = 8192
+    share = seconds / 3.0  # each of the three parts samples until it has used its share
+    # linear: chunked form, head after head over the sample's tokens (cost is linear in tokens)
     x = lin_inputs[0]
-    q = x["q"][0, 0, :n_lin].double().cpu().numpy()
-    k = x["k"][0, 0, :n_lin].double().cpu().numpy()
-    v = x["v"][0, 0, :n_lin].double().cpu().numpy()
-    lam = float(x["decay"][0])
-    t0 = time.perf_counter()
-    OL.linear_attention_chunked(q, k, v, lam, 128)
-    t_lin_tok_head = (time.perf_counter() - t0) / n_lin
+    n_lin = x["q"].shape[2]
+    lin_heads = 0
+    t_lin = 0.0
+    while lin_heads < H and (lin_heads == 0 or t_lin < share):
+        q = x["q"][0, lin_heads].double().cpu().numpy()
+        k = x["k"][0, lin_heads].double().cpu().numpy()
+        v = x["v"][0, lin_heads].double().cpu().numpy()
+        lam = float(x["decay"][lin_heads])
+        t0 = time.perf_counter()
+        OL.linear_attention_chunked(q, k, v, lam, 128)
+        t_lin += time.perf_counter() - t0
+        lin_heads += 1
+    t_lin_tok_head = t_lin / (n_lin * lin_heads)
 
     # sparse: rows of query blocks deep in the sequence (67 blocks each), one KV group
     sq, sk, sv = sp_inputs["q"], sp_inputs["k"], sp_inputs["v"]
@@ -165,15 +171,25 @@ def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
     kbar = OS.pool_blocks(sk[0, 0].double().cpu().numpy(), 64)
     nb = kbar.shape[0]
     ix = idx.cpu().numpy()
-    sample_blocks = list(range(nb - 1, max(66, nb - 1 - 8), -1))
-    t0 = time.perf_counter()
-    for i in sample_blocks:  # selection: pooled query, scores against all blocks, top-k
+    # selection: query blocks from the end of the context backwards (pooled
+    # query, scores against all blocks, top-k), until the share is used
+    sample_blocks = []
+    t_sel = 0.0
+    for i in range(nb - 1, 66, -1):
+        t0 = time.perf_counter()
         qb = sq[0, :G, i * 64:(i + 1) * 64].double().cpu().numpy().reshape(-1, d).mean(axis=0)
         s = (kbar @ qb) / math.sqrt(d)
         OS.select_row(s, i, N, 64, 64, 1, 2)
-    t_sel_row = (time.perf_counter() - t0) / len(sample_blocks)
-    rows = [(0, h, i * 64 + r) for i in sample_blocks[:2] for h in range(2) for r in (0, 31, 63)]
+        t_sel += time.perf_counter() - t0
+        sample_blocks.append(i)
+        if t_sel >= share:
+            break
+    t_sel_row = t_sel / len(sample_blocks)
+    # restricted softmax: rows of those blocks (67 selected blocks each), both
+    # KV groups, three rows per block and head, until the share is used
+    rows = [(0, h, i * 64 + r) for i in sample_blocks for h in (0, G) for r in (0, 31, 63)]
     t0 = time.perf_counter()
+    n_rows = 0
     for (b, h, t) in rows:
         i = t // 64
         blocks = [int(j) for j in ix[0, h // G, i] if j >= 0]
@@ -186,15 +202,18 @@ def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
         logit -= logit.max()
         p = np.exp(logit)
         (p / p.sum()) @ vv
-    t_att_row = (time.perf_counter() - t0) / len(rows)
+        n_rows += 1
+        if time.perf_counter() - t0 >= share:
+            break
+    t_att_row = (time.perf_counter() - t0) / n_rows
     nqb = (N + 63) // 64
     total = 3 * H * N * t_lin_tok_head + Hkv * nqb * t_sel_row + Hq * N * t_att_row
     return {"value": N / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"float64 oracle on the host: chunked linear form over {n_lin} tokens of one head "
-                       f"({t_lin_tok_head * 1e6:.2f} us/token/head); selection of {len(sample_blocks)} query blocks "
-                       f"at the end of the 256K context ({t_sel_row * 1e3:.1f} ms/row); restricted softmax for "
-                       f"{len(rows)} query rows of 67 blocks ({t_att_row * 1e3:.2f} ms/row); scaled to 3 linear "
-                       f"layers x 32 heads x N + 2 x 4096 selection rows + 32 x N attention rows")}
+            "sample": (f"float64 oracle on the host, about {seconds:.0f} s of it: chunked linear form over {n_lin} "
+                       f"tokens of {lin_heads} heads ({t_lin_tok_head * 1e6:.2f} us/token/head); selection of "
+                       f"{len(sample_blocks)} query blocks at the end of the 256K context ({t_sel_row * 1e3:.2f} ms/row); "
+                       f"restricted softmax for {n_rows} query rows of 67 blocks ({t_att_row * 1e3:.2f} ms/row); "
+                       f"scaled to 3 linear layers x 32 heads x N + 2 x 4096 selection rows + 32 x N attention rows")}
 
 
 def measure_ceilings(torch, sala):
