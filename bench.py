@@ -209,7 +209,7 @@ def cpu_baseline(lin_inputs, sp_inputs, idx, seconds):
     nqb = (N + 63) // 64
     total = 3 * H * N * t_lin_tok_head + Hkv * nqb * t_sel_row + Hq * N * t_att_row
     return {"value": N / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"float64 oracle on the host, about {seconds:.0f} s of it: chunked linear form over {n_lin} "
+            "sample": (f"float64 oracle on the host, up to {seconds:.0f} s of it: chunked linear form over {n_lin} "
                        f"tokens of {lin_heads} heads ({t_lin_tok_head * 1e6:.2f} us/token/head); selection of "
                        f"{len(sample_blocks)} query blocks at the end of the 256K context ({t_sel_row * 1e3:.2f} ms/row); "
                        f"restricted softmax for {n_rows} query rows of 67 blocks ({t_att_row * 1e3:.2f} ms/row); "
