@@ -686,8 +686,13 @@ hipError_t launch_sparse_select(const SparseSelectArgs &a, hipStream_t st) {
       hipLaunchKernelGGL(score_tiles, dim3(nTq * nTk, BH), dim3(256), 0, st, qbar, a.k_pooled, scores, NQB, NB,
                          NBs, qb0, nTk, a.d, inv_sqrt_d);
     }
-    hipLaunchKernelGGL((select_rows<256, 8192>), dim3(BH * NQB), dim3(256), 0, st, scores, a.idx, NQB, NB, a.L,
-                       a.block, a.topk, a.n_init, a.n_local, -1, qb0);
+    // candidate keys held in LDS: 16 KiB up to 4096 blocks (more workgroups per CU), else 32 KiB
+    if (NB <= 4096)
+      hipLaunchKernelGGL((select_rows<256, 4096>), dim3(BH * NQB), dim3(256), 0, st, scores, a.idx, NQB, NB, a.L,
+                         a.block, a.topk, a.n_init, a.n_local, -1, qb0);
+    else
+      hipLaunchKernelGGL((select_rows<256, 8192>), dim3(BH * NQB), dim3(256), 0, st, scores, a.idx, NQB, NB, a.L,
+                         a.block, a.topk, a.n_init, a.n_local, -1, qb0);
   } else if (a.topk <= 64 && (NB + 255) / 256 * 64 <= 4096) {
     // two exact levels: local top-64 per 256 blocks, then threshold + rank per row
     const int nchunk = (NB + 255) / 256;
