@@ -103,18 +103,31 @@ __global__ __launch_bounds__(512) void sparse_attn_bf16(const uint16_t *__restri
       nvalid_sh = i + 1;
       diag_sh = 1;
     }
-  } else if (tid == 0) {
+  } else if (tid < 64) {
+    // wave 0, 64 entries per round: one load per lane, then ballots keep the
+    // entries before the row's first negative one that lie below the query
+    // block, in their order (a serial scan would wait for each index in turn)
     const int32_t *row = idx + ((size_t)bkv * NQB + i_loc) * n_sel;
-    int n = 0, has_diag = 0;
-    for (int e = 0; e < n_sel; ++e) {
-      const int j = row[e];
-      if (j < 0) break;
-      if (j < i) sel[n++] = j;
-      else if (j == i) has_diag = 1;
+    const int lane = tid;
+    int n = 0;
+    bool has_diag = false;
+    for (int e0 = 0; e0 < n_sel; e0 += 64) {
+      const int e = e0 + lane;
+      const int j = (e < n_sel) ? row[e] : -1;
+      const uint64_t neg = __ballot(j < 0);
+      const bool alive = neg == 0 || lane < __builtin_ctzll(neg);  // before the first negative entry
+      const bool keep = alive && j < i;
+      const uint64_t kept = __ballot(keep);
+      if (keep) sel[n + __builtin_popcountll(kept & ((1ull << lane) - 1))] = j;
+      n += __builtin_popcountll(kept);
+      has_diag = has_diag || __ballot(alive && j == i) != 0;
+      if (neg != 0) break;
     }
-    if (has_diag) sel[n++] = i;
-    nvalid_sh = n;
-    diag_sh = has_diag;
+    if (lane == 0) {
+      if (has_diag) sel[n] = i;
+      nvalid_sh = n + (has_diag ? 1 : 0);
+      diag_sh = has_diag ? 1 : 0;
+    }
   }
 
   // Q fragments (B operand of K Q^T): lane holds Q[t = 64 i_loc + 16qt + lr][32s + 8lg .. +7],
