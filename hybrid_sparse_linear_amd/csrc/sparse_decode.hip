@@ -51,10 +51,17 @@ __global__ __launch_bounds__(256) void decode_partial(const T *__restrict__ q, c
   const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int32_t *row = idx + (size_t)bkv * n_sel;
-  if (tid == 0) {
-    int n = 0;
-    while (n < n_sel && row[n] >= 0) ++n;
-    nvalid_sh = n;
+  if (tid < 64) {  // wave 0: the index of the first negative entry, 64 entries per load
+    int n = n_sel;
+    for (int e0 = 0; e0 < n_sel; e0 += 64) {
+      const int e = e0 + tid;
+      const uint64_t neg = __ballot(e < n_sel && row[e] < 0);
+      if (neg != 0) {
+        n = e0 + __builtin_ctzll(neg);
+        break;
+      }
+    }
+    if (tid == 0) nvalid_sh = n;
   }
   for (int x = tid; x < G * D; x += 256) {
     const int g = x / D, c = x % D;
