@@ -144,6 +144,7 @@ SEL_CASES = [
     (1, 4, 1, 64 * 20 + 5, 64, I.BF16, 0, 1, 2, 0.0),     # k = 0: forced only
     (1, 4, 2, 64 * 25, 128, I.BF16, 5, 0, 0, 0.0),        # no forced blocks
     (1, 4, 2, 64 * 25 + 63, 128, I.F32, 3, 2, 3, 0.1),
+    (1, 16, 1, 64 * 22 + 33, 128, I.BF16, 6, 1, 2, 0.05),  # G = 16, the workloads' group size
 ]
 
 
@@ -246,6 +247,7 @@ ATT_CASES = [
     (1, 4, 1, 64 * 20 + 64, 64, I.BF16, 3, 1.0),
     (1, 4, 4, 2048, 64, I.F32, 4, 1.0 / 8.0),          # tiny-group sparse shape
     (1, 4, 2, 64 * 12 + 9, 128, I.F32, 2, 1.0),
+    (1, 16, 1, 64 * 14 + 33, 128, I.BF16, 5, 1.0),    # G = 16: four full head groups per query block
 ]
 
 
