@@ -104,6 +104,8 @@ int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk, const 
   REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
   if ((s = check_d(d))) return s;
   REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: libsala supports 64 and 128", chunk);
+  REQUIRE(dtype != SALA_BF16 || (long long)N * d * 2 < (1ll << 31), SALA_ERR_UNSUPPORTED,
+          "one head's rows must stay under 2 GiB");
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(k, "k");
   REQUIRE_PTR(v, "v");

@@ -80,6 +80,9 @@ typedef enum {
  *   state_out    [B, H, d, d] fp32 or NULL; may alias state_in.
  *   ws, ws_bytes workspace of at least sala_linear_prefill_workspace(...)
  *                bytes (may be NULL when that is 0).
+ * bf16: one head's rows N * d * 2 bytes must stay under 2 GiB (the kernels
+ * address a head's rows with 32-bit offsets); larger N returns
+ * SALA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk,
                         const void *q, const void *k, const void *v, void *o,

@@ -61,6 +61,8 @@ def test_linear_prefill_validation():
     assert lp(B=0) == INVALID
     assert lp(d=96) == UNSUPPORTED
     assert lp(chunk=32) == UNSUPPORTED
+    assert lp(N=1 << 23) == UNSUPPORTED  # bf16: one head's rows reach 2 GiB
+    assert lp(N=(1 << 23) - 1, ws=NUL, wsb=0) == WORKSPACE  # just under: accepted up to the workspace check
     assert lp(q=NUL) == INVALID
     assert lp(o=MIS) == INVALID
     assert lp(sin=MIS) == INVALID
