@@ -161,6 +161,15 @@ def test_workload4_sparse_layer_256K():
     sparse_full_check(262144, 4, n_rows=6, attn_rows_per_block=2)
 
 
+def test_sparse_layer_1M_candidates_beyond_lds():
+    """A 1M-token prefill: query blocks past 8194 have more candidate blocks
+    (up to 16381) than the 8192 keys the selection holds in LDS, and rank them
+    from the score rows in global memory; the sampled rows include the last
+    block and, at random, others on both sides of that line."""
+    say("sparse layer 1M")
+    sparse_full_check(1048576, 4, n_rows=6, attn_rows_per_block=1)
+
+
 def test_workload5_decode_1M():
     say("workload 5")
     lin, sp = I.workload5_decode("cuda")
