@@ -205,6 +205,30 @@ def test_sparse_select_decode(L, dt, d, pooled_only):
                           f"decode b{b} h{h}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,topk", [(2, 8, 2, 64 * 300 + 7, 128, 100), (1, 2, 1, 64 * 32800 + 5, 64, 64)],
+                         ids=["topk100", "NB32801"])
+def test_sparse_select_decode_general_path(B, Hq, Hkv, L, d, topk):
+    """Decode selection outside the two-level top-64 path: topk above 64, or
+    more than 16384 pooled blocks (a cache past 1M tokens), where every score
+    of the row is written and one workgroup ranks the row (past 16384
+    candidates from global memory).  Exact against the oracle."""
+    say("sparse_select decode, general path", B, Hq, Hkv, L, d, topk)
+    NB = (L + 63) // 64
+    kbar = I.normal((B, Hkv, NB, d), 133, 1.0, I.F32)
+    q = I.normal((B, Hq, 1, d), 134, 1.0, I.BF16)
+    idx, _ = sala.sparse_select(dev(q), None, k_pooled=dev(kbar), L=L, topk=topk)
+    torch.cuda.synchronize()
+    ridx, scores = OS.sparse_select_decode(host64(q[:, :, 0]), host64(kbar), L, 64, topk)
+    i = (L - 1) // 64
+    cands = OS.candidate_blocks(i, L, 64, 1, 2)
+    g = idx.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            nt = near_tie_rows([scores[b, h]], [cands], topk)[0]
+            check_idx_row(g[b, h, 0], ridx[b, h], scores[b, h], cands, sorted(OS.forced_blocks(i, 1, 2)), topk, nt,
+                          f"decode b{b} h{h}")
+
+
 def test_sparse_select_decode_many_chunks_reuses_workspace():
     """Decode selection over 1501 pooled blocks (several workgroups per row, a
     ragged last one), top-64: exact against the oracle, twice on one
