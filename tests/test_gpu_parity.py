@@ -360,7 +360,8 @@ def test_sparse_end_to_end_gpu_idx():
 # ---------------------------------------------------------------- sparse decode
 
 @pytest.mark.parametrize("L,dt,d,G", [(64 * 50 + 5, I.BF16, 128, 4), (64 * 70, I.F32, 128, 16),
-                                      (64 * 33 + 40, I.BF16, 64, 8), (100, I.BF16, 128, 2)])
+                                      (64 * 33 + 40, I.BF16, 64, 8), (100, I.BF16, 128, 2),
+                                      (64 * 40 + 9, I.BF16, 128, 32)])  # G > 16: the vector-ALU split kernel
 def test_sparse_decode(L, dt, d, G):
     say("sparse_decode", L, dt, d, G)
     B, Hkv, topk = 2, 2, 8
