@@ -44,6 +44,13 @@ TRAFFIC_MEASURED = {
     "fetch_kib": 8780152.375, "fetch_scale": 2.0,
     "write_kib": 2097208.03125, "write_scale": 1.0,
 }
+# Fraction of the cycles in which the MFMA pipes are busy while
+# sparse_attn_bf16 runs at 256K (SQ_VALU_MFMA_BUSY_CYCLES over the cycles its
+# workgroups are resident; profiles/sparse_attn_and_linear_256K_sq_counters.md).
+# That is its MFMA efficiency at the clock it actually runs at, so a clock
+# reading that would put the efficiency well above it was not taken while the
+# kernel ran.
+MFMA_BUSY_MEASURED = 0.569
 TRAFFIC_SOURCES = ("hybrid_sparse_linear_amd/csrc/sparse_prefill.hip", "hybrid_sparse_linear_amd/csrc/sala_common.hpp")
 
 
@@ -497,9 +504,14 @@ def main():
     flops = sparse_flops(idx, N, d, Hq // Hkv)
     group_flops = 3 * (32 * N * (2 * 128 * 128 + 4 * 128 * 128)) * 1.0 + flops  # algorithmic (causal) counts
     achieved = flops / (att_ms * 1e-3) / 1e12
-    if sclk and achieved > PEAK_BF16_TFLOPS * sclk / 2400.0:
-        # the rate needs a faster clock than the one read (the readings came
-        # from idle moments, as under a profiler that serialises launches)
+    sclk_note = None
+    if sclk and achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0) > MFMA_BUSY_MEASURED + 0.1:
+        # the rate needs a faster clock than the one read: the readings came
+        # from between launches (as under a profiler that serialises them) or
+        # the driver reported another clock
+        sclk_note = ("a reading of %d MHz would put the kernel at %.2f MFMA efficiency, above the %.3f MFMA-busy "
+                     "fraction the counters measure: not the kernel's clock" %
+                     (sclk, achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), MFMA_BUSY_MEASURED))
         sclk = None
     traffic = measured_traffic_bytes() if N == 262144 else None
     # unique bytes: Q read and O written once; K and V of the KV heads read once
@@ -547,6 +559,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(lin1, sp, idx, args.cpu_sample_seconds)
     if out["roofline"]["sclk_mhz"] is None and sclock.error:
         out["roofline"]["sclk_error"] = sclock.error
+    if sclk_note:
+        out["roofline"]["sclk_note"] = sclk_note
     print(json.dumps(out), flush=True)
 
 
