@@ -445,4 +445,38 @@ int sala_sparse_prefill_chunk(int dtype, int B, int Hq, int Hkv, int capacity, i
   return hip_status(sala::launch_sparse_prefill(pa, st), "sala_sparse_prefill_chunk attend");
 }
 
+size_t sala_workspace_bytes(int op, const int64_t *dims, int ndims) {
+  static const int nargs[] = {6, 11, 8, 8, 11, 10};
+  const size_t bad = (size_t)-1;
+  if (op < SALA_OP_LINEAR_PREFILL || op > SALA_OP_SPARSE_DECODE_STEP) {
+    fail(SALA_ERR_INVALID_ARG, "unknown operation %d", op);
+    return bad;
+  }
+  if (!dims || ndims != nargs[op]) {
+    fail(SALA_ERR_INVALID_ARG, "operation %d takes %d dimensions, got %d%s", op, nargs[op], ndims,
+         dims ? "" : " (dims is NULL)");
+    return bad;
+  }
+  int a[11];
+  for (int i = 0; i < ndims; ++i) {
+    if (dims[i] < -2147483648ll || dims[i] > 2147483647ll) {
+      fail(SALA_ERR_INVALID_ARG, "dimension %d (%lld) does not fit an int", i, (long long)dims[i]);
+      return bad;
+    }
+    a[i] = (int)dims[i];
+  }
+  g_err[0] = '\0';
+  switch (op) {
+    case SALA_OP_LINEAR_PREFILL: return sala_linear_prefill_workspace(a[0], a[1], a[2], a[3], a[4], a[5]);
+    case SALA_OP_SPARSE_SELECT:
+      return sala_sparse_select_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], a[10]);
+    case SALA_OP_SPARSE_PREFILL: return sala_sparse_prefill_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]);
+    case SALA_OP_SPARSE_DECODE: return sala_sparse_decode_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]);
+    case SALA_OP_SPARSE_PREFILL_CHUNK:
+      return sala_sparse_prefill_chunk_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], a[10]);
+    default:
+      return sala_sparse_decode_step_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9]);
+  }
+}
+
 }  // extern "C"

@@ -463,11 +463,11 @@ __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ 
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the key loads ahead of the query loads
   constexpr int P = 256 / d;   // the G heads are split over P thread groups per dimension
-  constexpr int QPT = 32 / P;  // at most 32 heads per group
+  constexpr int QPT = 32 / P;  // heads per thread loaded up front (all of them for G <= 32)
   const int qc = tid % d, qp = tid / d;
   float qv[QPT];
+  const T *qb = q + (size_t)(b * Hq + h * G) * d + qc;
   {
-    const T *qb = q + (size_t)(b * Hq + h * G) * d + qc;
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
       const int g = min(qp + P * i, G - 1);
@@ -479,6 +479,11 @@ __global__ __launch_bounds__(256) void score_decode_top64(const T *__restrict__ 
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < QPT; ++i) s += (qp + P * i < G) ? qv[i] : 0.f;
+    // heads past the first 32 of a larger group, in the same order (i = QPT, ...)
+    for (int g = qp + P * QPT; g < G; g += P) {
+      if constexpr (sizeof(T) == 2) s += bf16_to_f32(qb[(size_t)g * d]);
+      else s += qb[(size_t)g * d];
+    }
     qpart[tid] = s;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);

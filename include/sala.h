@@ -325,6 +325,33 @@ size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, in
 int sala_ceiling_mfma(int workgroups, int iters, float *out, void *stream);
 int sala_ceiling_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * sala_workspace_bytes -- the workspace query of every entry point behind
+ * one call: `op` names the operation and dims[0 .. ndims-1] are the integer
+ * arguments of that operation's *_workspace query, in the order listed.
+ *
+ *   SALA_OP_LINEAR_PREFILL       dtype, B, H, N, d, chunk
+ *   SALA_OP_SPARSE_SELECT        dtype, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local
+ *   SALA_OP_SPARSE_PREFILL       dtype, B, Hq, Hkv, N, d, block, n_sel
+ *   SALA_OP_SPARSE_DECODE        dtype, B, Hq, Hkv, L, d, block, n_sel
+ *   SALA_OP_SPARSE_PREFILL_CHUNK dtype, B, Hq, Hkv, capacity, d, n, block, topk, n_init, n_local
+ *   SALA_OP_SPARSE_DECODE_STEP   dtype, B, Hq, Hkv, capacity, d, block, topk, n_init, n_local
+ *
+ * Returns the number of bytes (0: the call needs no workspace), or
+ * (size_t)-1 when op is unknown, ndims does not match op, dims is NULL or a
+ * dimension does not fit an int; sala_last_error() then says which.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  SALA_OP_LINEAR_PREFILL = 0,
+  SALA_OP_SPARSE_SELECT = 1,
+  SALA_OP_SPARSE_PREFILL = 2,
+  SALA_OP_SPARSE_DECODE = 3,
+  SALA_OP_SPARSE_PREFILL_CHUNK = 4,
+  SALA_OP_SPARSE_DECODE_STEP = 5
+} sala_op;
+
+size_t sala_workspace_bytes(int op, const int64_t *dims, int ndims);
+
 /* ------------------------------------------------------------------------ */
 const char *sala_status_string(int status);  /* static string, never NULL      */
 const char *sala_last_error(void);           /* thread-local detail, never NULL */
