@@ -23,8 +23,14 @@ Readings where the pages are silent (listed in the design notes):
   * The output gate is elementwise: o * sigmoid(g), g being a gate
     pre-activation of the same shape as o, computed upstream from the
     layer input.
+  * Where the transformed vectors are stored: with store="bf16" the
+    normalised and rotated q and k are rounded once to bf16 (round to
+    nearest even) before the attention, as an unfused producer writing
+    them to memory at the inputs' precision would leave them; v and the
+    attention itself stay in float64.  store=None keeps them exact.
 
 Functions:
+  round_bf16                           -- float64 -> nearest bf16 value (ties to even)
   rms_norm, rope, output_gate          -- the three neighbours
   linear_layer_fused                   -- norm + RoPE -> linear attention -> gate
   linear_decode_fused                  -- the same for one token per (b, h)
@@ -73,28 +79,47 @@ def output_gate(o, g):
     return _f64(o) / (1.0 + np.exp(-g))
 
 
-def _prologue(x, gamma, eps, base, positions):
+def round_bf16(x):
+    """The bf16 value nearest to each element (ties to the even significand).
+
+    bf16 keeps the upper 16 bits of an IEEE fp32 pattern: the value is first
+    taken to fp32 (nearest), then the low 16 bits are rounded off by adding
+    0x7FFF plus the lowest kept bit and truncating.
+    """
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _prologue(x, gamma, eps, base, positions, store=None):
+    transformed = False
     if gamma is not None:
         x = rms_norm(x, gamma, eps)
+        transformed = True
     if base is not None and base > 0:
         x = rope(x, positions, base)
+        transformed = True
+    if transformed and store == "bf16":
+        x = round_bf16(x)
     return _f64(x)
 
 
 def linear_layer_fused(q, k, v, decay=None, state_in=None, gamma_q=None, gamma_k=None, eps=1e-6,
-                       rope_base=10000.0, pos0=0, gate=None):
+                       rope_base=10000.0, pos0=0, gate=None, store=None):
     """One linear layer with its neighbours, batched [B, H, N, d].
 
     q_hat = RoPE(rms_norm(q)), k_hat = RoPE(rms_norm(k)) at positions
     pos0 .. pos0 + N - 1; (o, S) = decayed linear attention of (q_hat, k_hat, v);
     o <- o * sigmoid(gate).  A None gamma skips that normalisation, a None or
-    non-positive rope_base skips RoPE, a None gate skips the gate.
+    non-positive rope_base skips RoPE, a None gate skips the gate; store="bf16"
+    rounds the transformed q and k to bf16 (see the module docstring).
     Returns (o [B, H, N, d_v], state_out [B, H, d_k, d_v]).
     """
     n = np.shape(q)[2]
     pos = np.arange(n, dtype=np.float64) + float(pos0)
-    qh = _prologue(q, gamma_q, eps, rope_base, pos)
-    kh = _prologue(k, gamma_k, eps, rope_base, pos)
+    qh = _prologue(q, gamma_q, eps, rope_base, pos, store)
+    kh = _prologue(k, gamma_k, eps, rope_base, pos, store)
     o, st = _lin.linear_prefill(qh, kh, v, decay, state_in)
     if gate is not None:
         o = output_gate(o, gate)
@@ -102,15 +127,15 @@ def linear_layer_fused(q, k, v, decay=None, state_in=None, gamma_q=None, gamma_k
 
 
 def linear_layer_fused_rows(q, k, v, lam, rows, state_in=None, gamma_q=None, gamma_k=None, eps=1e-6,
-                            rope_base=10000.0, pos0=0, gate=None):
+                            rope_base=10000.0, pos0=0, gate=None, store=None):
     """linear_layer_fused for one head [N, d] at chosen query rows (long sequences)."""
     n = np.shape(q)[0]
     last = int(max(rows)) + 1
     pos = np.arange(last, dtype=np.float64) + float(pos0)
-    kh = _prologue(k[:last], gamma_k, eps, rope_base, pos)
+    kh = _prologue(k[:last], gamma_k, eps, rope_base, pos, store)
     qh = np.zeros((last, np.shape(q)[1]))
     rows_i = [int(r) for r in rows]
-    qh[rows_i] = _prologue(_f64(q)[rows_i], gamma_q, eps, rope_base, pos[rows_i])
+    qh[rows_i] = _prologue(_f64(q)[rows_i], gamma_q, eps, rope_base, pos[rows_i], store)
     o = _lin.linear_attention_rows(qh, kh, _f64(v)[:last], lam, rows_i, state_in)
     if gate is not None:
         o = output_gate(o, _f64(gate)[rows_i])
@@ -119,7 +144,7 @@ def linear_layer_fused_rows(q, k, v, lam, rows, state_in=None, gamma_q=None, gam
 
 
 def linear_decode_fused(q, k, v, state, decay=None, gamma_q=None, gamma_k=None, eps=1e-6,
-                        rope_base=10000.0, pos=None, gate=None):
+                        rope_base=10000.0, pos=None, gate=None, store=None):
     """One decode token per (b, h): q, k, v [B, H, d], state [B, H, d_k, d_v],
     pos [B] absolute positions.  Returns (o [B, H, d_v], state')."""
     b_, h_, _ = np.shape(q)
@@ -127,8 +152,8 @@ def linear_decode_fused(q, k, v, state, decay=None, gamma_q=None, gamma_k=None, 
     kh = np.zeros(np.shape(k))
     for b in range(b_):
         p = np.array([float(pos[b])])
-        qh[b] = _prologue(_f64(q)[b][:, None, :], gamma_q, eps, rope_base, p)[:, 0, :]
-        kh[b] = _prologue(_f64(k)[b][:, None, :], gamma_k, eps, rope_base, p)[:, 0, :]
+        qh[b] = _prologue(_f64(q)[b][:, None, :], gamma_q, eps, rope_base, p, store)[:, 0, :]
+        kh[b] = _prologue(_f64(k)[b][:, None, :], gamma_k, eps, rope_base, p, store)[:, 0, :]
     o, st = _lin.linear_decode_batched(qh, kh, v, state, decay)
     if gate is not None:
         o = output_gate(o, gate)

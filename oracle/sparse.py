@@ -113,6 +113,32 @@ def sparse_select_prefill(q, k, block=64, topk=64, n_init=1, n_local=2):
     return idx, scores, kbar
 
 
+def sparse_select_prefill_rows(q, k, blocks, block=64, topk=64, n_init=1, n_local=2):
+    """The prefill selection of ``sparse_select_prefill`` for chosen query blocks only.
+
+    q [B, Hq, N, d] and k [B, Hkv, N, d] may be any arrays indexable like NumPy
+    arrays (only the rows read are converted); blocks: query block indices.
+    Returns (idx [B, Hkv, len(blocks), W], scores [B, Hkv, len(blocks), NB],
+    kbar [B, Hkv, NB, d]) with the same definitions.
+    """
+    b_, hq, n, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    nb = n_blocks(n, block)
+    width = topk + n_init + n_local
+    idx = np.full((b_, hkv, len(blocks), width), -1, dtype=np.int64)
+    scores = np.zeros((b_, hkv, len(blocks), nb))
+    kbar = np.zeros((b_, hkv, nb, d))
+    for b in range(b_):
+        for h in range(hkv):
+            kbar[b, h] = pool_blocks(k[b, h], block)
+            for r, i in enumerate(blocks):
+                qbar = _f64(q[b, h * g:(h + 1) * g, i * block:(i + 1) * block]).reshape(-1, d).mean(axis=0)
+                scores[b, h, r] = (kbar[b, h] @ qbar) / math.sqrt(d)
+                idx[b, h, r] = select_row(scores[b, h, r], i, n, block, topk, n_init, n_local)
+    return idx, scores, kbar
+
+
 def sparse_attention_prefill(q, k, v, idx, block=64, scale=None):
     """Softmax attention over the selected token sets.
 

@@ -13,6 +13,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import linear as L
 from oracle import neighbours as NB
@@ -155,3 +156,47 @@ def test_fused_layer_split_rows_and_decode():
                                     gate=g[:, :, 49], **kw)
     np.testing.assert_allclose(od, o[:, :, 49], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(sd, st, rtol=1e-11, atol=1e-12)
+
+
+def test_round_bf16_hand_values_and_library_cast():
+    """Ties go to the even significand (bf16 spacing at 1 is 2^-7); values off
+    the tie go to the nearer neighbour; the result equals torch's fp32 -> bf16
+    cast (a library routine) on random fp32 values across many binades."""
+    cases = [(1 + 2 ** -8, 1.0), (1 + 3 * 2 ** -8, 1 + 2 ** -6), (1 + 2 ** -8 + 2 ** -20, 1 + 2 ** -7),
+             (-1.5, -1.5), (0.0, 0.0), (2 ** 40 * (1 + 3 * 2 ** -8), 2 ** 40 * (1 + 2 ** -6)),
+             (-(2 ** -30) * (1 + 2 ** -8), -(2 ** -30))]
+    for x, want in cases:
+        assert NB.round_bf16(np.array([x]))[0] == want, x
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-40, 40, 20000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(NB.round_bf16(x.astype(np.float64)), want)
+
+
+def test_fused_layer_bf16_store_is_the_plain_layer_on_rounded_inputs():
+    """store="bf16": the attention runs on the transformed q, k rounded to bf16,
+    and nothing is rounded when no transform is enabled."""
+    rng = np.random.default_rng(13)
+    B, H, n, d = 1, 2, 40, 8
+    q, k, v = (rng.standard_normal((B, H, n, d)) for _ in range(3))
+    gq, gk = 1 + 0.1 * rng.standard_normal(d), 1 + 0.1 * rng.standard_normal(d)
+    decay = [0.9, 1.0]
+    o, st = NB.linear_layer_fused(q, k, v, decay, None, gq, gk, 1e-6, 100.0, 5, None, store="bf16")
+    pos = np.arange(n) + 5.0
+    qh = NB.round_bf16(NB.rope(NB.rms_norm(q, gq), pos, 100.0))
+    kh = NB.round_bf16(NB.rope(NB.rms_norm(k, gk), pos, 100.0))
+    ro, rs = L.linear_prefill(qh, kh, v, decay)
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st, rs, rtol=1e-12, atol=1e-12)
+    o2, _ = NB.linear_layer_fused(q, k, v, decay, store="bf16", rope_base=None)
+    np.testing.assert_array_equal(o2, L.linear_prefill(q, k, v, decay)[0])
+    # decode and sampled rows take the same rounding
+    od, _ = NB.linear_decode_fused(q[:, :, 7], k[:, :, 7], v[:, :, 7], np.zeros((B, H, d, d)), decay, gq, gk, 1e-6,
+                                  100.0, [12], None, store="bf16")
+    qd = NB.round_bf16(NB.rope(NB.rms_norm(q[:, :, 7:8], gq), np.array([12.0]), 100.0))[:, :, 0]
+    kd = NB.round_bf16(NB.rope(NB.rms_norm(k[:, :, 7:8], gk), np.array([12.0]), 100.0))[:, :, 0]
+    np.testing.assert_allclose(od, L.linear_decode_batched(qd, kd, v[:, :, 7], np.zeros((B, H, d, d)), decay)[0],
+                               rtol=1e-12, atol=1e-12)
+    rows = NB.linear_layer_fused_rows(q[0, 1], k[0, 1], v[0, 1], 1.0, [0, 17, 39], None, gq, gk, 1e-6, 100.0, 5,
+                                     store="bf16")
+    np.testing.assert_allclose(rows, o[0, 1, [0, 17, 39]], rtol=1e-12, atol=1e-12)

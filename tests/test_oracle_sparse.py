@@ -230,3 +230,19 @@ def test_rows_form_equals_full_form():
     r = S.sparse_attention_prefill_rows(q, k, v, idx, rows, block=blk)
     for i, (bb, hh, t) in enumerate(rows):
         np.testing.assert_allclose(r[i], o[bb, hh, t], rtol=1e-13, atol=1e-13)
+
+
+def test_selection_rows_form_equals_full_form():
+    """sparse_select_prefill_rows on chosen query blocks equals those rows of the
+    full selection (indices, scores, pooled keys), including a ragged last block,
+    several KV heads and planted ties."""
+    rng = np.random.default_rng(11)
+    b, hq, hkv, n, d, blk = 2, 6, 2, 16 * 13 + 5, 8, 16
+    q = rng.integers(-2, 3, (b, hq, n, d)).astype(np.float64)
+    k = rng.integers(-2, 3, (b, hkv, n, d)).astype(np.float64)
+    idx, sc, kbar = S.sparse_select_prefill(q, k, block=blk, topk=3, n_init=1, n_local=2)
+    blocks = [0, 1, 4, 7, 13]
+    ri, rs, rk = S.sparse_select_prefill_rows(q, k, blocks, block=blk, topk=3, n_init=1, n_local=2)
+    assert np.array_equal(ri, idx[:, :, blocks])
+    np.testing.assert_allclose(rs, sc[:, :, blocks], rtol=1e-13, atol=1e-13)  # BLAS summation order
+    np.testing.assert_array_equal(rk, kbar)
