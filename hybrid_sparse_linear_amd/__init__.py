@@ -1,8 +1,11 @@
 """libsala Python binding: the SALA hybrid attention layer group on MI355X.
 
-Thin wrappers over the C ABI in ``include/sala.h``.  They check tensor
-shapes, dtypes and devices, allocate outputs and workspaces with torch when
-the caller does not pass them, and call the HIP library on torch's current
+Thin wrappers over the C ABI in ``include/sala.h``.  Each wrapper checks the
+shape and dtype of every tensor it is given against the sizes taken from its
+first argument (the C ABI sees only pointers, so a mismatched buffer would
+otherwise become an out-of-bounds device access), then that every tensor is a
+contiguous GPU tensor, allocates outputs and workspaces with torch when the
+caller does not pass them, and calls the HIP library on torch's current
 stream.  Every step of the computation runs in the HIP kernels; there is no
 CPU or PyTorch fallback -- a missing ``libsala.so`` raises.
 
@@ -15,10 +18,16 @@ Entry points (same names as the C ABI, without the ``sala_`` prefix):
   dense_prefill    plain causal attention (the full-attention comparison)
   ceiling_mfma / ceiling_copy   microkernels measuring this GPU's ceilings
   layer_group_prefill  three linear layers then one sparse layer, one stream
+
+Debugging: with the environment variable SALA_DEBUG_POISON=1, every output,
+index array and workspace the wrappers allocate is filled first (NaN for
+float tensors, -123456789 for int32, 0xFF bytes for workspaces), so an
+element a kernel fails to write shows up in a comparison.
 """
 
 import ctypes
 import math
+import os
 
 import torch
 
@@ -28,6 +37,8 @@ __all__ = ["linear_prefill", "linear_decode", "linear_prefill_fused", "linear_de
            "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_select",
            "sparse_prefill", "sparse_decode",
            "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
+
+POISON_INT32 = -123456789
 
 
 def _code(t):
@@ -46,6 +57,29 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _poisoning():
+    return os.environ.get("SALA_DEBUG_POISON", "") == "1"
+
+
+def _poison(t):
+    if t.dtype.is_floating_point:
+        t.fill_(float("nan"))
+    elif t.dtype == torch.int32:
+        t.fill_(POISON_INT32)
+    else:
+        t.fill_(0xFF)
+    return t
+
+
+def _empty(shape, dtype, device):
+    t = torch.empty(tuple(shape), dtype=dtype, device=device)
+    return _poison(t) if _poisoning() else t
+
+
+def _empty_like(x):
+    return _empty(x.shape, x.dtype, x.device)
+
+
 def _dev(*ts):
     for t in ts:
         if t is None:
@@ -56,6 +90,26 @@ def _dev(*ts):
             raise ValueError("libsala tensors must be contiguous")
 
 
+def _want(t, name, shape, dtype):
+    """t is None, or has exactly `shape` and `dtype`."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _dims(t, name, ndim):
+    if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+        raise ValueError(f"{name} must be a {ndim}-d tensor")
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    return tuple(t.shape)
+
+
 def _ws(nbytes, ws, like):
     if nbytes == 0:
         return None
@@ -63,31 +117,47 @@ def _ws(nbytes, ws, like):
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    return _empty((nbytes,), torch.uint8, like.device)
+
+
+# operation codes of sala_workspace_bytes and the integer arguments it takes for each, in order
+_WS_OPS = {
+    "linear_prefill": (0, ("dtype", "B", "H", "N", "d", "chunk")),
+    "sparse_select": (1, ("dtype", "B", "Hq", "Hkv", "d", "Nq", "L", "block", "topk", "n_init", "n_local")),
+    "sparse_prefill": (2, ("dtype", "B", "Hq", "Hkv", "N", "d", "block", "n_sel")),
+    "sparse_decode": (3, ("dtype", "B", "Hq", "Hkv", "L", "d", "block", "n_sel")),
+    "sparse_prefill_chunk": (4, ("dtype", "B", "Hq", "Hkv", "capacity", "d", "n", "block", "topk", "n_init",
+                                 "n_local")),
+    "sparse_decode_step": (5, ("dtype", "B", "Hq", "Hkv", "capacity", "d", "block", "topk", "n_init", "n_local")),
+}
 
 
 def workspace_bytes(op, **kw):
-    """Workspace size in bytes of an entry point for the given arguments."""
-    L = lib()
-    if op == "linear_prefill":
-        return L.sala_linear_prefill_workspace(kw["dtype"], kw["B"], kw["H"], kw["N"], kw["d"], kw["chunk"])
-    if op == "sparse_select":
-        return L.sala_sparse_select_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["d"], kw["Nq"], kw["L"],
-                                              kw["block"], kw["topk"], kw["n_init"], kw["n_local"])
-    if op == "sparse_prefill":
-        return L.sala_sparse_prefill_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["N"], kw["d"],
-                                               kw["block"], kw["n_sel"])
-    if op == "sparse_decode":
-        return L.sala_sparse_decode_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["L"], kw["d"],
-                                              kw["block"], kw["n_sel"])
-    if op == "sparse_prefill_chunk":
-        return L.sala_sparse_prefill_chunk_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["capacity"],
-                                                     kw["d"], kw["n"], kw["block"], kw["topk"], kw["n_init"],
-                                                     kw["n_local"])
-    if op == "sparse_decode_step":
-        return L.sala_sparse_decode_step_workspace(kw["dtype"], kw["B"], kw["Hq"], kw["Hkv"], kw["capacity"],
-                                                   kw["d"], kw["block"], kw["topk"], kw["n_init"], kw["n_local"])
-    raise ValueError(op)
+    """Workspace size in bytes of an entry point for the given arguments (sala_workspace_bytes)."""
+    if op not in _WS_OPS:
+        raise ValueError(f"unknown operation {op!r}")
+    code, names = _WS_OPS[op]
+    dims = (ctypes.c_int64 * len(names))(*[int(kw[n]) for n in names])
+    nb = lib().sala_workspace_bytes(code, dims, len(names))
+    if nb == ctypes.c_size_t(-1).value:
+        raise SalaError("sala_workspace_bytes", -1, lib().sala_last_error().decode())
+    return nb
+
+
+def _check_linear(q, k, v, decay, state, out, state_out):
+    B, H, N, d = _dims(q, "q", 4)
+    _want(k, "k", q.shape, q.dtype)
+    _want(v, "v", q.shape, q.dtype)
+    _want(out, "out", q.shape, q.dtype)
+    _want(decay, "decay", (H,), torch.float32)
+    _want(state, "state", (B, H, d, d), torch.float32)
+    _want(state_out, "state_out", (B, H, d, d), torch.float32)
+    return B, H, N, d
+
+
+def _check_gammas(d, gamma_q, gamma_k):
+    _want(gamma_q, "gamma_q", (d,), torch.float32)
+    _want(gamma_k, "gamma_k", (d,), torch.float32)
 
 
 def linear_prefill(q, k, v, decay=None, state=None, *, chunk=None, out=None, state_out=None, workspace=None,
@@ -96,17 +166,15 @@ def linear_prefill(q, k, v, decay=None, state=None, *, chunk=None, out=None, sta
 
     state: optional [B, H, d, d] fp32 carried state S[d_k][d_v].  Returns (o, S_out or None).
     """
-    _dev(q, k, v, decay, state, out, state_out)
-    B, H, N, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
+    B, H, N, d = _check_linear(q, k, v, decay, state, out, state_out)
+    _dev(q, k, v, decay, state, out, state_out, workspace)
     chunk = chunk or (64 if d == 64 else 128)
     dt = _code(q)
-    o = torch.empty_like(q) if out is None else out
+    o = _empty_like(q) if out is None else out
     so = state_out
     if so is None and want_state:
-        so = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    nb = lib().sala_linear_prefill_workspace(dt, B, H, N, d, chunk)
+        so = _empty((B, H, d, d), torch.float32, q.device)
+    nb = workspace_bytes("linear_prefill", dtype=dt, B=B, H=H, N=N, d=d, chunk=chunk)
     ws = _ws(nb, workspace, q)
     call("sala_linear_prefill", dt, B, H, N, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay), _ptr(state),
          _ptr(so), _ptr(ws), nb, _stream())
@@ -115,9 +183,16 @@ def linear_prefill(q, k, v, decay=None, state=None, *, chunk=None, out=None, sta
 
 def linear_decode(q, k, v, state, decay=None, *, out=None):
     """One decode token: state [B, H, d, d] fp32 is updated in place; returns o [B, H, d]."""
+    B, H, d = _dims(q, "q", 3)
+    _want(k, "k", q.shape, q.dtype)
+    _want(v, "v", q.shape, q.dtype)
+    _want(out, "out", q.shape, q.dtype)
+    if state is None:
+        raise ValueError("state must be given (it is updated in place)")
+    _want(state, "state", (B, H, d, d), torch.float32)
+    _want(decay, "decay", (H,), torch.float32)
     _dev(q, k, v, state, decay, out)
-    B, H, d = q.shape
-    o = torch.empty_like(q) if out is None else out
+    o = _empty_like(q) if out is None else out
     call("sala_linear_decode", _code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay), _ptr(state),
          _stream())
     return o
@@ -132,22 +207,17 @@ def linear_prefill_fused(q, k, v, decay=None, state=None, *, gamma_q=None, gamma
     gamma_q, gamma_k: [d] fp32 or None; rope_base 0 / None = no RoPE; gate: like q or None.
     Returns (o, S_out or None) as linear_prefill.
     """
-    _dev(q, k, v, decay, state, out, state_out, gamma_q, gamma_k, gate)
-    B, H, N, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
-    if gate is not None and (gate.shape != q.shape or gate.dtype != q.dtype):
-        raise ValueError("gate must match q in shape and dtype")
-    for gname, gt in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
-        if gt is not None and (gt.shape != (d,) or gt.dtype != torch.float32):
-            raise ValueError(f"{gname} must be a float32 [{d}] tensor")
+    B, H, N, d = _check_linear(q, k, v, decay, state, out, state_out)
+    _want(gate, "gate", q.shape, q.dtype)
+    _check_gammas(d, gamma_q, gamma_k)
+    _dev(q, k, v, decay, state, out, state_out, gamma_q, gamma_k, gate, workspace)
     chunk = chunk or (64 if d == 64 else 128)
     dt = _code(q)
-    o = torch.empty_like(q) if out is None else out
+    o = _empty_like(q) if out is None else out
     so = state_out
     if so is None and want_state:
-        so = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    nb = lib().sala_linear_prefill_workspace(dt, B, H, N, d, chunk)
+        so = _empty((B, H, d, d), torch.float32, q.device)
+    nb = workspace_bytes("linear_prefill", dtype=dt, B=B, H=H, N=N, d=d, chunk=chunk)
     ws = _ws(nb, workspace, q)
     call("sala_linear_prefill_fused", dt, B, H, N, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay),
          _ptr(state), _ptr(so), _ptr(gamma_q), _ptr(gamma_k), float(eps), float(rope_base or 0.0), int(pos0),
@@ -159,11 +229,19 @@ def linear_decode_fused(q, k, v, state, decay=None, *, gamma_q=None, gamma_k=Non
                         pos=None, gate=None, out=None):
     """One decode token with the neighbours fused (see linear_prefill_fused); pos: int64 [B]
     device tensor of positions (needed with RoPE).  state is updated in place; returns o."""
+    B, H, d = _dims(q, "q", 3)
+    _want(k, "k", q.shape, q.dtype)
+    _want(v, "v", q.shape, q.dtype)
+    _want(out, "out", q.shape, q.dtype)
+    _want(gate, "gate", q.shape, q.dtype)
+    if state is None:
+        raise ValueError("state must be given (it is updated in place)")
+    _want(state, "state", (B, H, d, d), torch.float32)
+    _want(decay, "decay", (H,), torch.float32)
+    _want(pos, "pos", (B,), torch.int64)
+    _check_gammas(d, gamma_q, gamma_k)
     _dev(q, k, v, state, decay, out, gamma_q, gamma_k, pos, gate)
-    B, H, d = q.shape
-    if pos is not None and (pos.dtype != torch.int64 or pos.shape != (B,)):
-        raise ValueError("pos must be an int64 [B] tensor")
-    o = torch.empty_like(q) if out is None else out
+    o = _empty_like(q) if out is None else out
     call("sala_linear_decode_fused", _code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay),
          _ptr(state), _ptr(gamma_q), _ptr(gamma_k), float(eps), float(rope_base or 0.0), _ptr(pos), _ptr(gate),
          _stream())
@@ -173,11 +251,11 @@ def linear_decode_fused(q, k, v, state, decay=None, *, gamma_q=None, gamma_k=Non
 def qk_norm_rope(x, *, gamma=None, eps=1e-6, rope_base=0.0, pos0=0, out=None):
     """Standalone RMS norm (weight gamma [d] fp32 or None) then rotate-half RoPE at
     positions pos0 .. (rope_base 0 = none) of x [B, H, N, d]; out may be x."""
+    B, H, N, d = _dims(x, "x", 4)
+    _want(gamma, "gamma", (d,), torch.float32)
+    _want(out, "out", x.shape, x.dtype)
     _dev(x, gamma, out)
-    B, H, N, d = x.shape
-    if gamma is not None and (gamma.shape != (d,) or gamma.dtype != torch.float32):
-        raise ValueError(f"gamma must be a float32 [{d}] tensor")
-    o = torch.empty_like(x) if out is None else out
+    o = _empty_like(x) if out is None else out
     call("sala_qk_norm_rope", _code(x), B, H, N, d, _ptr(x), _ptr(o), _ptr(gamma), float(eps),
          float(rope_base or 0.0), int(pos0), _stream())
     return o
@@ -185,10 +263,12 @@ def qk_norm_rope(x, *, gamma=None, eps=1e-6, rope_base=0.0, pos0=0, out=None):
 
 def output_gate(o, gate, *, out=None):
     """o * sigmoid(gate), elementwise (numel a multiple of 8); out may be o."""
+    if not isinstance(o, torch.Tensor):
+        raise ValueError("o must be a torch tensor")
+    _want(gate, "gate", o.shape, o.dtype)
+    _want(out, "out", o.shape, o.dtype)
     _dev(o, gate, out)
-    if gate.shape != o.shape or gate.dtype != o.dtype:
-        raise ValueError("gate must match o in shape and dtype")
-    r = torch.empty_like(o) if out is None else out
+    r = _empty_like(o) if out is None else out
     call("sala_output_gate", _code(o), o.numel(), _ptr(o), _ptr(gate), _ptr(r), _stream())
     return r
 
@@ -200,42 +280,67 @@ def sparse_select(q, k=None, *, k_pooled=None, L=None, block=64, topk=64, n_init
     k [B, Hkv, L, d] (pooled into k_pooled), or k=None with k_pooled [B, Hkv, ceil(L/block), d] fp32 given.
     Returns (idx [B, Hkv, NQB, topk+n_init+n_local] int32, k_pooled[, scores]).
     """
-    _dev(q, k, k_pooled, idx_out)
-    B, Hq, Nq, d = q.shape
+    B, Hq, Nq, d = _dims(q, "q", 4)
     if k is not None:
-        Hkv, L = k.shape[1], k.shape[2]
+        Bk, Hkv, L_k, dk = _dims(k, "k", 4)
+        if L is not None and L != L_k:
+            raise ValueError(f"L = {L} disagrees with k's {L_k} tokens")
+        L = L_k
+        _want(k, "k", (B, Hkv, L, d), q.dtype)
     else:
         if k_pooled is None or L is None:
             raise ValueError("without k, pass k_pooled and L")
+        if k_pooled.dim() != 4:
+            raise ValueError("k_pooled must be a 4-d tensor")
         Hkv = k_pooled.shape[1]
+    if Nq != L and Nq != 1:
+        raise ValueError(f"q must hold all L = {L} queries (prefill) or one (decode), got {Nq}")
     NB = (L + block - 1) // block
     NQB = 1 if (Nq == 1 and L != 1) else NB
     W = topk + n_init + n_local
+    _want(k_pooled, "k_pooled", (B, Hkv, NB, d), torch.float32)
+    _want(idx_out, "idx_out", (B, Hkv, NQB, W), torch.int32)
+    _dev(q, k, k_pooled, idx_out, workspace)
     dt = _code(q)
     if k_pooled is None:
-        k_pooled = torch.empty((B, Hkv, NB, d), dtype=torch.float32, device=q.device)
-    idx = torch.empty((B, Hkv, NQB, W), dtype=torch.int32, device=q.device) if idx_out is None else idx_out
-    scores = torch.empty((B, Hkv, NQB, NB), dtype=torch.float32, device=q.device) if return_scores else None
+        k_pooled = _empty((B, Hkv, NB, d), torch.float32, q.device)
+    idx = _empty((B, Hkv, NQB, W), torch.int32, q.device) if idx_out is None else idx_out
+    scores = _empty((B, Hkv, NQB, NB), torch.float32, q.device) if return_scores else None
     # the size for scores == NULL covers every case (with a scores buffer the need is never larger)
-    nb = lib().sala_sparse_select_workspace(dt, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local)
+    nb = workspace_bytes("sparse_select", dtype=dt, B=B, Hq=Hq, Hkv=Hkv, d=d, Nq=Nq, L=L, block=block, topk=topk,
+                         n_init=n_init, n_local=n_local)
     ws = _ws(nb, workspace, q)
     call("sala_sparse_select", dt, B, Hq, Hkv, d, Nq, L, block, topk, n_init, n_local, _ptr(q), _ptr(k),
          _ptr(k_pooled), _ptr(idx), _ptr(scores), _ptr(ws), nb, _stream())
     return (idx, k_pooled, scores) if return_scores else (idx, k_pooled)
 
 
+def _check_idx(idx, shape_lead, allow_one_block=False):
+    """idx: int32 of shape shape_lead + (n_sel,); with allow_one_block also
+    shape_lead + (1, n_sel), the layout decode selection returns."""
+    if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int32:
+        raise ValueError("idx must be an int32 tensor")
+    lead = tuple(idx.shape[:-1])
+    if allow_one_block and idx.dim() == len(shape_lead) + 2 and lead == tuple(shape_lead) + (1,):
+        return idx.shape[-1]
+    if lead != tuple(shape_lead) or idx.dim() != len(shape_lead) + 1:
+        raise ValueError(f"idx must have shape {tuple(shape_lead)} + (n_sel,), got {tuple(idx.shape)}")
+    return idx.shape[-1]
+
+
 def sparse_prefill(q, k, v, idx, *, block=64, scale=None, out=None, workspace=None):
     """Softmax attention of q [B, Hq, N, d] over the blocks listed in idx [B, Hkv, NQB, n_sel]."""
-    _dev(q, k, v, idx, out)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    n_sel = idx.shape[-1]
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
+    B, Hq, N, d = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[1]
+    _want(k, "k", (B, Hkv, N, d), q.dtype)
+    _want(v, "v", (B, Hkv, N, d), q.dtype)
+    _want(out, "out", q.shape, q.dtype)
+    n_sel = _check_idx(idx, (B, Hkv, (N + block - 1) // block))
+    _dev(q, k, v, idx, out, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _code(q)
-    o = torch.empty_like(q) if out is None else out
-    nb = lib().sala_sparse_prefill_workspace(dt, B, Hq, Hkv, N, d, block, n_sel)
+    o = _empty_like(q) if out is None else out
+    nb = workspace_bytes("sparse_prefill", dtype=dt, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, block=block, n_sel=n_sel)
     ws = _ws(nb, workspace, q)
     call("sala_sparse_prefill", dt, B, Hq, Hkv, N, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v),
          _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
@@ -243,30 +348,37 @@ def sparse_prefill(q, k, v, idx, *, block=64, scale=None, out=None, workspace=No
 
 
 def sparse_decode(q, k_cache, v_cache, idx, *, L=None, block=64, scale=None, out=None, workspace=None):
-    """One query token per head, q [B, Hq, d], against the cached blocks listed in idx [B, Hkv, n_sel]."""
-    _dev(q, k_cache, v_cache, idx, out)
-    B, Hq, d = q.shape
-    Hkv = k_cache.shape[1]
-    L = k_cache.shape[2] if L is None else L
-    n_sel = idx.shape[-1]
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
+    """One query token per head, q [B, Hq, d], against the cached blocks listed in idx
+    [B, Hkv, n_sel] (or [B, Hkv, 1, n_sel], as decode selection returns it)."""
+    B, Hq, d = _dims(q, "q", 3)
+    _, Hkv, Lk, _ = _dims(k_cache, "k_cache", 4)
+    if L is not None and L != Lk:
+        raise ValueError(f"L = {L} must equal the cache's {Lk} tokens (a cache of larger capacity: "
+                         "sparse_decode_step)")
+    L = Lk
+    _want(k_cache, "k_cache", (B, Hkv, L, d), q.dtype)
+    _want(v_cache, "v_cache", (B, Hkv, L, d), q.dtype)
+    _want(out, "out", q.shape, q.dtype)
+    n_sel = _check_idx(idx, (B, Hkv), allow_one_block=True)
+    _dev(q, k_cache, v_cache, idx, out, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _code(q)
-    o = torch.empty_like(q) if out is None else out
-    nb = lib().sala_sparse_decode_workspace(dt, B, Hq, Hkv, L, d, block, n_sel)
+    o = _empty_like(q) if out is None else out
+    nb = workspace_bytes("sparse_decode", dtype=dt, B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=block, n_sel=n_sel)
     ws = _ws(nb, workspace, q)
     call("sala_sparse_decode", dt, B, Hq, Hkv, L, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k_cache),
          _ptr(v_cache), _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
     return o
 
 
-def _cache_dims(k_cache, v_cache, k_pooled, block):
-    B, Hkv, cap, d = k_cache.shape
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must share shape and dtype")
-    if k_pooled.dtype != torch.float32 or tuple(k_pooled.shape) != (B, Hkv, (cap + block - 1) // block, d):
-        raise ValueError("k_pooled must be float32 [B, Hkv, ceil(capacity / block), d]")
+def _cache_dims(q, k_cache, v_cache, k_pooled, block):
+    B, Hkv, cap, d = _dims(k_cache, "k_cache", 4)
+    _want(v_cache, "v_cache", k_cache.shape, k_cache.dtype)
+    if not isinstance(k_pooled, torch.Tensor):
+        raise ValueError("k_pooled must be a torch tensor")
+    _want(k_pooled, "k_pooled", (B, Hkv, (cap + block - 1) // block, d), torch.float32)
+    if q.dtype != k_cache.dtype:
+        raise ValueError("q must have the caches' dtype")
     return B, Hkv, cap, d
 
 
@@ -276,18 +388,22 @@ def sparse_prefill_chunk(q, k_new, v_new, k_cache, v_cache, k_pooled, pos0, *, b
     q [B, Hq, n, d], k_new, v_new [B, Hkv, n, d] are written into k_cache, v_cache
     [B, Hkv, capacity, d]; k_pooled [B, Hkv, ceil(capacity/64), d] fp32 is updated.
     Returns (o [B, Hq, n, d], idx [B, Hkv, ceil(n/64), n_sel])."""
-    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out)
-    B, Hkv, cap, d = _cache_dims(k_cache, v_cache, k_pooled, block)
-    Hq, n = q.shape[1], q.shape[2]
-    if k_new.shape != (B, Hkv, n, d) or v_new.shape != (B, Hkv, n, d):
-        raise ValueError("k_new, v_new must be [B, Hkv, n, d]")
+    _, Hq, n, _ = _dims(q, "q", 4)
+    B, Hkv, cap, d = _cache_dims(q, k_cache, v_cache, k_pooled, block)
+    _want(q, "q", (B, Hq, n, d), k_cache.dtype)
+    _want(k_new, "k_new", (B, Hkv, n, d), k_cache.dtype)
+    _want(v_new, "v_new", (B, Hkv, n, d), k_cache.dtype)
+    _want(out, "out", q.shape, q.dtype)
     n_sel = topk + n_init + n_local
+    _want(idx_out, "idx_out", (B, Hkv, (n + block - 1) // block, n_sel), torch.int32)
+    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _code(q)
-    o = torch.empty_like(q) if out is None else out
-    idx = idx_out if idx_out is not None else torch.empty((B, Hkv, (n + block - 1) // block, n_sel),
-                                                         dtype=torch.int32, device=q.device)
-    nb = lib().sala_sparse_prefill_chunk_workspace(dt, B, Hq, Hkv, cap, d, n, block, topk, n_init, n_local)
+    o = _empty_like(q) if out is None else out
+    idx = idx_out if idx_out is not None else _empty((B, Hkv, (n + block - 1) // block, n_sel), torch.int32,
+                                                     q.device)
+    nb = workspace_bytes("sparse_prefill_chunk", dtype=dt, B=B, Hq=Hq, Hkv=Hkv, capacity=cap, d=d, n=n, block=block,
+                         topk=topk, n_init=n_init, n_local=n_local)
     ws = _ws(nb, workspace, q)
     call("sala_sparse_prefill_chunk", dt, B, Hq, Hkv, cap, d, int(pos0), n, block, topk, n_init, n_local,
          ctypes.c_float(scale), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_pooled),
@@ -299,17 +415,21 @@ def sparse_decode_step(q, k_new, v_new, k_cache, v_cache, k_pooled, pos, *, bloc
                        n_local=2, scale=None, idx_out=None, out=None, workspace=None):
     """One generated token at position pos: q [B, Hq, d], k_new, v_new [B, Hkv, d] are
     appended to the caches (see sparse_prefill_chunk).  Returns (o [B, Hq, d], idx [B, Hkv, n_sel])."""
-    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out)
-    B, Hkv, cap, d = _cache_dims(k_cache, v_cache, k_pooled, block)
-    Hq = q.shape[1]
-    if k_new.shape != (B, Hkv, d) or v_new.shape != (B, Hkv, d):
-        raise ValueError("k_new, v_new must be [B, Hkv, d]")
+    _, Hq, _ = _dims(q, "q", 3)
+    B, Hkv, cap, d = _cache_dims(q, k_cache, v_cache, k_pooled, block)
+    _want(q, "q", (B, Hq, d), k_cache.dtype)
+    _want(k_new, "k_new", (B, Hkv, d), k_cache.dtype)
+    _want(v_new, "v_new", (B, Hkv, d), k_cache.dtype)
+    _want(out, "out", q.shape, q.dtype)
     n_sel = topk + n_init + n_local
+    _want(idx_out, "idx_out", (B, Hkv, n_sel), torch.int32)
+    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _code(q)
-    o = torch.empty_like(q) if out is None else out
-    idx = idx_out if idx_out is not None else torch.empty((B, Hkv, n_sel), dtype=torch.int32, device=q.device)
-    nb = lib().sala_sparse_decode_step_workspace(dt, B, Hq, Hkv, cap, d, block, topk, n_init, n_local)
+    o = _empty_like(q) if out is None else out
+    idx = idx_out if idx_out is not None else _empty((B, Hkv, n_sel), torch.int32, q.device)
+    nb = workspace_bytes("sparse_decode_step", dtype=dt, B=B, Hq=Hq, Hkv=Hkv, capacity=cap, d=d, block=block,
+                         topk=topk, n_init=n_init, n_local=n_local)
     ws = _ws(nb, workspace, q)
     call("sala_sparse_decode_step", dt, B, Hq, Hkv, cap, d, int(pos), block, topk, n_init, n_local,
          ctypes.c_float(scale), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_pooled),
@@ -319,11 +439,14 @@ def sparse_decode_step(q, k_new, v_new, k_cache, v_cache, k_pooled, pos, *, bloc
 
 def dense_prefill(q, k, v, *, scale=None, out=None):
     """Causal softmax attention of q [B, Hq, N, d] over every earlier token of k, v [B, Hkv, N, d] (bf16)."""
+    B, Hq, N, d = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[1]
+    _want(k, "k", (B, Hkv, N, d), q.dtype)
+    _want(v, "v", (B, Hkv, N, d), q.dtype)
+    _want(out, "out", q.shape, q.dtype)
     _dev(q, k, v, out)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
+    o = _empty_like(q) if out is None else out
     call("sala_dense_prefill", _code(q), B, Hq, Hkv, N, d, ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
          _stream())
     return o
@@ -331,25 +454,35 @@ def dense_prefill(q, k, v, *, scale=None, out=None):
 
 def ceiling_mfma(workgroups, iters, out):
     """Launch the MFMA ceiling microkernel (flops = workgroups*8*iters*8*16384)."""
+    _want(out, "out", (workgroups * 512,), torch.float32)
     _dev(out)
     call("sala_ceiling_mfma", workgroups, iters, _ptr(out), _stream())
 
 
 def ceiling_copy(src, dst):
     """Launch the streaming-copy ceiling microkernel over src.nbytes bytes."""
-    _dev(src, dst)
+    if not isinstance(src, torch.Tensor) or not isinstance(dst, torch.Tensor):
+        raise ValueError("src and dst must be torch tensors")
     nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _dev(src, dst)
     call("sala_ceiling_copy", _ptr(src), _ptr(dst), nbytes, _stream())
 
 
-def layer_group_prefill(linear_layers, sparse_layer, *, block=64, topk=64, n_init=1, n_local=2, chunk=None):
+def layer_group_prefill(linear_layers, sparse_layer, *, block=64, topk=64, n_init=1, n_local=2, chunk=None,
+                        workspaces=None):
     """The 3:1 group: each linear layer {q,k,v,decay}, then select + attend on the sparse layer {q,k,v}.
 
     Returns ([o_linear...], o_sparse, idx).  All launches go to torch's current stream.
+    workspaces: optional {"linear": uint8 tensor, "select": uint8 tensor} reused across calls.
     """
-    outs = [linear_prefill(x["q"], x["k"], x["v"], x.get("decay"), chunk=chunk, want_state=False)[0]
+    ws = workspaces or {}
+    outs = [linear_prefill(x["q"], x["k"], x["v"], x.get("decay"), chunk=chunk, want_state=False,
+                           workspace=ws.get("linear"))[0]
             for x in linear_layers]
     sp = sparse_layer
-    idx, _ = sparse_select(sp["q"], sp["k"], block=block, topk=topk, n_init=n_init, n_local=n_local)
+    idx, _ = sparse_select(sp["q"], sp["k"], block=block, topk=topk, n_init=n_init, n_local=n_local,
+                           workspace=ws.get("select"))
     o = sparse_prefill(sp["q"], sp["k"], sp["v"], idx, block=block)
     return outs, o, idx
