@@ -7,6 +7,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# Outputs, index arrays and workspaces the binding allocates are filled with
+# NaN / a sentinel first, so an element a kernel never writes fails its check.
+os.environ.setdefault("SALA_DEBUG_POISON", "1")
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -253,3 +253,44 @@ def test_generation_loop_validation():
     assert step(d=48) == UNSUPPORTED
     assert step() == WORKSPACE
     assert L.sala_sparse_decode_step_workspace(BF16, 1, 4, 2, 1000, 128, 64, 4, 1, 2) > 0
+
+
+def test_generic_workspace_query_matches_per_op_queries():
+    """sala_workspace_bytes(op, dims, ndims) returns what each per-op query returns,
+    and (size_t)-1 with a message for an unknown op, a wrong dimension count,
+    NULL dims or a dimension beyond int."""
+    L = _lib.lib()
+    cases = [
+        (0, L.sala_linear_prefill_workspace, (BF16, 1, 32, 32768, 128, 128)),
+        (0, L.sala_linear_prefill_workspace, (BF16, 2, 3, 1000, 128, 64)),
+        (1, L.sala_sparse_select_workspace, (BF16, 1, 32, 2, 128, 131072, 131072, 64, 64, 1, 2)),
+        (1, L.sala_sparse_select_workspace, (BF16, 4, 32, 2, 128, 1, 1048576, 64, 64, 1, 2)),
+        (2, L.sala_sparse_prefill_workspace, (BF16, 1, 32, 2, 262144, 128, 64, 67)),
+        (3, L.sala_sparse_decode_workspace, (BF16, 4, 32, 2, 1048576, 128, 64, 67)),
+        (4, L.sala_sparse_prefill_chunk_workspace, (BF16, 2, 8, 2, 587, 128, 256, 64, 3, 1, 2)),
+        (5, L.sala_sparse_decode_step_workspace, (BF16, 2, 8, 2, 587, 128, 64, 3, 1, 2)),
+    ]
+    for op, fn, dims in cases:
+        arr = (ctypes.c_int64 * len(dims))(*dims)
+        want = fn(*dims)
+        assert L.sala_workspace_bytes(op, arr, len(dims)) == want, (op, dims)
+    bad = ctypes.c_size_t(-1).value
+    arr = (ctypes.c_int64 * 6)(BF16, 1, 2, 256, 128, 128)
+    assert L.sala_workspace_bytes(6 + 3, arr, 6) == bad and b"unknown operation" in L.sala_last_error()
+    assert L.sala_workspace_bytes(-1, arr, 6) == bad
+    assert L.sala_workspace_bytes(0, arr, 5) == bad and b"takes 6" in L.sala_last_error()
+    assert L.sala_workspace_bytes(0, None, 6) == bad and b"NULL" in L.sala_last_error()
+    big = (ctypes.c_int64 * 6)(BF16, 1, 2, 1 << 40, 128, 128)
+    assert L.sala_workspace_bytes(0, big, 6) == bad and b"does not fit" in L.sala_last_error()
+    # the binding's query goes through the generic call
+    import hybrid_sparse_linear_amd as sala
+    assert sala.workspace_bytes("linear_prefill", dtype=BF16, B=1, H=32, N=32768, d=128, chunk=128) == \
+        L.sala_linear_prefill_workspace(BF16, 1, 32, 32768, 128, 128)
+    with pytest.raises(ValueError):
+        sala.workspace_bytes("no_such_op")
+
+
+def test_decode_selection_accepts_large_groups():
+    """Decode selection sums every query head of a group (no upper limit on G);
+    here the call gets as far as the workspace check for G = 64."""
+    assert ss(Hq=128, Hkv=2, Nq=1, L=64 * 300, topk=8) == WORKSPACE

@@ -14,7 +14,7 @@ import torch
 import hybrid_sparse_linear_amd as sala
 from hybrid_sparse_linear_amd import inputs as I
 from oracle import sparse as OS
-from parity import assert_close, check_idx_row, host64, near_tie_rows
+from parity import assert_close, check_idx_row, host64, near_tie_rows, poisoned
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +32,8 @@ def _oracle_prefix_checks(q, k, v, L, rows_q, topk, n_init, n_local, o_rows, idx
     for b in range(B):
         for h in range(Hkv):
             for i in range(qb0, ridx.shape[2]):
-                cands = list(range(n_init, min(i - n_local, L // 64 - 1) + 1))
-                forced = sorted(set(range(min(n_init, i + 1))) | set(range(max(0, i - n_local + 1), i + 1)))
+                cands = OS.candidate_blocks(i, L, 64, n_init, n_local)
+                forced = sorted(OS.forced_blocks(i, n_init, n_local))
                 nt = near_tie_rows([scores[b, h, i]], [cands], topk)[0]
                 check_idx_row(idx_rows[b, h, i - qb0].tolist(), ridx[b, h, i].tolist(), scores[b, h, i], cands,
                               forced, topk, nt, f"{what} b{b} h{h} block {i}")
@@ -56,7 +56,7 @@ def test_chunked_prefill_then_decode_steps():
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     kc = torch.zeros((B, Hkv, cap, d), dtype=I.BF16, device="cuda")
     vc = torch.zeros_like(kc)
-    kp = torch.zeros((B, Hkv, (cap + 63) // 64, d), dtype=torch.float32, device="cuda")
+    kp = poisoned((B, Hkv, (cap + 63) // 64, d), torch.float32)  # every block is pooled before it is read
     kw = dict(topk=topk, n_init=n_init, n_local=n_local)
     ws = torch.empty(max(sala.workspace_bytes("sparse_prefill_chunk", dtype=1, B=B, Hq=Hq, Hkv=Hkv, capacity=cap, d=d,
                                               n=256, block=64, **kw),
@@ -92,8 +92,8 @@ def test_chunked_prefill_then_decode_steps():
             kbar = np.stack([np.stack([OS.pool_blocks(kh[b, h], 64) for h in range(Hkv)]) for b in range(B)])
             ridx, sc = OS.sparse_select_decode(host64(q[:, :, t]), kbar, L, 64, topk, n_init, n_local)
             i = t // 64
-            cands = list(range(n_init, min(i - n_local, L // 64 - 1) + 1))
-            forced = sorted(set(range(min(n_init, i + 1))) | set(range(max(0, i - n_local + 1), i + 1)))
+            cands = OS.candidate_blocks(i, L, 64, n_init, n_local)
+            forced = sorted(OS.forced_blocks(i, n_init, n_local))
             for b in range(B):
                 for h in range(Hkv):
                     nt = near_tie_rows([sc[b, h]], [cands], topk)[0]

@@ -1,6 +1,8 @@
 """GPU parity of the fused linear layer (QK RMS norm, rotate-half RoPE and the
 output gate inside the linear-attention kernels) through the C ABI against
-the float64 oracle (oracle.neighbours), on ragged multi-chunk, multi-segment
+the float64 oracle (oracle.neighbours; bf16 layers with the transformed q and
+k stored in bf16, as the kernels and an unfused producer keep them), on
+ragged multi-chunk, multi-segment
 shapes, with each neighbour alone and all together, at large positions, with
 carried state, split prefills and decode steps, and at the 32-head 32K and
 256K shapes on sampled rows."""
@@ -52,7 +54,8 @@ def _oracle(x, nb, decay, s0, norm_q, norm_k, rope, gate, pos0):
     return NB.linear_layer_fused(host64(x["q"]), host64(x["k"]), host64(x["v"]), decay.double().numpy(),
                                  None if s0 is None else host64(s0),
                                  host64(nb["gamma_q"]) if norm_q else None, host64(nb["gamma_k"]) if norm_k else None,
-                                 1e-6, 10000.0 if rope else None, pos0, host64(nb["gate"]) if gate else None)
+                                 1e-6, 10000.0 if rope else None, pos0, host64(nb["gate"]) if gate else None,
+                                 store="bf16")
 
 
 @pytest.mark.parametrize("case", NB_CASES, ids=lambda c: f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}C{c[4]}p{c[5]}"
@@ -105,7 +108,8 @@ def test_fused_split_prefill_and_decode_continue_the_sequence():
                                   dev(decay), pos=pos, gate=gt[:, :, N].contiguous(), **kw)
     torch.cuda.synchronize()
     ro, rs = NB.linear_layer_fused(host64(x["q"]), host64(x["k"]), host64(x["v"]), decay.double().numpy(), None,
-                                   host64(nb["gamma_q"]), host64(nb["gamma_k"]), 1e-6, 10000.0, 0, host64(nb["gate"]))
+                                   host64(nb["gamma_q"]), host64(nb["gamma_k"]), 1e-6, 10000.0, 0, host64(nb["gate"]),
+                                   store="bf16")
     assert_close(o_all, ro[:, :, :N], I.BF16, "whole")
     assert_close(torch.cat([o1, o2], dim=2), ro[:, :, :N], I.BF16, "split")
     assert_close(s2, host64(s_all), I.BF16, "split state vs whole state")
@@ -132,7 +136,7 @@ def test_fused_linear_decode(dt, d):
     torch.cuda.synchronize()
     ro, rs = NB.linear_decode_fused(host64(q), host64(k), host64(v), host64(s0), decay.double().numpy(),
                                     host64(nb["gamma_q"]), host64(nb["gamma_k"]), 1e-6, 10000.0, positions,
-                                    host64(gate))
+                                    host64(gate), store="bf16" if dt == I.BF16 else None)
     assert_close(o, ro, dt, "o")
     assert_close(state, rs, dt, "state")
 
@@ -153,7 +157,7 @@ def test_fused_linear_full_size_rows(N):
     for h in ([0, 31] if N > 32768 else [0, 13, 31]):
         ref = NB.linear_layer_fused_rows(host64(x["q"][0, h]), host64(x["k"][0, h]), host64(x["v"][0, h]), dec[h],
                                          rows, None, host64(nb["gamma_q"]), host64(nb["gamma_k"]), 1e-6, 10000.0, 0,
-                                         host64(nb["gate"][0, h]))
+                                         host64(nb["gate"][0, h]), store="bf16")
         assert_close(o[0, h, rows], ref, I.BF16, f"head {h} rows")
 
 

@@ -56,6 +56,25 @@ def test_linear_prefill(case):
     assert_close(st, rs, torch.float32 if dt == I.F32 else I.BF16, "state")
 
 
+def test_linear_prefill_large_inputs():
+    """q, k, v ~ N(0, 0.25) -- four times the workloads' scale per factor -- over
+    2085 tokens with lam = 1 (plain causal linear attention, outputs growing as
+    sqrt(t)) and lam = 0.99, and a carried state: every row and every head held to
+    the relative rules.  The absolute floor of 1 in the elementwise rule is
+    below this output scale (row RMS up to ~60), where bf16 operand rounding alone
+    gives absolute errors of ~0.3, so that one rule is not applied here."""
+    B, H, N, d = 1, 2, 2085, 128
+    say("linear_prefill large inputs", B, H, N, d)
+    x = I.linear_inputs(B, H, N, d, I.BF16, 90, 7, 0.5)
+    decay = torch.tensor([1.0, 0.99], dtype=torch.float32)
+    s0 = I.normal((B, H, d, d), 76, 1.0)
+    o, st = sala.linear_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(decay), dev(s0))
+    torch.cuda.synchronize()
+    ro, rs = OL.linear_prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), decay.double().numpy(), host64(s0))
+    assert_close(o, ro, I.BF16, "o", absolute_floor=False)
+    assert_close(st, rs, I.BF16, "state", absolute_floor=False)
+
+
 def test_linear_prefill_state_alias_and_no_decay():
     say("linear_prefill alias")
     B, H, N, d = 1, 2, 700, 128
@@ -227,6 +246,29 @@ def test_sparse_select_decode_general_path(B, Hq, Hkv, L, d, topk):
             nt = near_tie_rows([scores[b, h]], [cands], topk)[0]
             check_idx_row(g[b, h, 0], ridx[b, h], scores[b, h], cands, sorted(OS.forced_blocks(i, 1, 2)), topk, nt,
                           f"decode b{b} h{h}")
+
+
+@pytest.mark.parametrize("topk", [8, 100], ids=["top64_path", "general_path"])
+def test_sparse_select_decode_group_of_64(topk):
+    """Decode selection with 64 query heads per KV head (more than the 32 the
+    top-64 path loads up front): the pooled query is the mean over all 64."""
+    B, Hq, Hkv, d = 2, 128, 2, 128
+    L = 64 * 300 + 7
+    say("sparse_select decode G=64", topk)
+    NB = (L + 63) // 64
+    kbar = I.normal((B, Hkv, NB, d), 135, 1.0, I.F32)
+    q = I.normal((B, Hq, 1, d), 136, 1.0, I.BF16)
+    idx, _ = sala.sparse_select(dev(q), None, k_pooled=dev(kbar), L=L, topk=topk)
+    torch.cuda.synchronize()
+    ridx, scores = OS.sparse_select_decode(host64(q[:, :, 0]), host64(kbar), L, 64, topk)
+    i = (L - 1) // 64
+    cands = OS.candidate_blocks(i, L, 64, 1, 2)
+    g = idx.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            nt = near_tie_rows([scores[b, h]], [cands], topk)[0]
+            check_idx_row(g[b, h, 0], ridx[b, h], scores[b, h], cands, sorted(OS.forced_blocks(i, 1, 2)), topk, nt,
+                          f"G64 b{b} h{h}")
 
 
 def test_sparse_select_decode_many_chunks_reuses_workspace():

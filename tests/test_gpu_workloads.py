@@ -9,7 +9,6 @@ Inputs are generated on the GPU by the seeded generator and copied to the
 host only where the oracle reads them.
 """
 
-import math
 
 import numpy as np
 import pytest
@@ -19,7 +18,7 @@ import hybrid_sparse_linear_amd as sala
 from hybrid_sparse_linear_amd import inputs as I
 from oracle import linear as OL
 from oracle import sparse as OS
-from parity import assert_close, check_idx_row, host64, near_tie_rows
+from parity import OnDevice, assert_close, check_idx_row, host64, near_tie_rows, poisoned
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +85,30 @@ def test_workload1_tiny_group_fp32():
     assert_close(o, ro, I.F32, "sparse layer")
 
 
+def test_workload1_group_entry_point():
+    """The group entry point (three linear layers, then selection and sparse
+    attention on one stream) at the tiny fp32 workload, against the oracle."""
+    say("workload 1 through layer_group_prefill")
+    lin = [I.workload1_linear(layer) for layer in range(3)]
+    sp = I.workload1_sparse()
+    outs, o, idx = sala.layer_group_prefill([{n: x[n].cuda() for n in ("q", "k", "v", "decay")} for x in lin],
+                                            {n: sp[n].cuda() for n in ("q", "k", "v")}, topk=4, chunk=64)
+    torch.cuda.synchronize()
+    for layer, (x, ol) in enumerate(zip(lin, outs)):
+        ro, _ = OL.linear_prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), x["decay"].double().numpy())
+        assert_close(ol, ro, I.F32, f"group linear layer {layer}")
+    ridx, scores, _ = OS.sparse_select_prefill(host64(sp["q"]), host64(sp["k"]), 64, 4)
+    g = idx.cpu().numpy()
+    for h in range(4):
+        cands = [OS.candidate_blocks(i, 2048, 64, 1, 2) for i in range(32)]
+        nt = near_tie_rows(scores[0, h], cands, 4)
+        for i in range(32):
+            check_idx_row(g[0, h, i], ridx[0, h, i], scores[0, h, i], cands[i], sorted(OS.forced_blocks(i, 1, 2)), 4,
+                          nt[i], f"group h{h} i{i}")
+    ro = OS.sparse_attention_prefill(host64(sp["q"]), host64(sp["k"]), host64(sp["v"]), g, 64)
+    assert_close(o, ro, I.F32, "group sparse layer")
+
+
 @pytest.mark.parametrize("N", [32768, 262144], ids=["workload2_32K", "workload4_linear_256K"])
 def test_linear_prefill_full_size(N):
     say("linear full", N)
@@ -105,12 +128,11 @@ def sparse_full_check(N, workload, n_rows=10, attn_rows_per_block=3):
     x = I.workload3_sparse(0 if workload == 3 else 3, "cuda", N=N, workload=workload)
     q, k, v = x["q"], x["k"], x["v"]
     Hq, Hkv, d = q.shape[1], k.shape[1], q.shape[3]
-    G = Hq // Hkv
     nqb = N // 64
-    ws_sel = torch.zeros(sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N, block=64,
-                                              topk=64, n_init=1, n_local=2), dtype=torch.uint8, device="cuda")
-    idx = torch.empty((1, Hkv, nqb, 67), dtype=torch.int32, device="cuda")
-    kp = torch.empty((1, Hkv, nqb, d), dtype=torch.float32, device="cuda")
+    ws_sel = poisoned((sala.workspace_bytes("sparse_select", dtype=1, B=1, Hq=Hq, Hkv=Hkv, d=d, Nq=N, L=N, block=64,
+                                            topk=64, n_init=1, n_local=2) // 4,), torch.float32)
+    idx = poisoned((1, Hkv, nqb, 67), torch.int32)
+    kp = poisoned((1, Hkv, nqb, d), torch.float32)
     sala.sparse_select(q, k, k_pooled=kp, idx_out=idx, workspace=ws_sel)
     o = sala.sparse_prefill(q, k, v, idx)
     torch.cuda.synchronize()
@@ -118,35 +140,22 @@ def sparse_full_check(N, workload, n_rows=10, attn_rows_per_block=3):
     g = idx.cpu().numpy()
     rng = np.random.default_rng(N)
     blocks = sorted({0, 1, 2, 65, 66, 67, nqb // 2, nqb - 1} | set(rng.integers(3, nqb, n_rows).tolist()))
+    # the oracle's selection of the sampled query blocks, from the device tensors
+    ridx, scores, kbar = OS.sparse_select_prefill_rows(OnDevice(q), OnDevice(k), blocks, 64, 64, 1, 2)
     ties = 0
     for h in range(Hkv):
-        kbar = OS.pool_blocks(host64(k[0, h]), 64)
-        assert_close(kp[0, h], kbar, I.F32, f"k_pooled h{h}")
-        for i in blocks:
-            qbar = host64(q[0, h * G:(h + 1) * G, i * 64:(i + 1) * 64]).reshape(-1, d).mean(axis=0)
-            scores = (kbar @ qbar) / math.sqrt(d)
-            ref = OS.select_row(scores, i, N, 64, 64, 1, 2)
+        assert_close(kp[0, h], kbar[0, h], I.F32, f"k_pooled h{h}")
+        for r, i in enumerate(blocks):
             cands = OS.candidate_blocks(i, N, 64, 1, 2)
-            nt = near_tie_rows([scores], [cands], 64)[0]
-            ok = check_idx_row(g[0, h, i], ref, scores, cands, sorted(OS.forced_blocks(i, 1, 2)), 64, nt,
-                               f"h{h} i{i}")
+            nt = near_tie_rows([scores[0, h, r]], [cands], 64)[0]
+            ok = check_idx_row(g[0, h, i], ridx[0, h, r], scores[0, h, r], cands, sorted(OS.forced_blocks(i, 1, 2)),
+                               64, nt, f"h{h} i{i}")
             ties += (not ok)
-    # attention rows: oracle restricted softmax over the GPU's (validated) selection
-    trip = [(0, hq, i * 64 + r) for i in blocks for hq in rng.choice(Hq, 2, replace=False).tolist()
+    # attention rows: the oracle's restricted softmax over the GPU's (validated) selection
+    rows = [(0, hq, i * 64 + r) for i in blocks for hq in rng.choice(Hq, 2, replace=False).tolist()
             for r in rng.choice(64, attn_rows_per_block, replace=False).tolist()]
-    ref = np.zeros((len(trip), d))
-    got = np.zeros((len(trip), d))
-    for n_, (b, hq, t) in enumerate(trip):
-        i = t // 64
-        toks = np.concatenate([np.arange(j * 64, (j + 1) * 64) for j in g[0, hq // G, i] if j >= 0])
-        toks = toks[toks <= t]
-        kk = host64(k[0, hq // G, torch.from_numpy(toks).cuda()])
-        vv = host64(v[0, hq // G, torch.from_numpy(toks).cuda()])
-        logit = (kk @ host64(q[0, hq, t])) / math.sqrt(d)
-        logit -= logit.max()
-        p = np.exp(logit)
-        ref[n_] = (p / p.sum()) @ vv
-        got[n_] = host64(o[0, hq, t])
+    ref = OS.sparse_attention_prefill_rows(OnDevice(q), OnDevice(k), OnDevice(v), g, rows, 64)
+    got = np.stack([host64(o[b, hq, t]) for b, hq, t in rows])
     assert_close(got, ref, I.BF16, "attention rows")
     return ties
 
@@ -185,7 +194,6 @@ def test_workload5_decode_1M():
     q, kc, vc = sp["q"], sp["k_cache"], sp["v_cache"]
     B, Hq, d = q.shape
     Hkv = kc.shape[1]
-    G = Hq // Hkv
     idx, kp = sala.sparse_select(q[:, :, None].contiguous(), kc)      # pooled cache built from the K cache
     idx2, _ = sala.sparse_select(q[:, :, None].contiguous(), None, k_pooled=kp, L=L)  # decode against the pooled cache
     o = sala.sparse_decode(q, kc, vc, idx2[:, :, 0].contiguous())
@@ -193,21 +201,15 @@ def test_workload5_decode_1M():
     assert torch.equal(idx, idx2)
     i = (L - 1) // 64
     cands = OS.candidate_blocks(i, L, 64, 1, 2)
+    kbar = np.stack([np.stack([OS.pool_blocks(host64(kc[b, h]), 64) for h in range(Hkv)]) for b in range(B)])
+    assert_close(kp, kbar, I.F32, "k_pooled")
+    ridx, scores = OS.sparse_select_decode(host64(q), kbar, L, 64, 64, 1, 2)
     g = idx2[:, :, 0].cpu().numpy()
     for b in range(B):
         for h in range(Hkv):
-            kbar = OS.pool_blocks(host64(kc[b, h]), 64)
-            assert_close(kp[b, h], kbar, I.F32, f"k_pooled b{b} h{h}")
-            qbar = host64(q[b, h * G:(h + 1) * G]).mean(axis=0)
-            scores = (kbar @ qbar) / math.sqrt(d)
-            ref = OS.select_row(scores, i, L, 64, 64, 1, 2)
-            nt = near_tie_rows([scores], [cands], 64)[0]
-            check_idx_row(g[b, h], ref, scores, cands, sorted(OS.forced_blocks(i, 1, 2)), 64, nt, f"b{b} h{h}")
-            for hq in range(h * G, (h + 1) * G):
-                toks = np.concatenate([np.arange(j * 64, min((j + 1) * 64, L)) for j in g[b, h] if j >= 0])
-                kk = host64(kc[b, h, torch.from_numpy(toks).cuda()])
-                vv = host64(vc[b, h, torch.from_numpy(toks).cuda()])
-                logit = (kk @ host64(q[b, hq])) / math.sqrt(d)
-                logit -= logit.max()
-                p = np.exp(logit)
-                assert_close(o[b, hq], (p / p.sum()) @ vv, I.BF16, f"decode o b{b} hq{hq}")
+            nt = near_tie_rows([scores[b, h]], [cands], 64)[0]
+            check_idx_row(g[b, h], ridx[b, h], scores[b, h], cands, sorted(OS.forced_blocks(i, 1, 2)), 64, nt,
+                          f"b{b} h{h}")
+    # every head's output: the oracle's decode softmax over the GPU's (validated) selection
+    ro = OS.sparse_attention_decode(host64(q), OnDevice(kc), OnDevice(vc), g, L, 64)
+    assert_close(o, ro, I.BF16, "decode o")
