@@ -34,7 +34,7 @@ import torch
 from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 
 __all__ = ["linear_prefill", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
-           "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_select",
+           "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_decode_step_noalloc", "sparse_select",
            "sparse_prefill", "sparse_decode",
            "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
 
@@ -435,6 +435,29 @@ def sparse_decode_step(q, k_new, v_new, k_cache, v_cache, k_pooled, pos, *, bloc
          ctypes.c_float(scale), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_pooled),
          _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
     return o, idx
+
+
+def sparse_decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, k_pooled, pos, idx_out, out, *, block=64, topk=64,
+                               n_init=1, n_local=2, scale=None):
+    """sparse_decode_step without a workspace and without allocating: the library's
+    fixed per-GPU scratch array serves as the workspace, and the caller passes the
+    outputs (idx_out [B, Hkv, n_sel] int32, out like q).  Calls that overlap on one
+    GPU share that array and must not be made.  Returns (out, idx_out)."""
+    _, Hq, _ = _dims(q, "q", 3)
+    B, Hkv, cap, d = _cache_dims(q, k_cache, v_cache, k_pooled, block)
+    _want(q, "q", (B, Hq, d), k_cache.dtype)
+    _want(k_new, "k_new", (B, Hkv, d), k_cache.dtype)
+    _want(v_new, "v_new", (B, Hkv, d), k_cache.dtype)
+    if out is None or idx_out is None:
+        raise ValueError("the allocation-free call needs out and idx_out")
+    _want(out, "out", q.shape, q.dtype)
+    _want(idx_out, "idx_out", (B, Hkv, topk + n_init + n_local), torch.int32)
+    _dev(q, k_new, v_new, k_cache, v_cache, k_pooled, idx_out, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    call("sala_sparse_decode_step_noalloc", _code(q), B, Hq, Hkv, cap, d, int(pos), block, topk, n_init, n_local,
+         ctypes.c_float(scale), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_pooled),
+         _ptr(idx_out), _ptr(out), _stream())
+    return out, idx_out
 
 
 def dense_prefill(q, k, v, *, scale=None, out=None):

@@ -29,6 +29,8 @@ _SIGS = {
     "sala_sparse_decode_step_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_sparse_decode_step": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p,
                                      _p, _p, _z, _p]),
+    "sala_sparse_decode_step_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p,
+                                             _p, _p, _p]),
     "sala_sparse_select": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_sparse_select_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_sparse_prefill": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _z, _p]),

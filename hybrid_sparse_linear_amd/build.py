@@ -26,6 +26,7 @@ SOURCES = [
     "sparse_prefill.hip",
     "sparse_decode.hip",
     "ceilings.hip",
+    "noalloc.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

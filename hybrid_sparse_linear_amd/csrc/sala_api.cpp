@@ -350,10 +350,14 @@ size_t sala_sparse_decode_step_workspace(int dtype, int B, int Hq, int Hkv, int 
          sala::sparse_decode_workspace(dtype, B, Hq, Hkv, capacity, d, block, n_sel);
 }
 
-int sala_sparse_decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block, int topk,
-                            int n_init, int n_local, float scale, const void *q, const void *k_new, const void *v_new,
-                            void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o, void *ws,
-                            size_t ws_bytes, void *stream) {
+namespace {
+// The decode step behind both entry points: with use_scratch, the workspace is
+// this device's fixed scratch array (ws / ws_bytes ignored), looked up only
+// after every argument has been validated.
+int decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block, int topk, int n_init,
+                int n_local, float scale, const void *q, const void *k_new, const void *v_new, void *k_cache,
+                void *v_cache, float *k_pooled, int32_t *idx, void *o, void *ws, size_t ws_bytes, bool use_scratch,
+                void *stream) {
   int s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_sparse_common(B, Hq, Hkv, block, topk, "topk"))) return s;
@@ -377,6 +381,13 @@ int sala_sparse_decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int
   const int L = pos + 1;
   const size_t sel = step_select_ws(dtype, B, Hq, Hkv, d, L, block, topk, n_init, n_local);
   const size_t need = sel + sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel);
+  if (use_scratch) {
+    REQUIRE(need <= SALA_NOALLOC_SCRATCH_BYTES, SALA_ERR_WORKSPACE,
+            "this step needs %zu bytes of workspace, more than the %u-byte scratch array of the allocation-free call",
+            need, (unsigned)SALA_NOALLOC_SCRATCH_BYTES);
+    if ((s = hip_status(sala::noalloc_scratch(&ws), "sala_sparse_decode_step_noalloc: scratch address"))) return s;
+    ws_bytes = SALA_NOALLOC_SCRATCH_BYTES;
+  }
   if ((s = check_ws(ws, ws_bytes, need))) return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = sala::launch_kv_append(dtype, B * Hkv, capacity, d, block, pos, k_new, v_new, k_cache, v_cache,
@@ -389,6 +400,23 @@ int sala_sparse_decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int
   sala::SparseDecodeArgs da{dtype, B, Hq, Hkv, L, d, block, n_sel, scale, q, k_cache, v_cache, idx, o,
                             static_cast<char *>(ws) + sel, capacity};
   return hip_status(sala::launch_sparse_decode(da, st), "sala_sparse_decode_step attend");
+}
+}  // namespace
+
+int sala_sparse_decode_step(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block, int topk,
+                            int n_init, int n_local, float scale, const void *q, const void *k_new, const void *v_new,
+                            void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o, void *ws,
+                            size_t ws_bytes, void *stream) {
+  return decode_step(dtype, B, Hq, Hkv, capacity, d, pos, block, topk, n_init, n_local, scale, q, k_new, v_new,
+                     k_cache, v_cache, k_pooled, idx, o, ws, ws_bytes, false, stream);
+}
+
+int sala_sparse_decode_step_noalloc(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block,
+                                    int topk, int n_init, int n_local, float scale, const void *q, const void *k_new,
+                                    const void *v_new, void *k_cache, void *v_cache, float *k_pooled, int32_t *idx,
+                                    void *o, void *stream) {
+  return decode_step(dtype, B, Hq, Hkv, capacity, d, pos, block, topk, n_init, n_local, scale, q, k_new, v_new,
+                     k_cache, v_cache, k_pooled, idx, o, nullptr, 0, true, stream);
 }
 
 size_t sala_sparse_prefill_chunk_workspace(int dtype, int B, int Hq, int Hkv, int capacity, int d, int n, int block,

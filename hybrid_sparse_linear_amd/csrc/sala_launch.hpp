@@ -102,6 +102,9 @@ hipError_t launch_sparse_decode(const SparseDecodeArgs &a, hipStream_t st);
 // kernel with the block list replaced by 0..i.
 hipError_t launch_dense_prefill(const SparsePrefillArgs &a, hipStream_t st);
 
+// Device address of this device's fixed scratch array (allocation-free entry points).
+hipError_t noalloc_scratch(void **out);
+
 // Measured-ceiling microkernels (not on the attention path).
 hipError_t launch_ceiling_mfma(int workgroups, int iters, float *out, hipStream_t st);
 hipError_t launch_ceiling_copy(const void *src, void *dst, size_t bytes, hipStream_t st);

@@ -199,6 +199,27 @@ int sala_output_gate(int dtype, size_t n, const void *o, const void *gate, void 
  * Results equal sala_sparse_select + sala_sparse_prefill (or
  * sala_sparse_decode) run on the first pos0 + n (pos + 1) tokens bit for bit.
  * ------------------------------------------------------------------------ */
+/* ------------------------------------------------------------------------
+ * sala_sparse_decode_step_noalloc -- sala_sparse_decode_step for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without
+ * ws / ws_bytes, the same kernels and bit-identical results.  The workspace
+ * is a fixed device array of SALA_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per GPU, held from library load until the process ends); a call whose
+ * workspace (sala_sparse_decode_step_workspace at capacity pos + 1) exceeds
+ * it returns SALA_ERR_WORKSPACE and enqueues nothing.  The call allocates
+ * nothing.  All calls on one GPU share that array: calls that may overlap on
+ * one GPU (different streams, no ordering between them) race and must not be
+ * made.  Failure to find the array's device address returns SALA_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+#define SALA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int sala_sparse_decode_step_noalloc(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos, int block,
+                                    int topk, int n_init, int n_local, float scale,
+                                    const void *q, const void *k_new, const void *v_new,
+                                    void *k_cache, void *v_cache, float *k_pooled, int32_t *idx, void *o,
+                                    void *stream);
+
 size_t sala_sparse_prefill_chunk_workspace(int dtype, int B, int Hq, int Hkv, int capacity, int d, int n,
                                            int block, int topk, int n_init, int n_local);
 int sala_sparse_prefill_chunk(int dtype, int B, int Hq, int Hkv, int capacity, int d, int pos0, int n,

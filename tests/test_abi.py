@@ -294,3 +294,24 @@ def test_decode_selection_accepts_large_groups():
     """Decode selection sums every query head of a group (no upper limit on G);
     here the call gets as far as the workspace check for G = 64."""
     assert ss(Hq=128, Hkv=2, Nq=1, L=64 * 300, topk=8) == WORKSPACE
+
+
+def test_noalloc_decode_step_validation():
+    """The allocation-free decode step validates like the decode step, and rejects
+    a step whose workspace exceeds its fixed scratch array, before any HIP call."""
+    L = _lib.lib()
+
+    def step(**kw):
+        a = dict(dtype=BF16, B=4, Hq=32, Hkv=2, cap=1 << 20, d=128, pos=(1 << 20) - 1, block=64, topk=64, n_init=1,
+                 n_local=2)
+        a.update(kw)
+        return L.sala_sparse_decode_step_noalloc(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["cap"], a["d"], a["pos"],
+                                                 a["block"], a["topk"], a["n_init"], a["n_local"],
+                                                 ctypes.c_float(0.088), A, A, A, A, A, A, A, A, NUL)
+    assert step(pos=1 << 20) == INVALID
+    assert step(d=96) == UNSUPPORTED
+    assert step(Hq=3) == INVALID
+    # B = 64 rows of 32 heads: 64 * 32 * 67 split partials of 130 floats = 71 MB > 16 MiB
+    assert step(B=64) == WORKSPACE and b"scratch" in L.sala_last_error()
+    need = L.sala_sparse_decode_step_workspace(BF16, 4, 32, 2, 1 << 20, 128, 64, 64, 1, 2)
+    assert 0 < need <= 16 << 20
