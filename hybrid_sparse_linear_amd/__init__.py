@@ -494,18 +494,30 @@ def ceiling_copy(src, dst):
 
 
 def layer_group_prefill(linear_layers, sparse_layer, *, block=64, topk=64, n_init=1, n_local=2, chunk=None,
-                        workspaces=None):
+                        workspaces=None, out=None, sparse_events=None):
     """The 3:1 group: each linear layer {q,k,v,decay}, then select + attend on the sparse layer {q,k,v}.
 
     Returns ([o_linear...], o_sparse, idx).  All launches go to torch's current stream.
-    workspaces: optional {"linear": uint8 tensor, "select": uint8 tensor} reused across calls.
+    workspaces: optional {"linear": [uint8 tensor per layer] or one tensor, "select": ..., "sparse": ...}
+    reused across calls.  out: optional preallocated {"linear": [o per layer], "sparse": o, "idx": idx,
+    "k_pooled": k_pooled}.  sparse_events: optional (start, end) torch events recorded on the current
+    stream around the sparse attention launch (its own duration, for measurement).
     """
     ws = workspaces or {}
-    outs = [linear_prefill(x["q"], x["k"], x["v"], x.get("decay"), chunk=chunk, want_state=False,
-                           workspace=ws.get("linear"))[0]
-            for x in linear_layers]
+    out = out or {}
+    lws = ws.get("linear")
+    outs = []
+    for n, x in enumerate(linear_layers):
+        w = lws[n] if isinstance(lws, (list, tuple)) else lws
+        o = out["linear"][n] if "linear" in out else None
+        outs.append(linear_prefill(x["q"], x["k"], x["v"], x.get("decay"), chunk=chunk, want_state=False,
+                                   workspace=w, out=o)[0])
     sp = sparse_layer
     idx, _ = sparse_select(sp["q"], sp["k"], block=block, topk=topk, n_init=n_init, n_local=n_local,
-                           workspace=ws.get("select"))
-    o = sparse_prefill(sp["q"], sp["k"], sp["v"], idx, block=block)
+                           workspace=ws.get("select"), idx_out=out.get("idx"), k_pooled=out.get("k_pooled"))
+    if sparse_events is not None:
+        sparse_events[0].record(torch.cuda.current_stream())
+    o = sparse_prefill(sp["q"], sp["k"], sp["v"], idx, block=block, workspace=ws.get("sparse"), out=out.get("sparse"))
+    if sparse_events is not None:
+        sparse_events[1].record(torch.cuda.current_stream())
     return outs, o, idx
