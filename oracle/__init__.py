@@ -30,10 +30,15 @@ Modules:
              selected token set (prefill and decode).
   neighbours -- the linear layer's QK RMS normalisation, HyPE RoPE and output
              gate, and the layer composed with them (prefill and decode).
+  backward -- gradients of the linear layer (dq, dk, dv, d state_in) and of
+             the sparse attention at a fixed selection (dq, dk, dv), for the
+             continual training the pages describe.
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle_linear.py``, ``tests/test_oracle_sparse.py`` and
-``tests/test_oracle_neighbours.py`` against
+``tests/test_oracle_linear.py``, ``tests/test_oracle_sparse.py``,
+``tests/test_oracle_neighbours.py`` and ``tests/test_oracle_backward.py``
+(central finite differences, an independent chunked form, torch autograd of
+scaled_dot_product_attention in float64) against
 exact rational brute force, closed forms, special cases that reduce to a
 library routine, or invariants.  The *choice* of the method's unstated
 details (no feature map or normaliser in linear attention, the decay form,
@@ -42,4 +47,4 @@ readings are listed in the design notes and are pinned only by the
 internal invariants, not by any number on the pages.
 """
 
-from . import linear, neighbours, sparse  # noqa: F401
+from . import backward, linear, neighbours, sparse  # noqa: F401
