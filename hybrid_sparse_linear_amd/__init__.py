@@ -11,6 +11,7 @@ CPU or PyTorch fallback -- a missing ``libsala.so`` raises.
 
 Entry points (same names as the C ABI, without the ``sala_`` prefix):
   linear_prefill   causal decayed linear attention over a sequence
+  linear_prefill_backward  its gradients (dq, dk, dv, d state_in)
   linear_decode    one token of the same recurrence (state updated in place)
   sparse_select    pooled block scores and top-k block selection
   sparse_prefill   softmax attention over the selected blocks
@@ -33,7 +34,7 @@ import torch
 
 from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 
-__all__ = ["linear_prefill", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
+__all__ = ["linear_prefill", "linear_prefill_backward", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
            "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_decode_step_noalloc", "sparse_select",
            "sparse_prefill", "sparse_decode",
            "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
@@ -179,6 +180,29 @@ def linear_prefill(q, k, v, decay=None, state=None, *, chunk=None, out=None, sta
     call("sala_linear_prefill", dt, B, H, N, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(decay), _ptr(state),
          _ptr(so), _ptr(ws), nb, _stream())
     return o, so
+
+
+def linear_prefill_backward(q, k, v, dout, decay=None, state=None, dstate_out=None, *, chunk=None, dq=None, dk=None,
+                            dv=None, want_dstate=True, workspace=None):
+    """Gradients of linear_prefill(q, k, v, decay, state) for dL/do = dout [B, H, N, d] and
+    dL/dS_out = dstate_out ([B, H, d, d] fp32 or None).  Returns (dq, dk, dv, dstate_in or None)."""
+    B, H, N, d = _check_linear(q, k, v, decay, state, None, None)
+    _want(dout, "dout", q.shape, q.dtype)
+    _want(dstate_out, "dstate_out", (B, H, d, d), torch.float32)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, name, q.shape, q.dtype)
+    _dev(q, k, v, dout, decay, state, dstate_out, dq, dk, dv, workspace)
+    chunk = chunk or (64 if d == 64 else 128)
+    dt = _code(q)
+    dq = _empty_like(q) if dq is None else dq
+    dk = _empty_like(q) if dk is None else dk
+    dv = _empty_like(q) if dv is None else dv
+    dsi = _empty((B, H, d, d), torch.float32, q.device) if want_dstate else None
+    nb = workspace_bytes("linear_prefill", dtype=dt, B=B, H=H, N=N, d=d, chunk=chunk)
+    ws = _ws(nb, workspace, q)
+    call("sala_linear_prefill_backward", dt, B, H, N, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(decay),
+         _ptr(state), _ptr(dstate_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsi), _ptr(ws), nb, _stream())
+    return dq, dk, dv, dsi
 
 
 def linear_decode(q, k, v, state, decay=None, *, out=None):

@@ -17,6 +17,8 @@ _i, _p, _f, _z, _ll = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_si
 _SIGS = {
     "sala_linear_prefill": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_linear_prefill_workspace": (_z, [_i, _i, _i, _i, _i, _i]),
+    "sala_linear_prefill_backward": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z,
+                                          _p]),
     "sala_linear_decode": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
     "sala_linear_prefill_fused": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _f, _f, _ll,
                                        _p, _p, _z, _p]),

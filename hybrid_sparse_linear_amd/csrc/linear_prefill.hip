@@ -24,6 +24,18 @@
 //           The last segment writes S_out.
 // fp32 path: lin_recurrent_f32 runs the recurrence S_t = lam S_{t-1} + k_t v_t^T,
 // o_t = q_t S_t token by token with one thread per d_v column (small shapes).
+//
+// Backward (sala_linear_prefill_backward).  For dO = dL/do and dS = dL/dS_out,
+//   dQ    = ((dO V^T) * D) K + diag(lam^(t+1)) dO S_in^T
+//   dK    = ((dO V^T) * D)^T Q + diag(lam^(N-1-s)) V dS^T
+//   dV    = ((Q K^T) * D)^T dO + diag(lam^(N-1-s)) K dS
+//   dS_in = Q^T diag(lam^(t+1)) dO + lam^N dS
+// (D the decayed causal mask).  The first is this same forward operation on
+// (dO, V, K) with initial state S_in^T.  The other two are the forward
+// operation on the time-reversed sequence -- (V, dO, Q) and (K, Q, dO) -- whose
+// initial state dS^T / dS enters one decay step later (weight lam^r on
+// reversed row r instead of lam^(r+1)); dS_in is lam times the final state of
+// the (K, Q, dO) pass.  So every kernel below takes the switches of LinDir.
 
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
@@ -68,6 +80,16 @@ struct LinCfg {
   }
 };
 
+// Switches of the backward passes (all zero for the forward operation):
+//   rev      tokens are read and written in reverse order (row N-1-t for t)
+//   lag      the initial state enters one decay step later: weight lam^t on row
+//            t (not lam^(t+1)) and lam^(t) in the states after it
+//   state_T  the initial state is read transposed (S[j][i] for S[i][j])
+//   scale    the final state is written multiplied by lam
+struct LinDir {
+  int rev, lag, state_T, scale;
+};
+
 // K and V rows live in LDS in their natural layout with 16-byte chunks XOR-
 // swizzled by row (fkv): conflict-free for the plain 16-byte reads of 16 rows
 // of one key pair and for the transposed reads (lds_read_tr).  S^T rows are
@@ -83,14 +105,15 @@ __device__ __forceinline__ u32x4 tr_frag(const char *lds, uint32_t base_k0, uint
 // each).  Rows at or past t_end load a clamped row; store_kv zeroes them.
 // Nothing here uses the loaded values, so the loads stay in flight until
 // store_kv of the next chunk step.
-template <int C, int D>
-__device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end,
+template <int C, int D, bool REV>
+__device__ __forceinline__ void load_kv(const uint16_t *kb, const uint16_t *vb, int tid, int c0, int t_end, int N,
                                         u32x4 (&xk)[LinCfg<C, D>::NSTG], u32x4 (&xv)[LinCfg<C, D>::NSTG]) {
   using Cf = LinCfg<C, D>;
   const int ch = tid % Cf::NCH;
 #pragma unroll
   for (int u = 0; u < Cf::NSTG; ++u) {
-    const int t = min(c0 + tid / Cf::NCH + Cf::RPP * u, t_end - 1);
+    int t = min(c0 + tid / Cf::NCH + Cf::RPP * u, t_end - 1);
+    if constexpr (REV) t = N - 1 - t;
     xk[u] = gload16(kb + (size_t)t * D + 8 * ch);
     xv[u] = gload16(vb + (size_t)t * D + 8 * ch);
   }
@@ -176,15 +199,16 @@ struct LinF {
   static constexpr uint32_t LDS = TRF + (D / 2) * 4;
 };
 
-// xr: buffer resource over one head's [N, D] rows
-template <int C, int D>
+// xr: buffer resource over one head's [N, D] rows (REV: row N-1-t holds token t)
+template <int C, int D, bool REV = false>
 __device__ __forceinline__ void load_rows_f(__amdgpu_buffer_rsrc_t xr, int tid, int c0, int t_end,
-                                            u32x4 (&x)[LinF<C, D>::NSF][2]) {
+                                            u32x4 (&x)[LinF<C, D>::NSF][2], int N = 0) {
   using F = LinF<C, D>;
   const uint32_t hc = tid % F::HC;
 #pragma unroll
   for (int u = 0; u < F::NSF; ++u) {
-    const uint32_t t = min(c0 + tid / F::HC + F::RPF * u, t_end - 1);
+    uint32_t t = min(c0 + tid / F::HC + F::RPF * u, t_end - 1);
+    if constexpr (REV) t = (uint32_t)(N - 1) - t;
     x[u][0] = bload16(xr, (t * D + 8 * hc) * 2u);
     x[u][1] = bload16(xr, (t * D + D / 2 + 8 * hc) * 2u);
   }
@@ -299,7 +323,7 @@ __device__ __forceinline__ void nb_row(const char *lds, int hc, bool norm, int w
 
 // ---------------------------------------------------------------- pass 1
 // F: k is normalised and rotated as it is staged (the fused form).
-template <int C, int D, bool F>
+template <int C, int D, bool F, bool REV>
 __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v,
                                                          const float *__restrict__ decay,
@@ -332,8 +356,8 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
     const int hc = tid % Fz::HC;
     const auto kr = buf_rsrc(kb, (uint32_t)N * D * 2u), vr = buf_rsrc(vb, (uint32_t)N * D * 2u);
     u32x4 xk[Fz::NSF][2], xv[Fz::NSF][2];
-    load_rows_f<C, D>(kr, tid, t_begin, t_end, xk);
-    load_rows_f<C, D>(vr, tid, t_begin, t_end, xv);
+    load_rows_f<C, D, REV>(kr, tid, t_begin, t_end, xk, N);
+    load_rows_f<C, D, REV>(vr, tid, t_begin, t_end, xv, N);
     for (int c0 = t_begin; c0 < t_end; c0 += C) {
       const int m = min(C, t_end - c0);
       __syncthreads();
@@ -351,21 +375,21 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
       if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
       __syncthreads();
       if (c0 + C < t_end) {
-        load_rows_f<C, D>(kr, tid, c0 + C, t_end, xk);
-        load_rows_f<C, D>(vr, tid, c0 + C, t_end, xv);
+        load_rows_f<C, D, REV>(kr, tid, c0 + C, t_end, xk, N);
+        load_rows_f<C, D, REV>(vr, tid, c0 + C, t_end, xv, N);
       }
       state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
     }
   } else {
     u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
-    load_kv<C, D>(kb, vb, tid, t_begin, t_end, xk, xv);
+    load_kv<C, D, REV>(kb, vb, tid, t_begin, t_end, N, xk, xv);
     for (int c0 = t_begin; c0 < t_end; c0 += C) {
       const int m = min(C, t_end - c0);
       __syncthreads();
       store_kv<C, D>(lds, tid, m, xk, xv);
       if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
       __syncthreads();
-      if (c0 + C < t_end) load_kv<C, D>(kb, vb, tid, c0 + C, t_end, xk, xv);
+      if (c0 + C < t_end) load_kv<C, D, REV>(kb, vb, tid, c0 + C, t_end, N, xk, xv);
       state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
     }
   }
@@ -378,22 +402,26 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
 
 // ---------------------------------------------------------------- pass 2
 // seg_state[bh][m] holds A_m for m < nseg-1 on entry, S_in(m) for every m on exit.
+// dir.state_T: state_in is read transposed; dir.lag: the initial state's first
+// transition decays by lam^(seg_len-1) (it enters one step late).
 __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_state,
                                                     const float *__restrict__ state_in,
-                                                    const float *__restrict__ decay, int H, int DD,
-                                                    int N, int seg_len, int nseg) {
+                                                    const float *__restrict__ decay, int H, int D, int DD,
+                                                    int N, int seg_len, int nseg, LinDir dir) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= DD) return;
   const int h = bh % H;
   const double lam = decay ? (double)decay[h] : 1.0;
   const float lam_seg = (float)pow(lam, (double)seg_len);
-  float s = state_in ? state_in[(size_t)bh * DD + e] : 0.f;
+  const float lam_first = dir.lag ? (float)pow(lam, (double)(seg_len - 1)) : lam_seg;
+  const int e_in = dir.state_T ? (e % D) * D + e / D : e;
+  float s = state_in ? state_in[(size_t)bh * DD + e_in] : 0.f;
   float *base = seg_state + (size_t)bh * nseg * DD + e;
   for (int m = 0; m < nseg; ++m) {
     const float a = (m + 1 < nseg) ? base[(size_t)m * DD] : 0.f;
     base[(size_t)m * DD] = s;
-    s = fmaf(lam_seg, s, a);
+    s = fmaf(m == 0 ? lam_first : lam_seg, s, a);
   }
 }
 
@@ -405,7 +433,9 @@ __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_stat
 // flight during it.  (Loading q straight into MFMA fragments reads each row
 // in 64-byte pieces; the row-wise staging is faster even with nothing to
 // apply.)
-template <int C, int D>
+// REV, dir: the backward passes' switches (LinDir); sin_T: seg_state is the
+// caller's initial state, to be read transposed (one segment with dir.state_T).
+template <int C, int D, bool REV>
 __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict__ q,
                                                       const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
@@ -413,7 +443,8 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
                                                       const float *__restrict__ decay,
                                                       const float *__restrict__ seg_state,
                                                       size_t seg_stride, float *__restrict__ state_out,
-                                                      int H, int N, int seg_len, int nseg, NbK nb) {
+                                                      int H, int N, int seg_len, int nseg, NbK nb, LinDir dir,
+                                                      int sin_T) {
   using Cf = LinCfg<C, D>;
   using Fz = LinF<C, D>;
   __shared__ __attribute__((aligned(16))) char lds[Fz::LDS];
@@ -440,8 +471,13 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
 #pragma unroll
   for (int a = 0; a < Cf::SDV; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      Sacc[a][i] = sin ? sin[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const size_t r = 16 * sdk + 4 * g + i, c = 16 * (sdv0 + a) + lr;
+      Sacc[a][i] = sin ? sin[sin_T ? c * D + r : r * D + c] : 0.f;
+    }
+  // the initial state enters one decay step late (backward passes): in this
+  // segment's first chunk it is weighted lam^qq and decays by lam^(m-1)
+  bool lag_chunk = dir.lag && seg == 0;
 
   // Q fragment s (B operand of Q^T, query tile qt): read from the staged Q
   // rows in LDS at each use
@@ -452,7 +488,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   // this lane's output row, gated by gv when given
   auto store_out = [&](int c0, int m, const f32x4 (&Oacc)[Cf::DVW], const u32x2 (&gv)[Cf::DVW], bool gated) {
     if (qq < m) {
-      uint16_t *orow = ob + (size_t)(c0 + qq) * D;
+      uint16_t *orow = ob + (size_t)(REV ? N - 1 - (c0 + qq) : c0 + qq) * D;
 #pragma unroll
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
         f32x4 x = Oacc[dvi];
@@ -476,9 +512,9 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   const auto gr = buf_rsrc(nb.gate ? nb.gate + head_off : qb, head_bytes);
   nb_tables<C, D>(lds, tid, nb);
   const bool norm_q = nb.gq != nullptr, norm_k = nb.gk != nullptr, rope = nb.rope_base > 0.f;
-  load_rows_f<C, D>(kr, tid, t_begin, t_end, xk);
-  load_rows_f<C, D>(vr, tid, t_begin, t_end, xv);
-  load_rows_f<C, D>(qr, tid, t_begin, t_end, xq);
+  load_rows_f<C, D, REV>(kr, tid, t_begin, t_end, xk, N);
+  load_rows_f<C, D, REV>(vr, tid, t_begin, t_end, xv, N);
+  load_rows_f<C, D, REV>(qr, tid, t_begin, t_end, xq, N);
 
   for (int c0 = t_begin; c0 < t_end; c0 += C) {
     const int m = min(C, t_end - c0);
@@ -508,8 +544,8 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
     if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
     __syncthreads();
     if (c0 + C < t_end) {
-      load_rows_f<C, D>(kr, tid, c0 + C, t_end, xk);
-      load_rows_f<C, D>(vr, tid, c0 + C, t_end, xv);
+      load_rows_f<C, D, REV>(kr, tid, c0 + C, t_end, xk, N);
+      load_rows_f<C, D, REV>(vr, tid, c0 + C, t_end, xv, N);
     }
 
     // (1) O^T = lam^(qq+1) * S^T Q^T for d_v tiles dvb .. of this wave's query tile
@@ -527,7 +563,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
       }
     }
     {
-      const float f = pw[qq + 1];
+      const float f = pw[lag_chunk ? qq : qq + 1];
 #pragma unroll
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi] *= f;
     }
@@ -567,64 +603,72 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
     // gate values of this lane's outputs (a clamped row is never stored)
     u32x2 gv[Cf::DVW] = {};
     if (nb.gate) {
-      const uint32_t t = min(c0 + qq, t_end - 1);
+      uint32_t t = min(c0 + qq, t_end - 1);
+      if constexpr (REV) t = (uint32_t)(N - 1) - t;
 #pragma unroll
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) gv[dvi] = bload8(gr, (t * D + 16 * (dvb + dvi) + 4 * g) * 2u);
     }
-    if (c0 + C < t_end) load_rows_f<C, D>(qr, tid, c0 + C, t_end, xq);
+    if (c0 + C < t_end) load_rows_f<C, D, REV>(qr, tid, c0 + C, t_end, xq, N);
     // (5) S = lam^m S + (diag(lam^(m-1-j)) K)^T V, then (4) the (gated) output row
-    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+    state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[lag_chunk ? m - 1 : m], Sacc);
     store_out(c0, m, Oacc, gv, nb.gate != nullptr);
+    lag_chunk = false;
   }
 
   if (state_out && seg == nseg - 1) {
     float *so = state_out + (size_t)bh * D * D;
+    const float f = dir.scale ? lam : 1.f;
 #pragma unroll
     for (int a = 0; a < Cf::SDV; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) so[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] = Sacc[a][i];
+      for (int i = 0; i < 4; ++i) so[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] = Sacc[a][i] * f;
   }
 }
 
 // ---------------------------------------------------------------- fp32 path
 // One workgroup per (b, h); thread = one d_v column of the state.
+// dir: the backward passes' switches (LinDir).
 template <int D>
 __global__ __launch_bounds__(D) void lin_recurrent_f32(const float *__restrict__ q, const float *__restrict__ k,
                                                        const float *__restrict__ v, float *__restrict__ o,
                                                        const float *__restrict__ decay,
                                                        const float *__restrict__ state_in,
-                                                       float *__restrict__ state_out, int H, int N) {
+                                                       float *__restrict__ state_out, int H, int N, LinDir dir) {
   constexpr int T = 32;  // tokens staged per step
   __shared__ float qs[T][D];
   __shared__ float ks[T][D];
   const int bh = blockIdx.x, h = bh % H, col = threadIdx.x;
   const float lam = decay ? decay[h] : 1.f;
   const size_t off = (size_t)bh * N * D;
+  auto row = [&](int t) -> size_t { return (size_t)(dir.rev ? N - 1 - t : t); };
   float S[D];
 #pragma unroll
-  for (int r = 0; r < D; ++r) S[r] = state_in ? state_in[(size_t)bh * D * D + (size_t)r * D + col] : 0.f;
+  for (int r = 0; r < D; ++r)
+    S[r] = state_in ? state_in[(size_t)bh * D * D + (dir.state_T ? (size_t)col * D + r : (size_t)r * D + col)] : 0.f;
   for (int t0 = 0; t0 < N; t0 += T) {
     const int nt = min(T, N - t0);
     __syncthreads();
     for (int i = col; i < nt * D; i += D) {
-      qs[i / D][i % D] = q[off + (size_t)t0 * D + i];
-      ks[i / D][i % D] = k[off + (size_t)t0 * D + i];
+      qs[i / D][i % D] = q[off + row(t0 + i / D) * D + i % D];
+      ks[i / D][i % D] = k[off + row(t0 + i / D) * D + i % D];
     }
     __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
-      const float vv = v[off + (size_t)(t0 + tt) * D + col];
+      const float vv = v[off + row(t0 + tt) * D + col];
+      const float lt = (dir.lag && t0 + tt == 0) ? 1.f : lam;  // a late initial state is not decayed at token 0
       float acc = 0.f;
 #pragma unroll
       for (int r = 0; r < D; ++r) {
-        S[r] = fmaf(lam, S[r], ks[tt][r] * vv);
+        S[r] = fmaf(lt, S[r], ks[tt][r] * vv);
         acc = fmaf(qs[tt][r], S[r], acc);
       }
-      o[off + (size_t)(t0 + tt) * D + col] = acc;
+      o[off + row(t0 + tt) * D + col] = acc;
     }
   }
   if (state_out) {
+    const float f = dir.scale ? lam : 1.f;
 #pragma unroll
-    for (int r = 0; r < D; ++r) state_out[(size_t)bh * D * D + (size_t)r * D + col] = S[r];
+    for (int r = 0; r < D; ++r) state_out[(size_t)bh * D * D + (size_t)r * D + col] = S[r] * f;
   }
 }
 
@@ -640,12 +684,13 @@ void seg_plan(int BH, int N, int C, int *seg_len, int *nseg) {
   *nseg = (N + *seg_len - 1) / *seg_len;
 }
 
-template <int C, int D>
+template <int C, int D, bool REV>
 hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   NbK nb{nullptr, nullptr, 0.f, 0.f, 0, nullptr};
   if (a.nb)
     nb = NbK{a.nb->gamma_q, a.nb->gamma_k, a.nb->eps, a.nb->rope_base, a.nb->pos0,
              static_cast<const uint16_t *>(a.nb->gate)};
+  const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
   const bool k_transformed = nb.gk != nullptr || nb.rope_base > 0.f;
   const int BH = a.B * a.H;
   int seg_len, nseg;
@@ -653,21 +698,28 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   float *ws = static_cast<float *>(a.ws);
   const size_t DD = (size_t)D * D;
   const float *seg_state = a.state_in;  // nseg == 1: segment 0 starts from state_in
+  int sin_T = a.state_T;
   if (nseg > 1) {
     if (k_transformed)
-      hipLaunchKernelGGL((lin_seg_aggregate<C, D, true>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
+      hipLaunchKernelGGL((lin_seg_aggregate<C, D, true, REV>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
                          (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
     else
-      hipLaunchKernelGGL((lin_seg_aggregate<C, D, false>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
+      hipLaunchKernelGGL((lin_seg_aggregate<C, D, false, REV>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
                          (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws,
-                       a.state_in, a.decay, a.H, (int)DD, a.N, seg_len, nseg);
+                       a.state_in, a.decay, a.H, D, (int)DD, a.N, seg_len, nseg, dir);
     seg_state = ws;
+    sin_T = 0;  // the scan wrote the segment states in the plain layout
   }
-  hipLaunchKernelGGL((lin_seg_output<C, D>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
+  hipLaunchKernelGGL((lin_seg_output<C, D, REV>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, DD,
-                     a.state_out, a.H, a.N, seg_len, nseg, nb);
+                     a.state_out, a.H, a.N, seg_len, nseg, nb, dir, sin_T);
   return hipGetLastError();
+}
+
+template <int C, int D>
+hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+  return a.rev ? run_bf16<C, D, true>(a, st) : run_bf16<C, D, false>(a, st);
 }
 
 }  // namespace
@@ -682,20 +734,47 @@ size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk
 
 hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st) {
   if (a.dtype == 0) {
+    const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
     if (a.d == 64)
       hipLaunchKernelGGL(lin_recurrent_f32<64>, dim3(a.B * a.H), dim3(64), 0, st, (const float *)a.q,
                          (const float *)a.k, (const float *)a.v, (float *)a.o, a.decay, a.state_in, a.state_out,
-                         a.H, a.N);
+                         a.H, a.N, dir);
     else
       hipLaunchKernelGGL(lin_recurrent_f32<128>, dim3(a.B * a.H), dim3(128), 0, st, (const float *)a.q,
                          (const float *)a.k, (const float *)a.v, (float *)a.o, a.decay, a.state_in, a.state_out,
-                         a.H, a.N);
+                         a.H, a.N, dir);
     return hipGetLastError();
   }
   if (a.chunk == 128 && a.d == 128) return run_bf16<128, 128>(a, st);
   if (a.chunk == 64 && a.d == 128) return run_bf16<64, 128>(a, st);
   if (a.chunk == 128 && a.d == 64) return run_bf16<128, 64>(a, st);
   return run_bf16<64, 64>(a, st);
+}
+
+// Gradients of the linear layer through three passes of the forward
+// operation (see the header comment): dQ on (dO, V, K) from S_in^T; dK on the
+// reversed (V, dO, Q) from a late dS^T; dV on the reversed (K, Q, dO) from a
+// late dS, whose final state times lam is dS_in.  The passes run in order on
+// `st` and share the workspace.
+hipError_t launch_linear_prefill_backward(const LinearBackwardArgs &a, hipStream_t st) {
+  LinearPrefillArgs pq{a.dtype, a.B, a.H, a.N, a.d, a.chunk, a.dout, a.v, a.k, a.dq, a.decay, a.state_in,
+                       nullptr, a.ws, nullptr};
+  pq.state_T = 1;
+  hipError_t e = launch_linear_prefill(pq, st);
+  if (e != hipSuccess) return e;
+  LinearPrefillArgs pk{a.dtype, a.B, a.H, a.N, a.d, a.chunk, a.v, a.dout, a.q, a.dk, a.decay, a.dstate_out,
+                       nullptr, a.ws, nullptr};
+  pk.rev = 1;
+  pk.lag = 1;
+  pk.state_T = 1;
+  e = launch_linear_prefill(pk, st);
+  if (e != hipSuccess) return e;
+  LinearPrefillArgs pv{a.dtype, a.B, a.H, a.N, a.d, a.chunk, a.k, a.q, a.dout, a.dv, a.decay, a.dstate_out,
+                       a.dstate_in, a.ws, nullptr};
+  pv.rev = 1;
+  pv.lag = 1;
+  pv.scale_final = 1;
+  return launch_linear_prefill(pv, st);
 }
 
 }  // namespace sala

@@ -118,6 +118,42 @@ int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk, const 
   return hip_status(sala::launch_linear_prefill(a, static_cast<hipStream_t>(stream)), "sala_linear_prefill launch");
 }
 
+int sala_linear_prefill_backward(int dtype, int B, int H, int N, int d, int chunk, const void *q, const void *k,
+                                 const void *v, const void *dout, const float *decay, const float *state_in,
+                                 const float *dstate_out, void *dq, void *dk, void *dv, float *dstate_in, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(B >= 1 && H >= 1 && N >= 1, SALA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if ((s = check_d(d))) return s;
+  REQUIRE(chunk == 64 || chunk == 128, SALA_ERR_UNSUPPORTED, "chunk = %d: libsala supports 64 and 128", chunk);
+  REQUIRE(dtype != SALA_BF16 || (long long)N * d * 2 < (1ll << 31), SALA_ERR_UNSUPPORTED,
+          "one head's rows must stay under 2 GiB");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(dout, "dout");
+  REQUIRE_PTR(dq, "dq");
+  REQUIRE_PTR(dk, "dk");
+  REQUIRE_PTR(dv, "dv");
+  OPT_PTR(decay, "decay");
+  OPT_PTR(state_in, "state_in");
+  OPT_PTR(dstate_out, "dstate_out");
+  OPT_PTR(dstate_in, "dstate_in");
+  const void *ins[] = {q, k, v, dout};
+  const void *outs[] = {dq, dk, dv};
+  for (const void *o : outs)
+    for (const void *i : ins) REQUIRE(o != i, SALA_ERR_INVALID_ARG, "dq, dk, dv must not overlap q, k, v or dout");
+  REQUIRE(dq != dk && dq != dv && dk != dv, SALA_ERR_INVALID_ARG, "dq, dk and dv must be distinct buffers");
+  REQUIRE(!dstate_in || (dstate_in != state_in && dstate_in != dstate_out), SALA_ERR_INVALID_ARG,
+          "dstate_in must not overlap state_in or dstate_out");
+  if ((s = check_ws(ws, ws_bytes, sala::linear_prefill_workspace(dtype, B, H, N, d, chunk)))) return s;
+  sala::LinearBackwardArgs a{dtype, B, H, N, d, chunk, q, k, v, dout, decay, state_in, dstate_out, dq, dk, dv,
+                             dstate_in, ws};
+  return hip_status(sala::launch_linear_prefill_backward(a, static_cast<hipStream_t>(stream)),
+                    "sala_linear_prefill_backward launch");
+}
+
 int sala_linear_decode(int dtype, int B, int H, int d, const void *q, const void *k, const void *v, void *o,
                        const float *decay, float *state, void *stream) {
   int s;

@@ -29,9 +29,24 @@ struct LinearPrefillArgs {
   float *state_out;
   void *ws;
   const LinearNeighbours *nb;  // nullptr: the plain layer
+  // the backward passes' switches (0 for the forward operation): tokens in
+  // reverse order; initial state entering one decay step late; initial state
+  // read transposed; final state written times lam
+  int rev = 0, lag = 0, state_T = 0, scale_final = 0;
 };
 size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk);
 hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st);
+
+struct LinearBackwardArgs {
+  int dtype, B, H, N, d, chunk;
+  const void *q, *k, *v, *dout;
+  const float *decay, *state_in, *dstate_out;
+  void *dq, *dk, *dv;
+  float *dstate_in;
+  void *ws;
+};
+// Workspace: the same as the forward operation's (the passes run in turn).
+hipError_t launch_linear_prefill_backward(const LinearBackwardArgs &a, hipStream_t st);
 
 struct QkNormRopeArgs {
   int dtype, B, H, N, d;

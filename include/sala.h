@@ -92,6 +92,38 @@ int sala_linear_prefill(int dtype, int B, int H, int N, int d, int chunk,
 size_t sala_linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk);
 
 /* ------------------------------------------------------------------------
+ * sala_linear_prefill_backward -- gradients of sala_linear_prefill, for the
+ * continual training by which the hybrid model is obtained from a pretrained
+ * Transformer (MiniCPM-SALA abstract, "cost-effective continual training
+ * framework"; gist.science (ja) 技術概要 section 2.3; gist.science (de)
+ * section 2, "Trainingsstrategie").  For a loss L with dout = dL/do and
+ * dstate_out = dL/dS_out (lam = decay[h], D[t,s] = lam^(t-s) for s <= t):
+ *   dq       = ((dO V^T) * D) K + diag(lam^(t+1)) dO S_in^T
+ *   dk       = ((dO V^T) * D)^T Q + diag(lam^(N-1-s)) V dS_out^T
+ *   dv       = ((Q K^T) * D)^T dO + diag(lam^(N-1-s)) K dS_out
+ *   dstate_in = Q^T diag(lam^(t+1)) dO + lam^N dS_out
+ * the chain rule through the definition above (no approximation).
+ *
+ *   dtype, B, H, N, d, chunk, decay, state_in: as for sala_linear_prefill
+ *                (the forward call's arguments).
+ *   q, k, v      [B, H, N, d] of dtype: the forward call's inputs.
+ *   dout         [B, H, N, d] of dtype: dL/do.
+ *   dstate_out   [B, H, d, d] fp32 or NULL (L does not depend on S_out).
+ *   dq, dk, dv   [B, H, N, d] of dtype (outputs); none may overlap q, k, v
+ *                or dout.
+ *   dstate_in    [B, H, d, d] fp32 or NULL (output, dL/dS_in).
+ *   ws, ws_bytes at least sala_linear_prefill_workspace(...) bytes for the
+ *                same arguments (three passes run in turn and share it).
+ * Errors as sala_linear_prefill; an output equal to an input pointer:
+ * SALA_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------ */
+int sala_linear_prefill_backward(int dtype, int B, int H, int N, int d, int chunk,
+                                 const void *q, const void *k, const void *v, const void *dout,
+                                 const float *decay, const float *state_in, const float *dstate_out,
+                                 void *dq, void *dk, void *dv, float *dstate_in,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * sala_linear_decode -- one token of the same recurrence:
  *   S <- lam S + k v^T ;  o = q S        (state updated in place)
  *
