@@ -15,6 +15,7 @@ Entry points (same names as the C ABI, without the ``sala_`` prefix):
   linear_decode    one token of the same recurrence (state updated in place)
   sparse_select    pooled block scores and top-k block selection
   sparse_prefill   softmax attention over the selected blocks
+  sparse_prefill_backward  its gradients (dq, dk, dv) at a fixed selection
   sparse_decode    one query token against the selected cached blocks
   dense_prefill    plain causal attention (the full-attention comparison)
   ceiling_mfma / ceiling_copy   microkernels measuring this GPU's ceilings
@@ -36,7 +37,7 @@ from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 
 __all__ = ["linear_prefill", "linear_prefill_backward", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
            "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_decode_step_noalloc", "sparse_select",
-           "sparse_prefill", "sparse_decode",
+           "sparse_prefill", "sparse_prefill_backward", "sparse_decode",
            "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
 
 POISON_INT32 = -123456789
@@ -130,6 +131,7 @@ _WS_OPS = {
     "sparse_prefill_chunk": (4, ("dtype", "B", "Hq", "Hkv", "capacity", "d", "n", "block", "topk", "n_init",
                                  "n_local")),
     "sparse_decode_step": (5, ("dtype", "B", "Hq", "Hkv", "capacity", "d", "block", "topk", "n_init", "n_local")),
+    "sparse_prefill_backward": (6, ("dtype", "B", "Hq", "Hkv", "N", "d", "block", "n_sel")),
 }
 
 
@@ -369,6 +371,32 @@ def sparse_prefill(q, k, v, idx, *, block=64, scale=None, out=None, workspace=No
     call("sala_sparse_prefill", dt, B, Hq, Hkv, N, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v),
          _ptr(idx), _ptr(o), _ptr(ws), nb, _stream())
     return o
+
+
+def sparse_prefill_backward(q, k, v, idx, dout, *, block=64, scale=None, dq=None, dk=None, dv=None,
+                            workspace=None):
+    """Gradients (dq, dk, dv) of sparse_prefill(q, k, v, idx) for dL/do = dout, at the
+    fixed selection idx (bf16)."""
+    B, Hq, N, d = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[1]
+    _want(k, "k", (B, Hkv, N, d), q.dtype)
+    _want(v, "v", (B, Hkv, N, d), q.dtype)
+    _want(dout, "dout", q.shape, q.dtype)
+    _want(dq, "dq", q.shape, q.dtype)
+    _want(dk, "dk", k.shape, k.dtype)
+    _want(dv, "dv", k.shape, k.dtype)
+    n_sel = _check_idx(idx, (B, Hkv, (N + block - 1) // block))
+    _dev(q, k, v, idx, dout, dq, dk, dv, workspace)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _code(q)
+    dq = _empty_like(q) if dq is None else dq
+    dk = _empty_like(k) if dk is None else dk
+    dv = _empty_like(k) if dv is None else dv
+    nb = workspace_bytes("sparse_prefill_backward", dtype=dt, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, block=block, n_sel=n_sel)
+    ws = _ws(nb, workspace, q)
+    call("sala_sparse_prefill_backward", dt, B, Hq, Hkv, N, d, block, n_sel, ctypes.c_float(scale), _ptr(q), _ptr(k),
+         _ptr(v), _ptr(idx), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nb, _stream())
+    return dq, dk, dv
 
 
 def sparse_decode(q, k_cache, v_cache, idx, *, L=None, block=64, scale=None, out=None, workspace=None):

@@ -39,6 +39,9 @@ _SIGS = {
     "sala_sparse_prefill_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_sparse_decode": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _z, _p]),
     "sala_sparse_decode_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "sala_sparse_prefill_backward": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z,
+                                          _p]),
+    "sala_sparse_prefill_backward_workspace": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sala_dense_prefill": (_i, [_i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p]),
     "sala_ceiling_mfma": (_i, [_i, _i, _p, _p]),
     "sala_ceiling_copy": (_i, [_p, _p, _z, _p]),

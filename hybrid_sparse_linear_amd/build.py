@@ -27,6 +27,7 @@ SOURCES = [
     "sparse_decode.hip",
     "ceilings.hip",
     "noalloc.hip",
+    "sparse_backward.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

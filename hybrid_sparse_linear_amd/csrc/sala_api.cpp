@@ -311,6 +311,43 @@ int sala_sparse_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, int blo
   return hip_status(sala::launch_sparse_prefill(a, static_cast<hipStream_t>(stream)), "sala_sparse_prefill launch");
 }
 
+size_t sala_sparse_prefill_backward_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || block != 64 || (d != 64 && d != 128) || n_sel < 1 || n_sel > 1024)
+    return 0;
+  return sala::sparse_backward_workspace(dtype, B, Hq, Hkv, N, d, block, n_sel);
+}
+
+int sala_sparse_prefill_backward(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel, float scale,
+                                 const void *q, const void *k, const void *v, const int32_t *idx, const void *dout,
+                                 void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_dtype(dtype))) return s;
+  REQUIRE(dtype == SALA_BF16, SALA_ERR_UNSUPPORTED, "sala_sparse_prefill_backward supports SALA_BF16 only");
+  if ((s = check_sparse_common(B, Hq, Hkv, block, n_sel, "n_sel"))) return s;
+  if ((s = check_d(d))) return s;
+  REQUIRE(N >= 1, SALA_ERR_INVALID_ARG, "N must be >= 1");
+  REQUIRE(n_sel >= 1 && n_sel <= 1024, SALA_ERR_UNSUPPORTED, "n_sel = %d must be in [1, 1024]", n_sel);
+  REQUIRE((long long)N * d * 2 < (1ll << 31), SALA_ERR_UNSUPPORTED, "one head's rows must stay under 2 GiB");
+  REQUIRE(scale == scale, SALA_ERR_INVALID_ARG, "scale is NaN");
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(idx, "idx");
+  REQUIRE_PTR(dout, "dout");
+  REQUIRE_PTR(dq, "dq");
+  REQUIRE_PTR(dk, "dk");
+  REQUIRE_PTR(dv, "dv");
+  const void *ins[] = {q, k, v, idx, dout};
+  const void *outs[] = {dq, dk, dv};
+  for (const void *x : outs)
+    for (const void *y : ins) REQUIRE(x != y, SALA_ERR_INVALID_ARG, "dq, dk, dv must not overlap an input");
+  REQUIRE(dq != dk && dq != dv && dk != dv, SALA_ERR_INVALID_ARG, "dq, dk and dv must be distinct buffers");
+  if ((s = check_ws(ws, ws_bytes, sala::sparse_backward_workspace(dtype, B, Hq, Hkv, N, d, block, n_sel)))) return s;
+  sala::SparseBackwardArgs a{dtype, B, Hq, Hkv, N, d, block, n_sel, scale, q, k, v, idx, dout, dq, dk, dv, ws};
+  return hip_status(sala::launch_sparse_backward(a, static_cast<hipStream_t>(stream)),
+                    "sala_sparse_prefill_backward launch");
+}
+
 int sala_dense_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, float scale, const void *q, const void *k,
                        const void *v, void *o, void *stream) {
   int s;
@@ -510,9 +547,9 @@ int sala_sparse_prefill_chunk(int dtype, int B, int Hq, int Hkv, int capacity, i
 }
 
 size_t sala_workspace_bytes(int op, const int64_t *dims, int ndims) {
-  static const int nargs[] = {6, 11, 8, 8, 11, 10};
+  static const int nargs[] = {6, 11, 8, 8, 11, 10, 8};
   const size_t bad = (size_t)-1;
-  if (op < SALA_OP_LINEAR_PREFILL || op > SALA_OP_SPARSE_DECODE_STEP) {
+  if (op < SALA_OP_LINEAR_PREFILL || op > SALA_OP_SPARSE_PREFILL_BACKWARD) {
     fail(SALA_ERR_INVALID_ARG, "unknown operation %d", op);
     return bad;
   }
@@ -538,8 +575,10 @@ size_t sala_workspace_bytes(int op, const int64_t *dims, int ndims) {
     case SALA_OP_SPARSE_DECODE: return sala_sparse_decode_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]);
     case SALA_OP_SPARSE_PREFILL_CHUNK:
       return sala_sparse_prefill_chunk_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], a[10]);
-    default:
+    case SALA_OP_SPARSE_DECODE_STEP:
       return sala_sparse_decode_step_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9]);
+    default:
+      return sala_sparse_prefill_backward_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]);
   }
 }
 

@@ -113,6 +113,18 @@ struct SparseDecodeArgs {
 size_t sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel);
 hipError_t launch_sparse_decode(const SparseDecodeArgs &a, hipStream_t st);
 
+struct SparseBackwardArgs {
+  int dtype, B, Hq, Hkv, N, d, block, n_sel;
+  float scale;
+  const void *q, *k, *v;
+  const int32_t *idx;
+  const void *dout;
+  void *dq, *dk, *dv;
+  void *ws;
+};
+size_t sparse_backward_workspace(int dtype, int B, int Hq, int Hkv, int N, int d, int block, int n_sel);
+hipError_t launch_sparse_backward(const SparseBackwardArgs &a, hipStream_t st);
+
 // Dense causal attention (every block up to the query's own): the sparse
 // kernel with the block list replaced by 0..i.
 hipError_t launch_dense_prefill(const SparsePrefillArgs &a, hipStream_t st);

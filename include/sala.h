@@ -331,6 +331,41 @@ size_t sala_sparse_prefill_workspace(int dtype, int B, int Hq, int Hkv, int N, i
                                      int block, int n_sel);
 
 /* ------------------------------------------------------------------------
+ * sala_sparse_prefill_backward -- gradients of sala_sparse_prefill at a fixed
+ * selection, for the continual training by which the hybrid is obtained
+ * from a pretrained Transformer (MiniCPM-SALA abstract; gist.science (ja)
+ * 技術概要 section 2.3; gist.science (de) section 2, "Trainingsstrategie").
+ * With p the softmax of row t over A(t), o_t its output, dO = dL/do and
+ * D_t = dO_t . o_t:
+ *   ds_s = p_s (dO_t . v_s - D_t)
+ *   dq_t = scale sum_{s in A(t)} ds_s k_s
+ *   dk_s = scale sum over (t, hq) with s in A(t) of ds_s q_t  (all G heads)
+ *   dv_s =       sum over (t, hq) with s in A(t) of p_s dO_t
+ * The block selection is a top-k and passes no gradient.
+ *
+ *   dtype        SALA_BF16 (SALA_ERR_UNSUPPORTED otherwise).
+ *   B, Hq, Hkv, N, d, block, n_sel, scale, q, k, v, idx: the forward call's.
+ *   dout         [B, Hq, N, d]: dL/do.  D_t is formed from the recomputed fp32
+ *                probabilities, so the forward's output is not needed.
+ *   dq           [B, Hq, N, d]; dk, dv [B, Hkv, N, d] (outputs; every row is
+ *                written, rows of never-selected blocks with 0).  None may
+ *                overlap an input.
+ *   ws, ws_bytes at least sala_sparse_prefill_backward_workspace(...) bytes
+ *                (row statistics, the inverted selection and per-item fp32
+ *                partial sums of dk, dv; about 0.27 * B * Hkv * N * d * 4
+ *                bytes at the workloads' 67 selected blocks).
+ * Every sum runs in a fixed order: results repeat bit for bit.
+ * ------------------------------------------------------------------------ */
+int sala_sparse_prefill_backward(int dtype, int B, int Hq, int Hkv, int N, int d,
+                                 int block, int n_sel, float scale,
+                                 const void *q, const void *k, const void *v, const int32_t *idx,
+                                 const void *dout, void *dq, void *dk, void *dv,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+size_t sala_sparse_prefill_backward_workspace(int dtype, int B, int Hq, int Hkv, int N, int d,
+                                              int block, int n_sel);
+
+/* ------------------------------------------------------------------------
  * sala_dense_prefill -- plain causal softmax attention over every earlier
  * token (exact attention, the FlashAttention related-list entry): the
  * full-attention layer the sparse layer replaces, for the layer-level
@@ -389,6 +424,8 @@ int sala_ceiling_copy(const void *src, void *dst, size_t bytes, void *stream);
  *   SALA_OP_SPARSE_DECODE        dtype, B, Hq, Hkv, L, d, block, n_sel
  *   SALA_OP_SPARSE_PREFILL_CHUNK dtype, B, Hq, Hkv, capacity, d, n, block, topk, n_init, n_local
  *   SALA_OP_SPARSE_DECODE_STEP   dtype, B, Hq, Hkv, capacity, d, block, topk, n_init, n_local
+ *   SALA_OP_SPARSE_PREFILL_BACKWARD dtype, B, Hq, Hkv, N, d, block, n_sel
+ *   (sala_linear_prefill_backward uses SALA_OP_LINEAR_PREFILL's size)
  *
  * Returns the number of bytes (0: the call needs no workspace), or
  * (size_t)-1 when op is unknown, ndims does not match op, dims is NULL or a
@@ -400,7 +437,8 @@ typedef enum {
   SALA_OP_SPARSE_PREFILL = 2,
   SALA_OP_SPARSE_DECODE = 3,
   SALA_OP_SPARSE_PREFILL_CHUNK = 4,
-  SALA_OP_SPARSE_DECODE_STEP = 5
+  SALA_OP_SPARSE_DECODE_STEP = 5,
+  SALA_OP_SPARSE_PREFILL_BACKWARD = 6
 } sala_op;
 
 size_t sala_workspace_bytes(int op, const int64_t *dims, int ndims);

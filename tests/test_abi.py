@@ -269,6 +269,7 @@ def test_generic_workspace_query_matches_per_op_queries():
         (3, L.sala_sparse_decode_workspace, (BF16, 4, 32, 2, 1048576, 128, 64, 67)),
         (4, L.sala_sparse_prefill_chunk_workspace, (BF16, 2, 8, 2, 587, 128, 256, 64, 3, 1, 2)),
         (5, L.sala_sparse_decode_step_workspace, (BF16, 2, 8, 2, 587, 128, 64, 3, 1, 2)),
+        (6, L.sala_sparse_prefill_backward_workspace, (BF16, 1, 32, 2, 262144, 128, 64, 67)),
     ]
     for op, fn, dims in cases:
         arr = (ctypes.c_int64 * len(dims))(*dims)
@@ -276,7 +277,7 @@ def test_generic_workspace_query_matches_per_op_queries():
         assert L.sala_workspace_bytes(op, arr, len(dims)) == want, (op, dims)
     bad = ctypes.c_size_t(-1).value
     arr = (ctypes.c_int64 * 6)(BF16, 1, 2, 256, 128, 128)
-    assert L.sala_workspace_bytes(6 + 3, arr, 6) == bad and b"unknown operation" in L.sala_last_error()
+    assert L.sala_workspace_bytes(7 + 3, arr, 6) == bad and b"unknown operation" in L.sala_last_error()
     assert L.sala_workspace_bytes(-1, arr, 6) == bad
     assert L.sala_workspace_bytes(0, arr, 5) == bad and b"takes 6" in L.sala_last_error()
     assert L.sala_workspace_bytes(0, None, 6) == bad and b"NULL" in L.sala_last_error()
