@@ -141,6 +141,7 @@ def parse():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling microkernels")
     ap.add_argument("--no-neighbours", action="store_true", help="skip the fused / unfused neighbour comparison")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload entries")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradient (training) timings")
     ap.add_argument("--cpu-sample-seconds", type=float, default=8.0,
                     help="oracle time budget of each sampled part of the CPU baselines")
     return ap.parse_args()
@@ -517,6 +518,54 @@ def bench_workload3(torch, sala, I, budget, reps=10):
                                       f"at the end of the context, scaled to the layer")}
 
 
+def bench_backward(torch, sala, I, x, sp, idx, reps=3):
+    """The gradients of one linear layer and of the sparse layer at the group's
+    shapes (N=262144), for dL/do ~ N(0, 1/d): sala_linear_prefill_backward
+    (HBM-bound: q, k, v, dO read and dq, dk, dv written, 7 tensors of the layer's
+    size) and sala_sparse_prefill_backward at the forward's selection
+    (MFMA-bound: S, dP, dQ, dK and dV products, 10 d flops per (query row, key)
+    pair of the selection).  Mean of `reps` after a warmup."""
+    q, k, v = x["q"], x["k"], x["v"]
+    B, H, N, d = q.shape
+    do = I.normal((B, H, N, d), 4999, 1.0 / math.sqrt(d), I.BF16, "cuda")
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ws = torch.empty(max(1, sala.workspace_bytes("linear_prefill", dtype=1, B=B, H=H, N=N, d=d, chunk=128)),
+                     dtype=torch.uint8, device="cuda")
+    lin = lambda: sala.linear_prefill_backward(q, k, v, do, x["decay"], dq=grads[0], dk=grads[1],  # noqa: E731
+                                               dv=grads[2], want_dstate=False, workspace=ws)
+    lin()
+    ms_lin = events_ms(torch, lin, reps)
+    del grads, ws
+    sq, sk, sv = sp["q"], sp["k"], sp["v"]
+    Hq, Hkv = sq.shape[1], sk.shape[1]
+    sdo = I.normal(sq.shape, 5000, 1.0 / math.sqrt(d), I.BF16, "cuda")
+    sdq, sdk, sdv = torch.empty_like(sq), torch.empty_like(sk), torch.empty_like(sk)
+    sws = torch.empty(sala.workspace_bytes("sparse_prefill_backward", dtype=1, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d,
+                                           block=64, n_sel=idx.shape[-1]), dtype=torch.uint8, device="cuda")
+    spb = lambda: sala.sparse_prefill_backward(sq, sk, sv, idx, sdo, dq=sdq, dk=sdk, dv=sdv,  # noqa: E731
+                                               workspace=sws)
+    spb()
+    ms_sp = events_ms(torch, spb, reps)
+    lin_bytes = 7 * B * H * N * d * 2
+    sp_flops = sparse_flops(idx, N, d, Hq // Hkv) * 10.0 / 4.0  # forward's 4 d per pair -> 10 d
+    del sdo, sdq, sdk, sdv, sws, do
+    torch.cuda.empty_cache()
+    return {"workload": "gradients at the group shapes, N=%d: one linear layer (H=32, d=128, slope decay) and the "
+                        "sparse layer at its forward selection (Hq=32, Hkv=2, 67 blocks)" % N,
+            "linear_layer_ms": round(ms_lin, 3),
+            "linear_roofline": {"bound": "hbm", "achieved": round(lin_bytes / (ms_lin * 1e-3) / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(lin_bytes / (ms_lin * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+                                "algorithmic_bytes": lin_bytes},
+            "sparse_layer_ms": round(ms_sp, 3),
+            "sparse_roofline": {"bound": "mfma", "achieved": round(sp_flops / (ms_sp * 1e-3) / 1e12, 1),
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(sp_flops / (ms_sp * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                                "algorithmic_tflop": round(sp_flops / 1e12, 3)},
+            "group_backward_ms": round(3 * ms_lin + ms_sp, 3),
+            "timing": "HIP events, mean of %d after a warmup" % reps}
+
+
 def bench_decode(torch, sala, I, reps=20):
     """The 1M-context decode step (B=4): three linear decode steps, selection over
     16384 pooled blocks per (b, KV head), attention over the 67 selected blocks.
@@ -778,6 +827,8 @@ def main():
     if not args.no_neighbours:
         x0 = dict(lin[0], o=out_bufs["linear"][0], ws=ws["linear"][0])
         out["neighbours"] = bench_neighbours(torch, sala, I, x0, N)
+    if not args.no_backward:
+        out["backward"] = bench_backward(torch, sala, I, lin[0], sp, idx)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(lin, sp, idx, args.cpu_sample_seconds)

@@ -135,3 +135,23 @@ def test_sparse_backward_repeats_bit_for_bit():
     torch.cuda.synchronize()
     for x1, x2 in zip(a, b):
         assert torch.equal(x1, x2)
+
+
+def test_sparse_backward_workload_shape():
+    """The sparse workload's head group and input recipe (16 query heads on one KV
+    head, top-64 + 1 + 2, 5 % shifted key blocks) at N = 4480, so query blocks
+    past the 66th select 67 blocks, against the oracle's gradients; the GPU's
+    selection is fed in (the selection tests check it against the oracle's)."""
+    N = 64 * 70
+    say("sparse_prefill_backward workload shape", N)
+    x = I.sparse_inputs(1, 16, 1, N, 128, I.BF16, 3, 0, 1.0, shift_frac=0.05)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    do = I.normal((1, 16, N, 128), 122, 1.0, I.BF16)
+    idx, _ = sala.sparse_select(q, k)
+    dq, dk, dv = sala.sparse_prefill_backward(q, k, v, idx, dev(do))
+    torch.cuda.synchronize()
+    r = BW.sparse_attention_backward(host64(x["q"]), host64(x["k"]), host64(x["v"]), idx.cpu().numpy(), host64(do),
+                                     64)
+    assert_close(dq, r[0], I.BF16, "dq")
+    assert_close(dk, r[1], I.BF16, "dk", absolute_floor=False)
+    assert_close(dv, r[2], I.BF16, "dv", absolute_floor=False)
