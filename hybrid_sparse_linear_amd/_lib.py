@@ -4,7 +4,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsala.so")
+# SALA_LIB_PATH selects another build of the library (the sanitizer build of the ABI checks)
+LIB_PATH = os.environ.get("SALA_LIB_PATH") or os.path.join(_HERE, "libsala.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "sala.h")
 
 SALA_F32 = 0

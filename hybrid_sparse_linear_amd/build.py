@@ -73,5 +73,33 @@ def build(verbose=False, jobs=6, out=LIB, defines=()):
     return out
 
 
+def build_sanitized_abi(out_dir=None, verbose=False):
+    """The C-ABI layer (sala_api.cpp, host code only) compiled with the host's
+    AddressSanitizer and UndefinedBehaviorSanitizer by g++, linked with the
+    kernel objects of the last build(): a library whose argument validation can
+    be exercised on a machine without a GPU.  Load it with the ASan runtime
+    preloaded and SALA_LIB_PATH pointing at it.  Returns its path."""
+    out_dir = out_dir or os.path.join(BUILD, "sanitized")
+    os.makedirs(out_dir, exist_ok=True)
+    kernel_objs = [os.path.join(BUILD, os.path.basename(src) + ".o") for src in SOURCES if src != "sala_api.cpp"]
+    missing = [o for o in kernel_objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: missing {missing}")
+    obj = os.path.join(out_dir, "sala_api.o")
+    lib = os.path.join(out_dir, "libsala_sanitized.so")
+    compile_cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-fno-omit-frame-pointer",
+                   "-fsanitize=address,undefined", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+                   "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", os.path.join(CSRC, "sala_api.cpp"), "-o", obj]
+    link_cmd = ["g++", "-shared", "-o", lib, obj] + kernel_objs + ["-lasan", "-lubsan", "-L/opt/rocm/lib",
+                                                                   "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    for cmd in (compile_cmd, link_cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized build failed:\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
