@@ -322,6 +322,20 @@ __device__ __forceinline__ void nb_row(const char *lds, int hc, bool norm, int w
 }
 
 // ---------------------------------------------------------------- pass 1
+// A key s enters its segment's aggregate with weight lam^(t_end-1-s).  Keys
+// whose weight is below 2^-126 (fp32's smallest normal number) are left out:
+// their terms lie below fp32's range relative to the inputs, where the
+// weights themselves flush to zero a few steps later.  For a fast-decaying
+// head this skips all but the segment's last few chunks.  Returns the first
+// chunk start to process (always a chunk boundary of the segment).
+__device__ __forceinline__ int agg_first_row(float lam, int t_begin, int t_end, int C) {
+  const float a = fabsf(lam);
+  if (!(a < 1.f)) return t_begin;  // |lam| >= 1 (or NaN): every key counts
+  const double keep = a == 0.f ? 1.0 : ceil(126.0 / -log2((double)a)) + 1.0;
+  if (keep >= (double)(t_end - t_begin)) return t_begin;
+  return t_begin + ((t_end - t_begin - (int)keep) / C) * C;
+}
+
 // F: k is normalised and rotated as it is staged (the fused form).
 template <int C, int D, bool F, bool REV>
 __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restrict__ k,
@@ -335,10 +349,12 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int nagg = nseg - 1;
-  const int bh = blockIdx.x / nagg, seg = blockIdx.x % nagg;
+  // (b, h) from the last: with slope decays the later heads decay slowest and
+  // keep the most chunks, so the longest workgroups are dispatched first.
+  const int bh = (int)(gridDim.x / nagg) - 1 - (int)(blockIdx.x / nagg), seg = blockIdx.x % nagg;
   const int h = bh % H;
-  const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
   const float lam = decay ? decay[h] : 1.f;
+  const int t_end = min(N, (seg + 1) * seg_len), t_begin = agg_first_row(lam, seg * seg_len, t_end, C);
   float *pw = reinterpret_cast<float *>(lds + Cf::PW) + Cf::PWZ;  // pw[n] = lam^n, 0 for n < 0
   float *rw = reinterpret_cast<float *>(lds + Cf::RW);
   for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);

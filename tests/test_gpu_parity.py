@@ -56,6 +56,25 @@ def test_linear_prefill(case):
     assert_close(st, rs, torch.float32 if dt == I.F32 else I.BF16, "state")
 
 
+def test_linear_prefill_fast_decay_segments():
+    """128 heads of 4133 tokens (chunk 64, 8 segments of 9 chunks) with decays from
+    0 to 1: the aggregate pass leaves out keys whose weight lam^n is below 2^-126
+    (all but the last chunk or so of each segment for lam <= 0.43, none for
+    lam >= 0.9), and every output row, head and final state must still match."""
+    B, H, N, d, C = 4, 32, 4133, 128, 64
+    say("linear_prefill fast decays", B, H, N, d, C)
+    x = I.linear_inputs(B, H, N, d, I.BF16, 95, 3, 1.0 / math.sqrt(d))
+    decay = torch.tensor(([0.0, 0.05, 0.2, 0.43, 0.6, 0.8, 0.85, 0.9, 0.95, 0.99, 0.999, 1.0] * 3)[:H],
+                         dtype=torch.float32)
+    s0 = I.normal((B, H, d, d), 78, 1.0 / d)
+    o, st = sala.linear_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(decay), dev(s0), chunk=C)
+    torch.cuda.synchronize()
+    ro, rs = OL.linear_prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), decay.double().numpy(), host64(s0),
+                               form="chunked", chunk=C)
+    assert_close(o, ro, I.BF16, "o")
+    assert_close(st, rs, I.BF16, "state")
+
+
 def test_linear_prefill_large_inputs():
     """q, k, v ~ N(0, 0.25) -- four times the workloads' scale per factor -- over
     2085 tokens with lam = 1 (plain causal linear attention, outputs growing as
