@@ -566,6 +566,60 @@ def bench_backward(torch, sala, I, x, sp, idx, reps=3):
             "timing": "HIP events, mean of %d after a warmup" % reps}
 
 
+def decode_floors(torch, sala, flush, sink, reps):
+    """What the decode step's launches would cost if each only streamed its bytes:
+    per call, the same number of launches of the in-repo streaming microkernels,
+    each moving that kernel's bytes (a copy of the 8.4 MB of linear states, read
+    and written; a read of the 67.1 MB of pooled keys and an empty launch for the
+    selection's merge; reads of the 17.6 MB of selected K, V rows and of the
+    4.5 MB of partials for the attention), timed like the calls themselves."""
+    MB = 1 << 20
+    st_bytes = 4 * 32 * 128 * 128 * 4
+    sizes = {"linear_decode": [("copy", st_bytes)], "sparse_select": [("read", 4 * 2 * 16384 * 128 * 4), ("read", 0)],
+             "sparse_decode": [("read", 4 * 2 * 67 * 64 * 128 * 2 * 2), ("read", 4 * 32 * 67 * 130 * 4)]}
+    pool = torch.empty(2 * st_bytes + 96 * MB, dtype=torch.uint8, device="cuda")
+    out_f = torch.empty(96 * MB // 16384 + 1, dtype=torch.float32, device="cuda")
+    src_c, dst_c = pool[:st_bytes], pool[st_bytes:2 * st_bytes]
+    rd = pool[2 * st_bytes:]
+
+    def launches(name):
+        off = 0
+        for kind, nb in sizes[name]:
+            if kind == "copy":
+                sala.ceiling_copy(src_c, dst_c)
+            else:
+                sala.ceiling_read(rd[off:], out_f, nb)
+                off += (nb + MB - 1) // MB * MB
+    names = list(sizes)
+    per = {n: [] for n in names}
+    for _ in range(3):
+        for n in names:
+            launches(n)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        sink.add_(flush.sum())
+        sink.add_(flush.sum())
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 2)]
+        evs[0].record()
+        for n, name in enumerate(names):
+            launches(name)
+            evs[n + 1].record()
+        sala.ceiling_read(rd, out_f, 0)
+        evs[-1].record()
+        torch.cuda.synchronize()
+        for n, name in enumerate(names):
+            per[name].append(evs[n].elapsed_time(evs[n + 1]) * 1000.0)
+        per.setdefault("empty", []).append(evs[-2].elapsed_time(evs[-1]) * 1000.0)
+    med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
+    calls = {"linear_decode": med["linear_decode"], "sparse_select": med["sparse_select"],
+             "sparse_decode": med["sparse_decode"]}
+    return {"method": "streaming microkernels moving each call's bytes in as many launches as the call makes, "
+                      "timed like the calls (median of %d)" % reps,
+            "empty_launch_us": round(med["empty"], 2),
+            "calls_us": {k: round(v, 2) for k, v in calls.items()},
+            "us_per_step": round(3 * calls["linear_decode"] + calls["sparse_select"] + calls["sparse_decode"], 2)}
+
+
 def bench_decode(torch, sala, I, reps=20):
     """The 1M-context decode step (B=4): three linear decode steps, selection over
     16384 pooled blocks per (b, KV head), attention over the 67 selected blocks.
@@ -623,6 +677,7 @@ def bench_decode(torch, sala, I, reps=20):
             per[name].append(evs[n].elapsed_time(evs[n + 1]) * 1000.0)
     calls_us = {name: sorted(t)[len(t) // 2] for name, t in per.items()}
     us_kernels = sum(calls_us.values())
+    floors = decode_floors(torch, sala, flush, sink, reps)
     # the step is five short calls; launching them from Python one by one would
     # time the host, so the wall time comes from one replay of a captured graph
     graph = torch.cuda.CUDAGraph()
@@ -652,6 +707,8 @@ def bench_decode(torch, sala, I, reps=20):
            "timing": "kernels: median per call of HIP events between the calls with the GPU kept ahead of the host, "
                      "summed; wall: HIP events around one replay of the captured step, median of %d reps; 1 GiB read "
                      "between reps" % reps, "graph_replay_matches_eager": replay_ok}
+    floors["hbm_frac"] = frac(floors["us_per_step"])
+    out["floors"] = floors
 
     # The same step as a generation loop runs it: the linear layers with QK norm,
     # RoPE at position L-1 and the gate fused in, and the sparse layer appending

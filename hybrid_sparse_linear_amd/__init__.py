@@ -18,7 +18,7 @@ Entry points (same names as the C ABI, without the ``sala_`` prefix):
   sparse_prefill_backward  its gradients (dq, dk, dv) at a fixed selection
   sparse_decode    one query token against the selected cached blocks
   dense_prefill    plain causal attention (the full-attention comparison)
-  ceiling_mfma / ceiling_copy   microkernels measuring this GPU's ceilings
+  ceiling_mfma / ceiling_copy / ceiling_read   microkernels measuring this GPU's ceilings
   layer_group_prefill  three linear layers then one sparse layer, one stream
 
 Debugging: with the environment variable SALA_DEBUG_POISON=1, every output,
@@ -38,7 +38,7 @@ from ._lib import SALA_BF16, SALA_F32, SalaError, call, lib  # noqa: F401
 __all__ = ["linear_prefill", "linear_prefill_backward", "linear_decode", "linear_prefill_fused", "linear_decode_fused", "qk_norm_rope",
            "output_gate", "sparse_prefill_chunk", "sparse_decode_step", "sparse_decode_step_noalloc", "sparse_select",
            "sparse_prefill", "sparse_prefill_backward", "sparse_decode",
-           "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "SalaError"]
+           "dense_prefill", "layer_group_prefill", "workspace_bytes", "ceiling_mfma", "ceiling_copy", "ceiling_read", "SalaError"]
 
 POISON_INT32 = -123456789
 
@@ -543,6 +543,21 @@ def ceiling_copy(src, dst):
         raise ValueError("dst is smaller than src")
     _dev(src, dst)
     call("sala_ceiling_copy", _ptr(src), _ptr(dst), nbytes, _stream())
+
+
+def ceiling_read(src, out, nbytes=None):
+    """Launch the read-only streaming microkernel over the first nbytes of src
+    (default: all of it; 0: one workgroup that reads nothing).  out: fp32 with
+    at least nbytes // 16384 + 1 elements."""
+    total = src.numel() * src.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes < 0 or nbytes > total or nbytes % 16:
+        raise ValueError("nbytes must be a multiple of 16 within src")
+    _want(out, "out", (out.numel(),), torch.float32)
+    if out.numel() < nbytes // 16384 + 1:
+        raise ValueError("out is too small")
+    _dev(src, out)
+    call("sala_ceiling_read", _ptr(src), nbytes, _ptr(out), _stream())
 
 
 def layer_group_prefill(linear_layers, sparse_layer, *, block=64, topk=64, n_init=1, n_local=2, chunk=None,

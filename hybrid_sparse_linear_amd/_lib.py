@@ -46,6 +46,7 @@ _SIGS = {
     "sala_dense_prefill": (_i, [_i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p]),
     "sala_ceiling_mfma": (_i, [_i, _i, _p, _p]),
     "sala_ceiling_copy": (_i, [_p, _p, _z, _p]),
+    "sala_ceiling_read": (_i, [_p, _z, _p, _p]),
     "sala_workspace_bytes": (_z, [_i, ctypes.POINTER(ctypes.c_int64), _i]),
     "sala_status_string": (ctypes.c_char_p, [_i]),
     "sala_last_error": (ctypes.c_char_p, []),

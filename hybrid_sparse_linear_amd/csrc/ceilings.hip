@@ -45,7 +45,33 @@ __global__ __launch_bounds__(256) void copy_stream(const u32x4 *__restrict__ src
   }
 }
 
+// Each workgroup reads one contiguous 16 KiB run (4 nontemporal 16-byte loads
+// per thread, all in flight) and keeps a sum that is stored only on an
+// impossible value.  With no bytes one workgroup runs and reads nothing: the
+// duration of a launch that does no work.
+__global__ __launch_bounds__(256) void read_stream(const u32x4 *__restrict__ src, size_t n16, float *__restrict__ out) {
+  constexpr int U = 4;
+  const size_t base = (size_t)blockIdx.x * 256 * U + threadIdx.x;
+  u32x4 x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const size_t i = base + 256 * u;
+    x[u] = (i < n16) ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) s ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
+  if (s == 0x9E3779B9u && threadIdx.x == 0) out[blockIdx.x] = 1.f;
+}
+
 }  // namespace
+
+hipError_t launch_ceiling_read(const void *src, size_t bytes, float *out, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  const size_t wgs = n16 ? (n16 + 1023) / 1024 : 1;
+  hipLaunchKernelGGL(read_stream, dim3((unsigned)wgs), dim3(256), 0, st, static_cast<const u32x4 *>(src), n16, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_ceiling_mfma(int workgroups, int iters, float *out, hipStream_t st) {
   hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(512), 0, st, iters, out);

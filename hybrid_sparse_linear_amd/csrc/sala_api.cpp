@@ -380,6 +380,15 @@ int sala_ceiling_copy(const void *src, void *dst, size_t bytes, void *stream) {
                     "sala_ceiling_copy launch");
 }
 
+int sala_ceiling_read(const void *src, size_t bytes, float *out, void *stream) {
+  REQUIRE(bytes % 16 == 0, SALA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  REQUIRE(bytes == 0 || src != nullptr, SALA_ERR_INVALID_ARG, "src is NULL");
+  REQUIRE(bytes / 16384 < (size_t)INT32_MAX, SALA_ERR_INVALID_ARG, "bytes too large");
+  REQUIRE_PTR(out, "out");
+  return hip_status(sala::launch_ceiling_read(src, bytes, out, static_cast<hipStream_t>(stream)),
+                    "sala_ceiling_read launch");
+}
+
 size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, int d, int block, int n_sel) {
   if (B < 1 || Hkv < 1 || n_sel < 1 || (d != 64 && d != 128)) return 0;
   return sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel);

@@ -135,5 +135,6 @@ hipError_t noalloc_scratch(void **out);
 // Measured-ceiling microkernels (not on the attention path).
 hipError_t launch_ceiling_mfma(int workgroups, int iters, float *out, hipStream_t st);
 hipError_t launch_ceiling_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
+hipError_t launch_ceiling_read(const void *src, size_t bytes, float *out, hipStream_t st);
 
 }  // namespace sala

@@ -409,9 +409,15 @@ size_t sala_sparse_decode_workspace(int dtype, int B, int Hq, int Hkv, int L, in
  *   Flops per launch: workgroups * 8 * iters * 8 * 16384.
  * sala_ceiling_copy: copies `bytes` (a multiple of 16, both pointers 16-byte
  *   aligned) from src to dst with 16-byte vector loads and stores.
+ * sala_ceiling_read: reads `bytes` (a multiple of 16, src 16-byte aligned;
+ *   src may be NULL when bytes is 0) with 16-byte vector loads, one
+ *   contiguous 16 KiB run per workgroup of 256 threads; out [bytes / 16384 + 1]
+ *   fp32 is only written on an impossible checksum.  With bytes = 0 a single
+ *   workgroup runs and reads nothing (the cost of a launch that does no work).
  * ------------------------------------------------------------------------ */
 int sala_ceiling_mfma(int workgroups, int iters, float *out, void *stream);
 int sala_ceiling_copy(const void *src, void *dst, size_t bytes, void *stream);
+int sala_ceiling_read(const void *src, size_t bytes, float *out, void *stream);
 
 /* ------------------------------------------------------------------------
  * sala_workspace_bytes -- the workspace query of every entry point behind

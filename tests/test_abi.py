@@ -156,6 +156,9 @@ def test_dense_prefill_and_ceiling_validation():
     assert L.sala_ceiling_mfma(4, 10, NUL, NUL) == INVALID
     assert L.sala_ceiling_copy(A, A, 17, NUL) == INVALID
     assert L.sala_ceiling_copy(NUL, A, 16, NUL) == INVALID
+    assert L.sala_ceiling_read(A, 17, A, NUL) == INVALID
+    assert L.sala_ceiling_read(NUL, 16, A, NUL) == INVALID
+    assert L.sala_ceiling_read(A, 16, NUL, NUL) == INVALID
 
 
 def lpf(**kw):
