@@ -28,6 +28,7 @@ SOURCES = [
     "ceilings.hip",
     "noalloc.hip",
     "sparse_backward.hip",
+    "checks.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

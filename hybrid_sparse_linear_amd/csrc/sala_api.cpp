@@ -4,6 +4,8 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/sala.h"
 #include "sala_launch.hpp"
@@ -61,6 +63,25 @@ int hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(SALA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   g_err[0] = '\0';
   return SALA_OK;
+}
+
+// SALA_DEBUG_CHECK=1: the index rows given to the gathering calls are checked
+// on the device against their contract before the launch (the stream is
+// synchronized; skipped while it is captured into a graph).
+int debug_idx(const int32_t *idx, long long rows, int n_sel, int nqb, int nb, int own, void *stream,
+              const char *call) {
+  const char *env = getenv("SALA_DEBUG_CHECK");
+  if (!env || strcmp(env, "1") != 0) return SALA_OK;
+  unsigned long long r = ~0ull;
+  const hipError_t e = sala::debug_check_idx(idx, rows, n_sel, nqb, nb, own, static_cast<hipStream_t>(stream), &r);
+  if (e != hipSuccess) return fail(SALA_ERR_HIP, "%s idx check: %s", call, hipGetErrorString(e));
+  if (r == ~0ull) return SALA_OK;
+  const long long row = (long long)(r >> 32);
+  const int entry = (int)((r & 0xFFFFFFFFull) >> 2), code = (int)(r & 3ull);
+  if (code == 1) return fail(SALA_ERR_INVALID_ARG, "%s: idx row %lld entry %d is beyond the %d blocks", call, row, entry, nb);
+  if (code == 2) return fail(SALA_ERR_INVALID_ARG, "%s: idx row %lld entry %d lists a block twice", call, row, entry);
+  return fail(SALA_ERR_INVALID_ARG, "%s: idx row %lld does not list its own query block %lld", call, row,
+              row % (long long)nqb);
 }
 
 int check_sparse_common(int B, int Hq, int Hkv, int block, int topk_or_nsel, const char *what) {
@@ -307,6 +328,8 @@ int sala_sparse_prefill(int dtype, int B, int Hq, int Hkv, int N, int d, int blo
   REQUIRE_PTR(idx, "idx");
   REQUIRE_PTR(o, "o");
   if ((s = check_ws(ws, ws_bytes, sala::sparse_prefill_workspace(dtype, B, Hq, Hkv, N, d, block, n_sel)))) return s;
+  const int nqb = (N + 63) / 64;
+  if ((s = debug_idx(idx, (long long)B * Hkv * nqb, n_sel, nqb, nqb, 1, stream, "sala_sparse_prefill"))) return s;
   sala::SparsePrefillArgs a{dtype, B, Hq, Hkv, N, d, block, n_sel, scale, q, k, v, idx, o, ws};
   return hip_status(sala::launch_sparse_prefill(a, static_cast<hipStream_t>(stream)), "sala_sparse_prefill launch");
 }
@@ -343,6 +366,9 @@ int sala_sparse_prefill_backward(int dtype, int B, int Hq, int Hkv, int N, int d
     for (const void *y : ins) REQUIRE(x != y, SALA_ERR_INVALID_ARG, "dq, dk, dv must not overlap an input");
   REQUIRE(dq != dk && dq != dv && dk != dv, SALA_ERR_INVALID_ARG, "dq, dk and dv must be distinct buffers");
   if ((s = check_ws(ws, ws_bytes, sala::sparse_backward_workspace(dtype, B, Hq, Hkv, N, d, block, n_sel)))) return s;
+  const int nqb = (N + 63) / 64;
+  if ((s = debug_idx(idx, (long long)B * Hkv * nqb, n_sel, nqb, nqb, 1, stream, "sala_sparse_prefill_backward")))
+    return s;
   sala::SparseBackwardArgs a{dtype, B, Hq, Hkv, N, d, block, n_sel, scale, q, k, v, idx, dout, dq, dk, dv, ws};
   return hip_status(sala::launch_sparse_backward(a, static_cast<hipStream_t>(stream)),
                     "sala_sparse_prefill_backward launch");
@@ -411,6 +437,7 @@ int sala_sparse_decode(int dtype, int B, int Hq, int Hkv, int L, int d, int bloc
   REQUIRE_PTR(idx, "idx");
   REQUIRE_PTR(o, "o");
   if ((s = check_ws(ws, ws_bytes, sala::sparse_decode_workspace(dtype, B, Hq, Hkv, L, d, block, n_sel)))) return s;
+  if ((s = debug_idx(idx, (long long)B * Hkv, n_sel, 1, (L + 63) / 64, 0, stream, "sala_sparse_decode"))) return s;
   sala::SparseDecodeArgs a{dtype, B, Hq, Hkv, L, d, block, n_sel, scale, q, k_cache, v_cache, idx, o, ws};
   return hip_status(sala::launch_sparse_decode(a, static_cast<hipStream_t>(stream)), "sala_sparse_decode launch");
 }

@@ -137,4 +137,9 @@ hipError_t launch_ceiling_mfma(int workgroups, int iters, float *out, hipStream_
 hipError_t launch_ceiling_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
 hipError_t launch_ceiling_read(const void *src, size_t bytes, float *out, hipStream_t st);
 
+// Debug check of idx rows (see checks.hip): *result = ~0 when every row is
+// valid, else (first bad row << 32 | entry << 2 | code).  Synchronizes st.
+hipError_t debug_check_idx(const int32_t *idx, long long rows, int n_sel, int nqb, int nb, int own, hipStream_t st,
+                           unsigned long long *result);
+
 }  // namespace sala

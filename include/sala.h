@@ -314,7 +314,12 @@ size_t sala_sparse_select_workspace(int dtype, int B, int Hq, int Hkv, int d, in
  *   o_t  = sum_{s in A(t)} softmax_s(scale * q_t . k_s) v_s
  * idx rows list distinct blocks; the list ends at the first negative entry;
  * entries greater than i contribute nothing (they are skipped).  Every row
- * must contain its own block i (the forced local block does).
+ * must contain its own block i (the forced local block does).  With the
+ * environment variable SALA_DEBUG_CHECK=1, rows that break this (an entry
+ * beyond the blocks, a block listed twice, a missing own block) are reported
+ * as SALA_ERR_INVALID_ARG before the launch (the stream is synchronized; the
+ * check is skipped during graph capture); the same holds for
+ * sala_sparse_prefill_backward and sala_sparse_decode.
  *
  *   block        64.   n_sel = idx row length (topk + n_init + n_local).
  *   scale        usually 1/sqrt(d).
