@@ -14,9 +14,9 @@
 // gradients; the selection itself is a top-k and passes no gradient.
 //
 // Passes (bf16 inputs, bf16 MFMA 16x16x32 with fp32 accumulation):
-//   sparse_bwd_dq    one workgroup = 8 waves = 2 query heads of a group x the
-//                    64 rows of one query block (a wave: one head, one 16-row
-//                    tile).  A first sweep over the selected blocks forms each
+//   sparse_bwd_dq    one workgroup = 8 waves = 4 query heads of a group x the
+//                    64 rows of one query block (a wave: one head, two 16-row
+//                    tiles, each K / V fragment read from LDS feeding both).  A first sweep over the selected blocks forms each
 //                    row's log-sum-exp (log2 units) and D_t = sum_s p_s dP_s
 //                    online from the fp32 scores, so that the row's dS sums to
 //                    zero up to fp32 rounding (D_t from a bf16-rounded output
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
                                                      const uint16_t *__restrict__ dout,
                                                      const int32_t *__restrict__ idx, uint16_t *__restrict__ dq,
                                                      float *__restrict__ lse2_out, float *__restrict__ drow_out,
-                                                     int Hq, int Hkv, int N, int NQB, int n_sel, int HP, int ntasks,
+                                                     int Hq, int Hkv, int N, int NQB, int n_sel, int HG, int ntasks,
                                                      float scale) {
   using Cf = BwCfg<D>;
   __shared__ __attribute__((aligned(16))) char kb0[Cf::TB], kb1[Cf::TB];
@@ -99,22 +99,21 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
   __shared__ int sel[1024];
   __shared__ int nvalid_sh, diag_sh;
 
-  // XCD-aware: the HP workgroups of one task share blockIdx % 8
+  // XCD-aware: the HG workgroups of one task share blockIdx % 8
   const int x = blockIdx.x;
   const int slot = x >> 3;
-  const int task = (slot / HP) * 8 + (x & 7);
-  const int hp = slot % HP;
+  const int task = (slot / HG) * 8 + (x & 7);
+  const int hg = slot % HG;
   if (task >= ntasks) return;
   const int i = task % NQB;
   const int bkv = task / NQB;
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int hl = 2 * hp + (w >> 2);
+  const int hl = 4 * hg + (w & 3);
   const bool active = hl < G;
   const int hq = kvh * G + (active ? hl : 0);
-  const int rt = w & 3;                  // this wave's 16-row tile of the query block
-  const int t = BB * i + 16 * rt + lr;   // this lane's query row
+  const int r0 = 32 * (w >> 2);               // this wave's first row in the query block: tiles r0, r0 + 16
   const float scale_log2 = scale * 1.4426950408889634f;
 
   // block list as in the forward: entries before the first negative one that
@@ -142,15 +141,19 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
     }
   }
 
-  // q and dO fragments (B operands): lane holds row t, features 32s + 8lg .. +7
+  // q and dO fragments (B operands): lane holds row BB*i + r0 + 16a + lr, features 32s + 8lg .. +7
   const size_t rowbase = ((size_t)(b * Hq + hq) * N) * D;
-  u32x4 qf[Cf::NDS], df[Cf::NDS];
+  u32x4 qf[2][Cf::NDS], df[2][Cf::NDS];
 #pragma unroll
-  for (int s = 0; s < Cf::NDS; ++s) {
-    const bool ok = t < N;
-    const size_t off = rowbase + (size_t)t * D + 32 * s + 8 * lg;
-    qf[s] = ok ? gload16(q + off) : u32x4{0, 0, 0, 0};
-    df[s] = ok ? gload16(dout + off) : u32x4{0, 0, 0, 0};
+  for (int a = 0; a < 2; ++a) {
+    const int t = BB * i + r0 + 16 * a + lr;
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s) {
+      const bool ok = t < N;
+      const size_t off = rowbase + (size_t)t * D + 32 * s + 8 * lg;
+      qf[a][s] = ok ? gload16(q + off) : u32x4{0, 0, 0, 0};
+      df[a][s] = ok ? gload16(dout + off) : u32x4{0, 0, 0, 0};
+    }
   }
 
   __syncthreads();
@@ -167,42 +170,61 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
   };
   const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);
 
-  // S^T for one block: tile kt = 2p + tt holds keys 32p + 8lg + 4tt + e (e = 0..3)
-  // of this lane's row, in log2 units; masked keys (after the row in the
-  // diagonal block, or at or past N) are -inf
-  auto scores = [&](const char *kbuf, int j, bool diag, f32x4 (&S)[4]) {
+  // S^T for keys 32p .. 32p+31 of one block: tile [tt][a] holds keys
+  // 32p + 8lg + 4tt + e (e = 0..3) of row r0 + 16a + lr, in log2 units; masked
+  // keys (after the row in the diagonal block, or at or past N) are -inf.
+  // Each K fragment feeds both row tiles.
+  auto scores = [&](const char *kbuf, int j, bool diag, int p, f32x4 (&S)[2][2]) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) S[tt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        S[kt] = mfma16x16x32(lds_load<u32x4>(kbuf, kv_off(kt >> 1, kt & 1, s)), qf[s], S[kt]);
+      for (int tt = 0; tt < 2; ++tt) {
+        const u32x4 A = lds_load<u32x4>(kbuf, kv_off(p, tt, s));
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int a = 0; a < 2; ++a) S[tt][a] = mfma16x16x32(A, qf[a][s], S[tt][a]);
+      }
+    if (!diag && (j + 1) * BB <= N) {  // no key of the block is masked
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + e;
-        const bool masked = (diag && key > 16 * rt + lr) || (BB * j + key >= N);
-        S[kt][e] = masked ? -INFINITY : S[kt][e] * scale_log2;
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) S[tt][a] *= scale_log2;
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 32 * p + 8 * lg + 4 * tt + e;
+            const bool masked = (diag && key > r0 + 16 * a + lr) || (BB * j + key >= N);
+            S[tt][a][e] = masked ? -INFINITY : S[tt][a][e] * scale_log2;
+          }
+    }
+  };
+
+  // dP^T = V dO^T for keys 32p .. 32p+31, tiles as in scores
+  auto dprods = [&](const char *vbuf, int p, f32x4 (&dP)[2][2]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) dP[tt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const u32x4 A = lds_load<u32x4>(vbuf, kv_off(p, tt, s));
+#pragma unroll
+        for (int a = 0; a < 2; ++a) dP[tt][a] = mfma16x16x32(A, df[a][s], dP[tt][a]);
       }
   };
 
-  // dP^T = V dO^T for one block, tiles as in scores
-  auto dprods = [&](const char *vbuf, f32x4 (&dP)[4]) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) dP[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < Cf::NDS; ++s)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        dP[kt] = mfma16x16x32(lds_load<u32x4>(vbuf, kv_off(kt >> 1, kt & 1, s)), df[s], dP[kt]);
-  };
-
-  // sweep 1, online over the blocks: the row max m, lsum = sum 2^(s - m) and
-  // dsum = sum 2^(s - m) dP_s, both rescaled when m moves
-  float m = -INFINITY, lsum = 0.f, dsum = 0.f;
-  if (nvalid > 0) {
+  // The two sweeps walk the block list with K and V double buffered in LDS.
+  auto sweep = [&](auto &&body) {
+    if (nvalid <= 0) return;
     load_tile<D, 512>(kbase + (size_t)blk(0) * BB * D, N - blk(0) * BB, kb0, tid);
     load_tile<D, 512>(vbase + (size_t)blk(0) * BB * D, N - blk(0) * BB, vb0, tid);
     for (int e = 0; e < nvalid; ++e) {
@@ -216,94 +238,108 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
         load_tile<D, 512>(kbase + (size_t)jn * BB * D, N - jn * BB, odd ? kb0 : kb1, tid);
         load_tile<D, 512>(vbase + (size_t)jn * BB * D, N - jn * BB, odd ? vb0 : vb1, tid);
       }
-      const int j = blk(e);
-      f32x4 S[4], dP[4];
-      scores(kcur, j, has_diag && e == nvalid - 1, S);
-      dprods(vcur, dP);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ee = 0; ee < 4; ++ee) mx = fmaxf(mx, S[kt][ee]);
-      mx = row4_max(mx);
-      const float mn = fmaxf(m, mx);
-      float ps = 0.f, pd = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ee = 0; ee < 4; ++ee) {
-          const float pe = __builtin_amdgcn_exp2f(S[kt][ee] - mn);
-          ps += pe;
-          pd = fmaf(pe, dP[kt][ee], pd);
-        }
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      lsum = lsum * alpha + row4_sum(ps);
-      dsum = dsum * alpha + row4_sum(pd);
-      m = mn;
+      body(kcur, vcur, blk(e), has_diag && e == nvalid - 1);
       __syncthreads();  // every wave is done with kcur / vcur before they are reloaded
     }
-  }
+  };
+
+  // sweep 1, online over the blocks, per row tile a: the row max m, lsum =
+  // sum 2^(s - m) and dsum = sum 2^(s - m) dP_s, both rescaled when m moves
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, dsum[2] = {0.f, 0.f};
+  sweep([&](const char *kcur, const char *vcur, int j, bool diag) {
+    f32x4 S[2][2][2], dP[2][2][2];  // [p][tt][a]
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      scores(kcur, j, diag, p, S[p]);
+      dprods(vcur, p, dP[p]);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) mx = fmaxf(mx, S[p][tt][a][ee]);
+      mx = row4_max(mx);
+      const float mn = fmaxf(m[a], mx);
+      float ps = 0.f, pd = 0.f;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            const float pe = __builtin_amdgcn_exp2f(S[p][tt][a][ee] - mn);
+            ps += pe;
+            pd = fmaf(pe, dP[p][tt][a][ee], pd);
+          }
+      const float alpha = __builtin_amdgcn_exp2f(m[a] - mn);
+      lsum[a] = lsum[a] * alpha + row4_sum(ps);
+      dsum[a] = dsum[a] * alpha + row4_sum(pd);
+      m[a] = mn;
+    }
+  });
   // log2 of the row's sum of 2^s, and D_t; a row with no key (a list without
   // its own block) gets +inf, so its P is 0 (the forward gives it a zero output)
-  const float lse2 = lsum > 0.f ? m + __builtin_amdgcn_logf(lsum) : INFINITY;
-  const float drow = lsum > 0.f ? dsum / lsum : 0.f;
-
-  // sweep 2: dQ^T += K^T dS^T with dS = P (dP - D) scale
-  f32x4 dQ[Cf::ND];
+  float lse2[2], drow[2];
 #pragma unroll
-  for (int dt = 0; dt < Cf::ND; ++dt) dQ[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (nvalid > 0) {
-    load_tile<D, 512>(kbase + (size_t)blk(0) * BB * D, N - blk(0) * BB, kb0, tid);
-    load_tile<D, 512>(vbase + (size_t)blk(0) * BB * D, N - blk(0) * BB, vb0, tid);
-    for (int e = 0; e < nvalid; ++e) {
-      wait_vm0();
-      __syncthreads();
-      const bool odd = e & 1;
-      const char *kcur = odd ? kb1 : kb0;
-      const char *vcur = odd ? vb1 : vb0;
-      if (e + 1 < nvalid) {
-        const int jn = blk(e + 1);
-        load_tile<D, 512>(kbase + (size_t)jn * BB * D, N - jn * BB, odd ? kb0 : kb1, tid);
-        load_tile<D, 512>(vbase + (size_t)jn * BB * D, N - jn * BB, odd ? vb0 : vb1, tid);
-      }
-      const int j = blk(e);
-      f32x4 S[4], dP[4];
-      scores(kcur, j, has_diag && e == nvalid - 1, S);
-      dprods(vcur, dP);
+  for (int a = 0; a < 2; ++a) {
+    lse2[a] = lsum[a] > 0.f ? m[a] + __builtin_amdgcn_logf(lsum[a]) : INFINITY;
+    drow[a] = lsum[a] > 0.f ? dsum[a] / lsum[a] : 0.f;
+  }
+
+  // sweep 2, per 32-key half p: dQ^T += K^T dS^T with dS = P (dP - D) scale
+  f32x4 dQ[2][Cf::ND];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int dt = 0; dt < Cf::ND; ++dt) dQ[a][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sweep([&](const char *kcur, const char *vcur, int j, bool diag) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      f32x4 S[2][2], dP[2][2];
+      scores(kcur, j, diag, p, S);
+      dprods(vcur, p, dP);
       u32x4 dS[2];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int a = 0; a < 2; ++a) {
         float ds[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int ee = 0; ee < 4; ++ee) {
-            const float pr = __builtin_amdgcn_exp2f(S[2 * p + tt][ee] - lse2);
-            ds[tt][ee] = pr * (dP[2 * p + tt][ee] - drow) * scale;
+            const float pr = __builtin_amdgcn_exp2f(S[tt][a][ee] - lse2[a]);
+            ds[tt][ee] = pr * (dP[tt][a][ee] - drow[a]) * scale;
           }
-        dS[p] = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
+        dS[a] = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
                       pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
       }
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int dt = 0; dt < Cf::ND; ++dt) {
+        const u32x4 A = tr_frag(kcur, 32 * p * Cf::ROWB, tr_off, tr_xor, dt, Cf::NCH, Cf::ROWB);
 #pragma unroll
-        for (int dt = 0; dt < Cf::ND; ++dt)
-          dQ[dt] = mfma16x16x32(tr_frag(kcur, 32 * p * Cf::ROWB, tr_off, tr_xor, dt, Cf::NCH, Cf::ROWB), dS[p],
-                                dQ[dt]);
-      __syncthreads();  // every wave is done with kcur / vcur before they are reloaded
+        for (int a = 0; a < 2; ++a) dQ[a][dt] = mfma16x16x32(A, dS[a], dQ[a][dt]);
+      }
     }
-  }
+  });
 
-  if (!active || t >= N) return;
-  uint16_t *dqrow = dq + rowbase + (size_t)t * D;
+  if (!active) return;
 #pragma unroll
-  for (int dt = 0; dt < Cf::ND; ++dt)
-    *reinterpret_cast<u32x2 *>(dqrow + 16 * dt + 4 * lg) =
-        u32x2{pack_bf16x2(dQ[dt][0], dQ[dt][1]), pack_bf16x2(dQ[dt][2], dQ[dt][3])};
-  if (lg == 0) {
-    const size_t r = (size_t)(b * Hq + hq) * N + t;
-    lse2_out[r] = lse2;
-    drow_out[r] = drow;
+  for (int a = 0; a < 2; ++a) {
+    const int t = BB * i + r0 + 16 * a + lr;
+    if (t >= N) continue;
+    uint16_t *dqrow = dq + rowbase + (size_t)t * D;
+#pragma unroll
+    for (int dt = 0; dt < Cf::ND; ++dt)
+      *reinterpret_cast<u32x2 *>(dqrow + 16 * dt + 4 * lg) =
+          u32x2{pack_bf16x2(dQ[a][dt][0], dQ[a][dt][1]), pack_bf16x2(dQ[a][dt][2], dQ[a][dt][3])};
+    if (lg == 0) {
+      const size_t r = (size_t)(b * Hq + hq) * N + t;
+      lse2_out[r] = lse2[a];
+      drow_out[r] = drow[a];
+    }
   }
 }
 
@@ -476,6 +512,8 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
     const float(*sc)[256] = odd ? st1 : st0;
     if (n + 1 < steps) stage(n + 1, odd ? qb0 : qb1, odd ? ob0 : ob1, odd ? st0 : st1);
     const int i = plist[n / G];
+    // a query block after the key block, both wholly before N: no pair is masked
+    const bool interior = i > j && (i + 1) * BB <= N && (j + 1) * BB <= N;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {  // query rows 32p .. 32p + 31
       // S and dP tiles tt = 0, 1: lane holds queries 32p + 8lg + 4tt + e of key `key`
@@ -493,16 +531,27 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
       const f32x4 ls0 = lds_load<f32x4>(sc[0], (32 * p + 8 * lg) * 4), ls1 = lds_load<f32x4>(sc[0], (32 * p + 8 * lg + 4) * 4);
       const f32x4 dr0 = lds_load<f32x4>(sc[1], (32 * p + 8 * lg) * 4), dr1 = lds_load<f32x4>(sc[1], (32 * p + 8 * lg + 4) * 4);
       float pr[2][4], ds[2][4];
+      if (interior) {  // every (query, key) pair of the step is live: no masks
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qrow = BB * i + 32 * p + 8 * lg + 4 * tt + e;  // the query's token
-          const bool live = qrow < N && key < N && key <= qrow;
-          const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
-          pr[tt][e] = live ? __builtin_amdgcn_exp2f(S[tt][e] * scale_log2 - lsev) : 0.f;
-          ds[tt][e] = pr[tt][e] * (dP[tt][e] - drv) * scale;
-        }
+          for (int e = 0; e < 4; ++e) {
+            const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
+            pr[tt][e] = __builtin_amdgcn_exp2f(S[tt][e] * scale_log2 - lsev);
+            ds[tt][e] = pr[tt][e] * (dP[tt][e] - drv) * scale;
+          }
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int qrow = BB * i + 32 * p + 8 * lg + 4 * tt + e;  // the query's token
+            const bool live = qrow < N && key < N && key <= qrow;
+            const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
+            pr[tt][e] = live ? __builtin_amdgcn_exp2f(S[tt][e] * scale_log2 - lsev) : 0.f;
+            ds[tt][e] = pr[tt][e] * (dP[tt][e] - drv) * scale;
+          }
+      }
       const u32x4 Pf = u32x4{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                              pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
       const u32x4 Sf = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
@@ -593,12 +642,12 @@ hipError_t run_bwd(const SparseBackwardArgs &a, hipStream_t st) {
   int4 *items = reinterpret_cast<int4 *>(ws + L.items);
   float *partial = reinterpret_cast<float *>(ws + L.partial);
   const int NQB = L.NQB, BKV = a.B * a.Hkv, G = a.Hq / a.Hkv;
-  const int HP = (G + 1) / 2;
+  const int HG = (G + 3) / 4;
   const int ntasks = BKV * NQB;
-  const int grid_dq = ((ntasks + 7) / 8) * 8 * HP;
+  const int grid_dq = ((ntasks + 7) / 8) * 8 * HG;
   hipLaunchKernelGGL((sparse_bwd_dq<D>), dim3(grid_dq), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (const uint16_t *)a.dout,
-                     a.idx, (uint16_t *)a.dq, lse, drow, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HP, ntasks, a.scale);
+                     a.idx, (uint16_t *)a.dq, lse, drow, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HG, ntasks, a.scale);
   const size_t nbits = (size_t)BKV * NQB * L.WPR;
   hipLaunchKernelGGL(bwd_clear, dim3((unsigned)((nbits + 255) / 256)), dim3(256), 0, st, bitmap, nbits);
   const long long rows = (long long)BKV * NQB;
