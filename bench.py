@@ -447,7 +447,7 @@ def bench_workload1(torch, sala, I, reps=20):
     return {"workload": "tiny group, fp32, B=1, N=2048: 3 linear layers (H=4, d=64, chunk 64, decay 1.0/0.99) + "
                         "1 sparse layer (4 heads, top-4 + 1 initial + 2 local)",
             "gpu_ms": round(ms, 4), "tokens_per_s": round(2048 / (ms * 1e-3), 1), "roofline": None,
-            "roofline_note": "a correctness workload: launch-bound at this size, no roofline is claimed",
+            "roofline_note": "a correctness workload (fp32, 2048 tokens, the VALU paths): no roofline is claimed",
             "cpu_oracle": dict(oracle_entry(t_or, 2048), sample="the whole workload (quadratic linear form, full "
                                                                 "selection, restricted softmax)")}
 

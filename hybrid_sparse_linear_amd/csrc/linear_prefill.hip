@@ -22,8 +22,8 @@
 //           with bf16 MFMA 16x16x32 and fp32 accumulation; the fp32 master S
 //           stays in registers, a bf16 copy of S^T in LDS feeds the Q S product.
 //           The last segment writes S_out.
-// fp32 path: lin_recurrent_f32 runs the recurrence S_t = lam S_{t-1} + k_t v_t^T,
-// o_t = q_t S_t token by token with one thread per d_v column (small shapes).
+// fp32 path: the same three passes on the VALU in fp32 over tiles of 32
+// tokens (lin_f32_pass, lin_seg_scan).
 //
 // Backward (sala_linear_prefill_backward).  For dO = dL/do and dS = dL/dS_out,
 //   dQ    = ((dO V^T) * D) K + diag(lam^(t+1)) dO S_in^T
@@ -642,49 +642,191 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------- fp32 path
-// One workgroup per (b, h); thread = one d_v column of the state.
-// dir: the backward passes' switches (LinDir).
+// The bf16 path's segment plan in fp32 on the VALU, with tiles of FT tokens:
+// lin_f32_pass<D, false> forms the aggregate of every segment but the last,
+// lin_seg_scan turns them into the states entering the segments, and
+// lin_f32_pass<D, true> walks each segment's tiles:
+//   P = (Q K^T) * decay mask                                   [FT x FT]
+//   O = P V + diag(w) Q S      w_i = lam^(i+1)  (lam^i while a late initial state is in its first tile)
+//   S = f S + (diag(lam^(m-1-j)) K)^T V     f = lam^m  (lam^(m-1) there)
+// S lives in LDS; each thread updates its own block of it.
+constexpr int FT = 32;  // tokens per fp32 tile
+
 template <int D>
-__global__ __launch_bounds__(D) void lin_recurrent_f32(const float *__restrict__ q, const float *__restrict__ k,
-                                                       const float *__restrict__ v, float *__restrict__ o,
-                                                       const float *__restrict__ decay,
-                                                       const float *__restrict__ state_in,
-                                                       float *__restrict__ state_out, int H, int N, LinDir dir) {
-  constexpr int T = 32;  // tokens staged per step
-  __shared__ float qs[T][D];
-  __shared__ float ks[T][D];
-  const int bh = blockIdx.x, h = bh % H, col = threadIdx.x;
+struct F32Cfg {
+  static constexpr int LD = D + 4;   // row stride (floats) of the staged tiles and of S
+  static constexpr int SR = D / 16;  // S block of a thread: SR rows x SR columns (16 x 16 blocks)
+  static constexpr int OR = 4;       // O block of a thread: OR rows (8 row groups) ...
+  static constexpr int OC = D / 32;  // ... x OC columns (32 column groups)
+};
+
+template <int D, bool OUT>
+__global__ __launch_bounds__(256) void lin_f32_pass(const float *__restrict__ q, const float *__restrict__ k,
+                                                    const float *__restrict__ v, float *__restrict__ o,
+                                                    const float *__restrict__ decay, float *__restrict__ seg_state,
+                                                    const float *__restrict__ s_init, float *__restrict__ state_out,
+                                                    int H, int N, int seg_len, int nseg, LinDir dir, int sin_T) {
+  using Cf = F32Cfg<D>;
+  constexpr int LD = Cf::LD, SR = Cf::SR, OR = Cf::OR, OC = Cf::OC;
+  __shared__ __attribute__((aligned(16))) float Ks[FT][LD];
+  __shared__ __attribute__((aligned(16))) float Vs[FT][LD];
+  __shared__ __attribute__((aligned(16))) float Qs[OUT ? FT : 1][LD];
+  __shared__ __attribute__((aligned(16))) float Ss[D][LD];
+  __shared__ float Ps[OUT ? FT : 1][FT + 1];
+  __shared__ float pw[FT + 1];  // lam^n, n = 0..FT
+  const int tid = threadIdx.x;
+  const int nblk = OUT ? nseg : nseg - 1;
+  const int bh = blockIdx.x / nblk, seg = blockIdx.x % nblk;
+  const int h = bh % H;
   const float lam = decay ? decay[h] : 1.f;
-  const size_t off = (size_t)bh * N * D;
-  auto row = [&](int t) -> size_t { return (size_t)(dir.rev ? N - 1 - t : t); };
-  float S[D];
+  const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
+  const size_t base = (size_t)bh * N * D;
+  const size_t DD = (size_t)D * D;
+  auto prow = [&](int t) -> size_t { return (size_t)(dir.rev ? N - 1 - t : t); };
+  for (int n = tid; n <= FT; n += 256) pw[n] = (float)pow((double)lam, (double)n);
+  // the state block of this thread: rows r0 .. r0+SR-1, columns c0 .. c0+SR-1
+  const int r0 = SR * (tid >> 4), c0 = SR * (tid & 15);
+  {
+    const float *sin = nullptr;
+    if (OUT) sin = nseg > 1 ? seg_state + ((size_t)bh * nseg + seg) * DD : (s_init ? s_init + (size_t)bh * DD : nullptr);
 #pragma unroll
-  for (int r = 0; r < D; ++r)
-    S[r] = state_in ? state_in[(size_t)bh * D * D + (dir.state_T ? (size_t)col * D + r : (size_t)r * D + col)] : 0.f;
-  for (int t0 = 0; t0 < N; t0 += T) {
-    const int nt = min(T, N - t0);
-    __syncthreads();
-    for (int i = col; i < nt * D; i += D) {
-      qs[i / D][i % D] = q[off + row(t0 + i / D) * D + i % D];
-      ks[i / D][i % D] = k[off + row(t0 + i / D) * D + i % D];
-    }
-    __syncthreads();
-    for (int tt = 0; tt < nt; ++tt) {
-      const float vv = v[off + row(t0 + tt) * D + col];
-      const float lt = (dir.lag && t0 + tt == 0) ? 1.f : lam;  // a late initial state is not decayed at token 0
-      float acc = 0.f;
+    for (int r = 0; r < SR; ++r)
 #pragma unroll
-      for (int r = 0; r < D; ++r) {
-        S[r] = fmaf(lt, S[r], ks[tt][r] * vv);
-        acc = fmaf(qs[tt][r], S[r], acc);
+      for (int c = 0; c < SR; ++c) {
+        const int rr = r0 + r, cc = c0 + c;
+        Ss[rr][cc] = sin ? sin[sin_T ? (size_t)cc * D + rr : (size_t)rr * D + cc] : 0.f;
       }
-      o[off + row(t0 + tt) * D + col] = acc;
-    }
   }
-  if (state_out) {
-    const float f = dir.scale ? lam : 1.f;
+  // O block of this thread: rows o0 .. o0+OR-1 of the tile, columns p0 .. p0+OC-1
+  const int o0 = OR * (tid >> 5), p0 = OC * (tid & 31);
+  for (int t0 = t_begin; t0 < t_end; t0 += FT) {
+    const int m = min(FT, t_end - t0);
+    __syncthreads();  // the previous tile's reads are done (and S is in LDS)
+    for (int e = tid; e < FT * D / 4; e += 256) {
+      const int i = e / (D / 4), c4 = 4 * (e % (D / 4));
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = kk, qq = kk;
+      if (i < m) {
+        const size_t g = base + prow(t0 + i) * D + c4;
+        kk = *reinterpret_cast<const f32x4 *>(k + g);
+        vv = *reinterpret_cast<const f32x4 *>(v + g);
+        if (OUT) qq = *reinterpret_cast<const f32x4 *>(q + g);
+      }
+      *reinterpret_cast<f32x4 *>(&Ks[i][c4]) = kk;
+      *reinterpret_cast<f32x4 *>(&Vs[i][c4]) = vv;
+      if (OUT) *reinterpret_cast<f32x4 *>(&Qs[i][c4]) = qq;
+    }
+    __syncthreads();
+    const bool late_first = dir.lag && t0 == 0;  // the initial state enters one step late
+    if constexpr (OUT) {
+      // P[i][j] = (q_i . k_j) lam^(i-j) for j <= i < m, else 0.  The dot
+      // products (here and in Q S below) keep four partial sums, added as a
+      // tree: sequential sums of 128 products left rows whose value cancels to
+      // near zero off by more than fp32's relative bound (CPU emulation of
+      // both orders against the float64 oracle).
+      for (int e = tid; e < FT * FT; e += 256) {
+        const int i = e / FT, j = e % FT;
+        float acc = 0.f;
+        if (j <= i && i < m) {
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+          for (int c = 0; c < D; c += 16) {
 #pragma unroll
-    for (int r = 0; r < D; ++r) state_out[(size_t)bh * D * D + (size_t)r * D + col] = S[r] * f;
+            for (int u = 0; u < 4; ++u) {
+              const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&Qs[i][c + 4 * u]);
+              const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&Ks[j][c + 4 * u]);
+              part[u] = fmaf(a4[0], b4[0], fmaf(a4[1], b4[1], fmaf(a4[2], b4[2], fmaf(a4[3], b4[3], part[u]))));
+            }
+          }
+          acc = ((part[0] + part[1]) + (part[2] + part[3])) * pw[i - j];
+        }
+        Ps[i][j] = acc;
+      }
+      __syncthreads();
+      float acc[OR][OC], qs[4][OR][OC];
+#pragma unroll
+      for (int r = 0; r < OR; ++r)
+#pragma unroll
+        for (int c = 0; c < OC; ++c) {
+          acc[r][c] = 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) qs[u][r][c] = 0.f;
+        }
+      for (int j = 0; j < m; ++j) {
+        float vv[OC], pp[OR];
+#pragma unroll
+        for (int c = 0; c < OC; ++c) vv[c] = Vs[j][p0 + c];
+#pragma unroll
+        for (int r = 0; r < OR; ++r) pp[r] = Ps[o0 + r][j];
+#pragma unroll
+        for (int r = 0; r < OR; ++r)
+#pragma unroll
+          for (int c = 0; c < OC; ++c) acc[r][c] = fmaf(pp[r], vv[c], acc[r][c]);
+      }
+#pragma unroll 2
+      for (int r4 = 0; r4 < D; r4 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int rr = r4 + u;
+          float ss[OC], qv[OR];
+#pragma unroll
+          for (int c = 0; c < OC; ++c) ss[c] = Ss[rr][p0 + c];
+#pragma unroll
+          for (int r = 0; r < OR; ++r) qv[r] = Qs[o0 + r][rr];
+#pragma unroll
+          for (int r = 0; r < OR; ++r)
+#pragma unroll
+            for (int c = 0; c < OC; ++c) qs[u][r][c] = fmaf(qv[r], ss[c], qs[u][r][c]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < OR; ++r) {
+        const int i = o0 + r;
+        if (i >= m) continue;
+        const float w = late_first ? pw[i] : pw[i + 1];
+        float *orow = o + base + prow(t0 + i) * D + p0;
+#pragma unroll
+        for (int c = 0; c < OC; ++c)
+          orow[c] = fmaf(w, (qs[0][r][c] + qs[1][r][c]) + (qs[2][r][c] + qs[3][r][c]), acc[r][c]);
+      }
+      __syncthreads();  // every read of S is done before it is updated
+    }
+    // S = f S + sum_j (lam^(m-1-j) k_j) v_j^T on this thread's block
+    const float f = late_first ? pw[m - 1] : pw[m];
+    float sb[SR][SR];
+#pragma unroll
+    for (int r = 0; r < SR; ++r)
+#pragma unroll
+      for (int c = 0; c < SR; ++c) sb[r][c] = f * Ss[r0 + r][c0 + c];
+    for (int j = 0; j < m; ++j) {
+      const float wj = pw[m - 1 - j];
+      float kr[SR], vc[SR];
+#pragma unroll
+      for (int r = 0; r < SR; ++r) kr[r] = wj * Ks[j][r0 + r];
+#pragma unroll
+      for (int c = 0; c < SR; ++c) vc[c] = Vs[j][c0 + c];
+#pragma unroll
+      for (int r = 0; r < SR; ++r)
+#pragma unroll
+        for (int c = 0; c < SR; ++c) sb[r][c] = fmaf(kr[r], vc[c], sb[r][c]);
+    }
+#pragma unroll
+    for (int r = 0; r < SR; ++r)
+#pragma unroll
+      for (int c = 0; c < SR; ++c) Ss[r0 + r][c0 + c] = sb[r][c];
+  }
+  // a segment's aggregate, or (last segment) the final state
+  float *dst = nullptr;
+  float fs = 1.f;
+  if (!OUT) dst = seg_state + ((size_t)bh * nseg + seg) * DD;
+  else if (seg == nseg - 1 && state_out) {
+    dst = state_out + (size_t)bh * DD;
+    fs = dir.scale ? lam : 1.f;
+  }
+  if (dst) {
+#pragma unroll
+    for (int r = 0; r < SR; ++r)
+#pragma unroll
+      for (int c = 0; c < SR; ++c) dst[(size_t)(r0 + r) * D + c0 + c] = Ss[r0 + r][c0 + c] * fs;
   }
 }
 
@@ -738,29 +880,39 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   return a.rev ? run_bf16<C, D, true>(a, st) : run_bf16<C, D, false>(a, st);
 }
 
+template <int D>
+hipError_t run_f32(const LinearPrefillArgs &a, hipStream_t st) {
+  const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
+  const int BH = a.B * a.H;
+  int seg_len, nseg;
+  seg_plan(BH, a.N, FT, &seg_len, &nseg);
+  float *ws = static_cast<float *>(a.ws);
+  const size_t DD = (size_t)D * D;
+  const float *q = static_cast<const float *>(a.q), *k = static_cast<const float *>(a.k),
+              *v = static_cast<const float *>(a.v);
+  if (nseg > 1) {
+    hipLaunchKernelGGL((lin_f32_pass<D, false>), dim3(BH * (nseg - 1)), dim3(256), 0, st, q, k, v, nullptr, a.decay,
+                       ws, nullptr, nullptr, a.H, a.N, seg_len, nseg, dir, 0);
+    hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws, a.state_in,
+                       a.decay, a.H, D, (int)DD, a.N, seg_len, nseg, dir);
+  }
+  // one segment: the pass reads the caller's initial state itself (transposed if asked)
+  hipLaunchKernelGGL((lin_f32_pass<D, true>), dim3(BH * nseg), dim3(256), 0, st, q, k, v, static_cast<float *>(a.o),
+                     a.decay, ws, a.state_in, a.state_out, a.H, a.N, seg_len, nseg, dir, nseg > 1 ? 0 : a.state_T);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk) {
-  if (dtype != 1) return 0;
   int seg_len, nseg;
-  seg_plan(B * H, N, chunk, &seg_len, &nseg);
+  seg_plan(B * H, N, dtype == 1 ? chunk : FT, &seg_len, &nseg);  // the fp32 path tiles by FT tokens
   if (nseg <= 1) return 0;
   return (size_t)B * H * nseg * d * d * sizeof(float);
 }
 
 hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st) {
-  if (a.dtype == 0) {
-    const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
-    if (a.d == 64)
-      hipLaunchKernelGGL(lin_recurrent_f32<64>, dim3(a.B * a.H), dim3(64), 0, st, (const float *)a.q,
-                         (const float *)a.k, (const float *)a.v, (float *)a.o, a.decay, a.state_in, a.state_out,
-                         a.H, a.N, dir);
-    else
-      hipLaunchKernelGGL(lin_recurrent_f32<128>, dim3(a.B * a.H), dim3(128), 0, st, (const float *)a.q,
-                         (const float *)a.k, (const float *)a.v, (float *)a.o, a.decay, a.state_in, a.state_out,
-                         a.H, a.N, dir);
-    return hipGetLastError();
-  }
+  if (a.dtype == 0) return a.d == 64 ? run_f32<64>(a, st) : run_f32<128>(a, st);
   if (a.chunk == 128 && a.d == 128) return run_bf16<128, 128>(a, st);
   if (a.chunk == 64 && a.d == 128) return run_bf16<64, 128>(a, st);
   if (a.chunk == 128 && a.d == 64) return run_bf16<128, 64>(a, st);

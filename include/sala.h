@@ -72,7 +72,8 @@ typedef enum {
  *   dtype        SALA_BF16 (MFMA path) or SALA_F32.
  *   B, H, N, d   batch, heads, tokens (N >= 1), head dim (64 or 128).
  *   chunk        intra-chunk length of the bf16 path (64 or 128); any value in
- *                {64, 128} gives the same result up to rounding.
+ *                {64, 128} gives the same result up to rounding.  The fp32
+ *                path works in tiles of 32 tokens whatever the chunk.
  *   q, k, v      [B, H, N, d] of dtype.
  *   o            [B, H, N, d] of dtype (output).
  *   decay        [H] fp32 in [0, 1], or NULL for lam = 1 on every head.

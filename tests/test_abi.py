@@ -73,7 +73,11 @@ def test_linear_prefill_workspace_rules():
     L = _lib.lib()
     need = L.sala_linear_prefill_workspace(BF16, 1, 32, 32768, 128, 128)
     assert need > 0 and need % (128 * 128 * 4) == 0
-    assert L.sala_linear_prefill_workspace(F32, 1, 32, 32768, 128, 128) == 0
+    # fp32 tiles by 32 tokens whatever the chunk: segment states of d * d floats
+    f32 = L.sala_linear_prefill_workspace(F32, 1, 32, 32768, 128, 128)
+    assert f32 > 0 and f32 % (128 * 128 * 4) == 0
+    assert f32 == L.sala_linear_prefill_workspace(F32, 1, 32, 32768, 128, 64)
+    assert L.sala_linear_prefill_workspace(F32, 1, 1, 32, 64, 64) == 0  # one tile: one segment, no workspace
     assert lp(B=1, H=32, N=32768, ws=NUL, wsb=0) == WORKSPACE
     assert lp(B=1, H=32, N=32768, ws=A, wsb=need - 1) == WORKSPACE
     assert L.sala_linear_prefill_workspace(BF16, 1, 32, 100, 128, 128) == 0  # one segment: no workspace
