@@ -38,6 +38,11 @@ Functions:
   linear_attention_backward_chunked  chunked reverse recurrence, one head
   linear_prefill_backward            batched [B, H, N, d] driver
   sparse_attention_backward          batched, rows of every query block
+  sparse_attention_backward_dq_rows  dq of chosen (b, hq, t) rows only: a
+                                     row's dq needs only that row's keys
+  sparse_attention_backward_kv_blocks  dk, dv of chosen key blocks only: the
+                                     rows of the query blocks that selected
+                                     them, over the whole group
 """
 
 import math
@@ -159,3 +164,68 @@ def sparse_attention_backward(q, k, v, idx, do, block=64, scale=None):
                 np.add.at(dk[b, kv], toks, scale * (ds.T @ q[b, h, t0:t1]))
                 np.add.at(dv[b, kv], toks, p.T @ do[b, h, t0:t1])
     return dq, dk, dv
+
+
+def sparse_attention_backward_dq_rows(q, k, v, idx, do, rows, block=64, scale=None):
+    """dq_t of sparse_attention_backward for selected (b, hq, t) triples only:
+    p, dp = dO_t . v_s and ds = p (dp - sum_s p dp) over the row's own token set
+    A(t), then dq_t = scale * sum_s ds_s k_s.  Returns [len(rows), d]."""
+    hq, n, d = q.shape[1], q.shape[2], q.shape[-1]
+    g = hq // k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((len(rows), d))
+    for r, (b, h, t) in enumerate(rows):
+        kv = h // g
+        i = t // block
+        toks = np.concatenate([np.arange(j * block, min((j + 1) * block, n))
+                               for j in idx[b, kv, i] if j >= 0])
+        toks = toks[toks <= t]
+        kt = _f64(k[b, kv, toks])
+        logits = scale * (kt @ _f64(q[b, h, t]))
+        logits -= logits.max()
+        p = np.exp(logits)
+        p /= p.sum()
+        dp = _f64(v[b, kv, toks]) @ _f64(do[b, h, t])
+        ds = p * (dp - np.sum(p * dp))
+        out[r] = scale * (ds @ kt)
+    return out
+
+
+def sparse_attention_backward_kv_blocks(q, k, v, idx, do, blocks, block=64, scale=None):
+    """dk and dv of sparse_attention_backward for selected key blocks (b, kv, j)
+    only: the sums over every query block i that lists j (j <= i), every row t
+    of it with s <= t and every head of the group, each row's softmax taken over
+    its own token set.  Returns (dk, dv), each [len(blocks), rows of block j, d]."""
+    hq, n, d = q.shape[1], q.shape[2], q.shape[-1]
+    g = hq // k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nb = n_blocks(n, block)
+    dk = np.zeros((len(blocks), block, k.shape[-1]))
+    dv = np.zeros((len(blocks), block, v.shape[-1]))
+    for r, (b, kv, j) in enumerate(blocks):
+        keys = np.arange(j * block, min((j + 1) * block, n))
+        for i in range(j, nb):
+            sel = [int(x) for x in idx[b, kv, i]]
+            if -1 in sel:
+                sel = sel[:sel.index(-1)]
+            if j not in sel:
+                continue
+            t0, t1 = i * block, min((i + 1) * block, n)
+            toks = np.concatenate([np.arange(x * block, min((x + 1) * block, n)) for x in sel])
+            cols = np.searchsorted(toks, keys) if np.all(np.diff(toks) > 0) else None
+            if cols is None:  # selection not ascending: find the key columns one by one
+                cols = np.array([int(np.nonzero(toks == s_)[0][0]) for s_ in keys])
+            kt, vt = _f64(k[b, kv, toks]), _f64(v[b, kv, toks])
+            for h in range(kv * g, (kv + 1) * g):
+                qi, doi = _f64(q[b, h, t0:t1]), _f64(do[b, h, t0:t1])
+                logits = scale * (qi @ kt.T)
+                logits = np.where(toks[None, :] <= np.arange(t0, t1)[:, None], logits, -np.inf)
+                logits -= logits.max(axis=1, keepdims=True)
+                p = np.exp(logits)
+                p /= p.sum(axis=1, keepdims=True)
+                dp = doi @ vt.T
+                ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+                dk[r, :len(keys)] += scale * (ds[:, cols].T @ qi)
+                dv[r, :len(keys)] += p[:, cols].T @ doi
+    return dk, dv
+

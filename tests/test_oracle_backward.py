@@ -181,3 +181,29 @@ def test_sparse_scale_enters_as_chain_rule():
     np.testing.assert_allclose(b[0], 2 * a[0], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b[1], a[1], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b[2], a[2], rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_dq_rows_equal_the_full_form():
+    """The per-row dq (a row's gradient needs only its own keys) equals the rows
+    of the batched gradient, GQA and ragged tail included."""
+    q, k, v, do, idx = _sparse_case(9, B=2, Hq=6, Hkv=2, n=23, d=5, topk=2)
+    dq, _, _ = BW.sparse_attention_backward(q, k, v, idx, do, block=4)
+    rows = [(0, 0, 0), (1, 5, 22), (0, 3, 9), (1, 2, 17), (0, 4, 4)]
+    got = BW.sparse_attention_backward_dq_rows(q, k, v, idx, do, rows, block=4)
+    for r, (b, h, t) in enumerate(rows):
+        np.testing.assert_allclose(got[r], dq[b, h, t], rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_kv_blocks_equal_the_full_form():
+    """dk, dv of chosen key blocks, summed over the query blocks that selected
+    them, equal the blocks of the batched gradient (GQA, the ragged last
+    block, both batch rows)."""
+    q, k, v, do, idx = _sparse_case(10, B=2, Hq=6, Hkv=2, n=27, d=5, topk=2)
+    _, dk, dv = BW.sparse_attention_backward(q, k, v, idx, do, block=4)
+    blocks = [(0, 0, 0), (1, 1, 3), (0, 1, 6), (1, 0, 5)]
+    gk, gv = BW.sparse_attention_backward_kv_blocks(q, k, v, idx, do, blocks, block=4)
+    for r, (b, kv, j) in enumerate(blocks):
+        m = min(4, 27 - 4 * j)
+        np.testing.assert_allclose(gk[r, :m], dk[b, kv, 4 * j:4 * j + m], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(gv[r, :m], dv[b, kv, 4 * j:4 * j + m], rtol=1e-11, atol=1e-12)
+
