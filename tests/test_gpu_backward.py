@@ -16,7 +16,7 @@ import hybrid_sparse_linear_amd as sala
 from hybrid_sparse_linear_amd import inputs as I
 from oracle import backward as BW
 from oracle import sparse as OS
-from parity import assert_close, host64
+from parity import OnDevice, assert_close, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -155,3 +155,43 @@ def test_sparse_backward_workload_shape():
     assert_close(dq, r[0], I.BF16, "dq")
     assert_close(dk, r[1], I.BF16, "dk", absolute_floor=False)
     assert_close(dv, r[2], I.BF16, "dv", absolute_floor=False)
+
+
+def test_sparse_backward_full_size_samples():
+    """The sparse workload at 131072 tokens (32 query heads on 2 KV heads,
+    top-64 + 1 + 2 over the GPU's selection, 5 % shifted key blocks): dq on
+    sampled rows against the oracle's per-row gradient, and dk, dv of sampled
+    key blocks -- blocks that few query blocks selected, whose sums the oracle
+    forms one by one over those query blocks and every head of the group."""
+    N = 131072
+    say("sparse_prefill_backward 128K samples")
+    x = I.workload3_sparse(0, "cuda", N=N)
+    q, k, v = x["q"], x["k"], x["v"]
+    do = I.normal(q.shape, 131, 1.0, I.BF16, "cuda")
+    idx, _ = sala.sparse_select(q, k)
+    dq, dk, dv = sala.sparse_prefill_backward(q, k, v, idx, do)
+    torch.cuda.synchronize()
+    ih = idx.cpu().numpy()
+    rng = np.random.default_rng(6)
+    rows = [(0, int(h), int(t)) for h, t in zip(rng.integers(0, 32, 24), rng.integers(0, N, 24))]
+    rows += [(0, 0, 0), (0, 31, N - 1), (0, 17, 64 * 66 + 5)]
+    ref = BW.sparse_attention_backward_dq_rows(OnDevice(q), OnDevice(k), OnDevice(v), ih, OnDevice(do), rows, 64)
+    got = np.stack([host64(dq[b, h, t]) for b, h, t in rows])
+    assert_close(got, ref, I.BF16, "dq rows")
+    # key blocks selected by 2 to 6 query blocks (their own and the next one at least)
+    nqb = N // 64
+    blocks = []
+    for kv in range(2):
+        counts = np.zeros(nqb, dtype=int)
+        for i in range(nqb):
+            sel = ih[0, kv, i]
+            sel = sel[sel >= 0]
+            counts[sel[sel <= i]] += 1
+        short = [j for j in range(1, nqb) if 2 <= counts[j] <= 6]
+        blocks += [(0, kv, int(j)) for j in rng.choice(short, 2, replace=False)]
+    say("key blocks", blocks)
+    rk, rv = BW.sparse_attention_backward_kv_blocks(OnDevice(q), OnDevice(k), OnDevice(v), ih, OnDevice(do), blocks, 64)
+    gk = np.stack([host64(dk[b, kv, 64 * j:64 * j + 64]) for b, kv, j in blocks])
+    gv = np.stack([host64(dv[b, kv, 64 * j:64 * j + 64]) for b, kv, j in blocks])
+    assert_close(gk, rk, I.BF16, "dk blocks")
+    assert_close(gv, rv, I.BF16, "dv blocks")
