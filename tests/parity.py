@@ -10,19 +10,25 @@ whole tensor otherwise.
   2. every element:  |g - r| <= tol * max(|r|, rms(r_row), rms(r_slice))
   3. every row:      ||g - r|| / (sqrt(n) * s_row) <= REL_NORM
   4. every slice:    ||g - r|| / ||r|| <= REL_NORM
-with s_row = max(rms(r_row), FLOOR * rms(r_slice)).
+with s_row = max(rms(r_row), FLOOR * rms(r_slice)), FLOOR = 1/4 (bf16) or
+1/16 (fp32).
 
 Rule 1 alone is an absolute 0.02 wherever |r| < 1, which is most outputs at
 the workloads' input scale (row RMS 0.01-0.3), so rules 2-4 hold every head
 and every row to the dtype's relative bound: a 5 % error confined to one head
 fails rule 4, and one confined to one row fails rule 3 in any row whose RMS is
-above 1/80 of its head's.  FLOOR = 1/16 keeps a row whose true value is nearly
-zero by cancellation (a decay-0 head's o_t = (q_t . k_t) v_t with q_t . k_t
-near 0, measured down to 0.0014 of the head's RMS) from being judged against
-its own vanishing scale: there the rounding of the terms, not of the result,
-sets the error.  bf16 rounding of the MFMA operands gives about 1e-3 to 6e-3
-per row; a dropped term, a wrong decay exponent or a wrong index gives 1e-1 or
-more.
+above FLOOR/5 of its head's (1/20 for bf16).  The floor keeps a row whose true
+value is nearly zero by cancellation (a decay-0 head's o_t = (q_t . k_t) v_t
+with q_t . k_t near 0, measured down to 0.0014 of the head's RMS) from being
+judged against its own vanishing scale: there the rounding of the summed
+terms, not of the result, sets the error.  For bf16 that rounding is up to
+2^-9 of each MFMA operand, on terms at about the head's RMS, so the floor times
+REL_NORM must exceed 2^-9: 1/4 x 1e-2 > 2^-9 = 0.00195 (a CPU emulation that
+rounds only P to bf16 exceeds the bound at FLOOR 1/16 on 2 of the 262144 rows
+of a decay-0.43 head's dq at 256K, and reaches half of it at 1/4).  For fp32,
+2^-24 is far below 1/16 x 1e-5.  bf16 operand rounding gives about 1e-3 to
+6e-3 per row; a dropped term, a wrong decay exponent or a wrong index gives
+1e-1 or more.
 
 Block indices are compared bit-exactly, except rows whose float64 oracle
 scores have a gap below NEAR_TIE = 1e-6 between the k-th and (k+1)-th
@@ -40,7 +46,7 @@ import torch
 
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 REL_NORM = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
-FLOOR = 1.0 / 16.0
+FLOOR = {torch.float32: 1.0 / 16.0, torch.bfloat16: 1.0 / 4.0}
 NEAR_TIE = 1e-6
 
 
@@ -72,7 +78,7 @@ def parity_stats(g, r, dtype):
         slice_e = (g - r).reshape(1, -1)
         rows_per_slice = rows_r.shape[0]
     slice_rms = _rms(slice_r, 1)
-    s_row = np.maximum(_rms(rows_r, 1), FLOOR * np.repeat(slice_rms, rows_per_slice))
+    s_row = np.maximum(_rms(rows_r, 1), FLOOR[dtype] * np.repeat(slice_rms, rows_per_slice))
     s_row = np.maximum(s_row, 1e-300)
     r1 = err / (tol * np.maximum(1.0, np.abs(rows_r)))
     slice_rms_row = np.maximum(np.repeat(slice_rms, rows_per_slice), 1e-300)

@@ -85,6 +85,27 @@ def test_linear_backward_full_size_heads():
         assert_close(dsi[0, h], r[3], I.BF16, f"dstate_in head {h}")
 
 
+def test_linear_backward_256K_heads():
+    """The linear layer at the group's 262144 tokens (32 heads, 32 segments of
+    8192 tokens per head, the aggregate passes leaving out keys below 2^-126):
+    every row of the fastest- and the slowest-decaying head against the
+    oracle's chunked backward."""
+    N = 262144
+    say("linear_prefill_backward 256K")
+    x = I.workload2_linear(0, "cuda", N=N)
+    do = I.normal((1, 32, N, 128), 115, 1.0 / math.sqrt(128), I.BF16, "cuda")
+    dec = x["decay"]
+    dq, dk, dv, dsi = sala.linear_prefill_backward(x["q"], x["k"], x["v"], do, dec.cuda())
+    torch.cuda.synchronize()
+    for h in (0, 31):
+        r = BW.linear_attention_backward_chunked(host64(x["q"][0, h]), host64(x["k"][0, h]), host64(x["v"][0, h]),
+                                                 host64(do[0, h]), float(dec[h]), 128)
+        assert_close(dq[0, h], r[0], I.BF16, f"dq head {h}")
+        assert_close(dk[0, h], r[1], I.BF16, f"dk head {h}")
+        assert_close(dv[0, h], r[2], I.BF16, f"dv head {h}")
+        assert_close(dsi[0, h], r[3], I.BF16, f"dstate_in head {h}")
+
+
 SP_BWD_CASES = [
     # B, Hq, Hkv, N, d, topk
     (2, 8, 2, 64 * 20 + 17, 128, 8),     # ragged tail, G = 4 (two head pairs)
