@@ -216,3 +216,43 @@ def test_sparse_backward_full_size_samples():
     gv = np.stack([host64(dv[b, kv, 64 * j:64 * j + 64]) for b, kv, j in blocks])
     assert_close(gk, rk, I.BF16, "dk blocks")
     assert_close(gv, rv, I.BF16, "dv blocks")
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 65])
+@pytest.mark.parametrize("dt", [I.BF16, I.F32], ids=["bf16", "f32"])
+def test_linear_backward_short_sequences(N, dt):
+    """A single token, a few tokens, one full chunk and a chunk plus one token,
+    with a carried state and a state gradient."""
+    B, H, d = 1, 2, 64
+    say("linear_prefill_backward short", N, dt)
+    std = 1.0 / math.sqrt(d)
+    x = I.linear_inputs(B, H, N, d, dt, 116, 0, std)
+    do = I.normal((B, H, N, d), 117, std, dt)
+    decay = torch.tensor([0.5, 1.0], dtype=torch.float32)
+    s0 = I.normal((B, H, d, d), 118, 1.0 / d)
+    ds = I.normal((B, H, d, d), 119, 1.0 / d)
+    dq, dk, dv, dsi = sala.linear_prefill_backward(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(do), dev(decay),
+                                                   dev(s0), dev(ds), chunk=64)
+    torch.cuda.synchronize()
+    r = BW.linear_prefill_backward(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(do),
+                                   decay.double().numpy(), host64(s0), host64(ds))
+    for name, g, ref in (("dq", dq, r[0]), ("dk", dk, r[1]), ("dv", dv, r[2])):
+        assert_close(g, ref, dt, name)
+    assert_close(dsi, r[3], torch.float32 if dt == I.F32 else I.BF16, "dstate_in")
+
+
+@pytest.mark.parametrize("N", [1, 7, 64, 65])
+def test_sparse_backward_short_sequences(N):
+    """The first token alone (its query gets no gradient, its value gets dO),
+    a few tokens inside the first block, one block, a block plus one token."""
+    case = (1, 4, 2, N, 128, 3)
+    say("sparse_prefill_backward short", case)
+    x, do, ridx = _sparse_bwd_case(case, 123)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    idx = dev(torch.from_numpy(ridx).to(torch.int32))
+    dq, dk, dv = sala.sparse_prefill_backward(q, k, v, idx, dev(do))
+    torch.cuda.synchronize()
+    r = BW.sparse_attention_backward(host64(x["q"]), host64(x["k"]), host64(x["v"]), ridx, host64(do), 64)
+    assert_close(dq, r[0], I.BF16, "dq")
+    assert_close(dk, r[1], I.BF16, "dk", absolute_floor=False)
+    assert_close(dv, r[2], I.BF16, "dv", absolute_floor=False)
