@@ -444,6 +444,48 @@ __global__ __launch_bounds__(64) void bwd_lists(const uint32_t *__restrict__ bit
     items[(size_t)bkv * items_per_bkv + mt.z + u] = int4{j, mt.x + u * ITEM_QB, min(ITEM_QB, mt.y - u * ITEM_QB), 0};
 }
 
+// One workgroup per bkv: the order in which the dk/dv pass takes the items,
+// sorted by the first query block of each item (a counting sort over buckets
+// of 2^shift query blocks).  Each item still writes its own slot, so results
+// do not depend on this order.
+__global__ __launch_bounds__(1024) void bwd_order(const int *__restrict__ pairs, const int4 *__restrict__ items,
+                                                  const int *__restrict__ nitems, int *__restrict__ order,
+                                                  int pairs_per_bkv, int items_per_bkv, int shift) {
+  constexpr int MAXB = 8192, PER = MAXB / 1024;
+  __shared__ int hist[MAXB];
+  __shared__ int wsum[16];
+  const int bkv = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = nitems[bkv];
+  const int4 *it = items + (size_t)bkv * items_per_bkv;
+  const int *pl = pairs + (size_t)bkv * pairs_per_bkv;
+  int *ord = order + (size_t)bkv * items_per_bkv;
+  for (int u = tid; u < MAXB; u += 1024) hist[u] = 0;
+  __syncthreads();
+  for (int r = tid; r < n; r += 1024) atomicAdd(&hist[pl[it[r].y] >> shift], 1);
+  __syncthreads();
+  int loc[PER], sum = 0;  // exclusive scan: thread tid owns buckets PER*tid ..
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    loc[u] = sum;
+    sum += hist[PER * tid + u];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int x = 0; x < w; ++x) before += wsum[x];
+  const int base = before + incl - sum;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) hist[PER * tid + u] = base + loc[u];
+  __syncthreads();
+  for (int r = tid; r < n; r += 1024) ord[atomicAdd(&hist[pl[it[r].y] >> shift], 1)] = r;
+}
+
 // ------------------------------------------------------------------ dk / dv pass
 template <int D>
 __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -451,17 +493,25 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
                                                       const uint16_t *__restrict__ dout,
                                                       const float *__restrict__ lse2, const float *__restrict__ drow,
                                                       const int *__restrict__ pairs, const int4 *__restrict__ items,
-                                                      const int *__restrict__ nitems, float *__restrict__ partial,
-                                                      int Hq, int Hkv, int N, int pairs_per_bkv, int items_per_bkv,
-                                                      float scale) {
+                                                      const int *__restrict__ nitems, const int *__restrict__ order,
+                                                      float *__restrict__ partial, int Hq, int Hkv, int N,
+                                                      int pairs_per_bkv, int items_per_bkv, float scale) {
   using Cf = BwCfg<D>;
   __shared__ __attribute__((aligned(16))) char qb0[Cf::TB], qb1[Cf::TB];
   __shared__ __attribute__((aligned(16))) char ob0[Cf::TB], ob1[Cf::TB];
   __shared__ __attribute__((aligned(16))) float st0[2][256], st1[2][256];  // lse2, D of the 64 rows (+ pad)
 
+  // Workgroup x runs on XCD x % 8.  Each XCD takes runs of 8 consecutive items
+  // of the sorted order in turn, so the items resident on one XCD at a time
+  // start at nearby query blocks and stage mostly the same Q and dO rows,
+  // which its L2 then serves.
+  const int ipb = (items_per_bkv + 63) & ~63;
   const int x = blockIdx.x;
-  const int bkv = x / items_per_bkv, r = x % items_per_bkv;
-  if (r >= nitems[bkv]) return;
+  const int bkv = x / ipb, xr = x % ipb;
+  const int y = xr >> 3;                       // position in this XCD's sequence
+  const int rr = (y >> 3) * 64 + (xr & 7) * 8 + (y & 7);
+  if (rr >= nitems[bkv]) return;
+  const int r = order[(size_t)bkv * items_per_bkv + rr];  // the item this workgroup takes
   const int4 it = items[(size_t)bkv * items_per_bkv + r];
   const int j = it.x, start = it.y, len = it.z;
   const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
@@ -604,7 +654,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(const float *__restrict__ part
 
 // Workspace layout (each part 256-byte aligned)
 struct BwLayout {
-  size_t lse, drow, bitmap, meta, nitems, pairs, items, partial, total;
+  size_t lse, drow, bitmap, meta, nitems, pairs, items, order, partial, total;
   int NQB, WPR, pairs_per_bkv, items_per_bkv;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -624,6 +674,7 @@ BwLayout bw_layout(int B, int Hq, int Hkv, int N, int d, int n_sel) {
   L.nitems = take(BKV * 4);
   L.pairs = take(BKV * L.pairs_per_bkv * 4);
   L.items = take(BKV * L.items_per_bkv * 16);
+  L.order = take(BKV * L.items_per_bkv * 4);
   L.partial = take(BKV * L.items_per_bkv * 2 * BB * (size_t)d * 4);
   L.total = off;
   return L;
@@ -640,6 +691,7 @@ hipError_t run_bwd(const SparseBackwardArgs &a, hipStream_t st) {
   int *nitems = reinterpret_cast<int *>(ws + L.nitems);
   int *pairs = reinterpret_cast<int *>(ws + L.pairs);
   int4 *items = reinterpret_cast<int4 *>(ws + L.items);
+  int *order = reinterpret_cast<int *>(ws + L.order);
   float *partial = reinterpret_cast<float *>(ws + L.partial);
   const int NQB = L.NQB, BKV = a.B * a.Hkv, G = a.Hq / a.Hkv;
   const int HG = (G + 3) / 4;
@@ -656,9 +708,14 @@ hipError_t run_bwd(const SparseBackwardArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(bwd_counts, dim3(BKV), dim3(1024), 0, st, bitmap, meta, nitems, NQB, L.WPR);
   hipLaunchKernelGGL(bwd_lists, dim3(BKV * NQB), dim3(64), 0, st, bitmap, meta, pairs, items, NQB, L.WPR,
                      L.pairs_per_bkv, L.items_per_bkv);
-  hipLaunchKernelGGL((sparse_bwd_dkv<D>), dim3(BKV * L.items_per_bkv), dim3(256), 0, st, (const uint16_t *)a.q,
-                     (const uint16_t *)a.k, (const uint16_t *)a.v, (const uint16_t *)a.dout, lse, drow, pairs, items,
-                     nitems, partial, a.Hq, a.Hkv, a.N, L.pairs_per_bkv, L.items_per_bkv, a.scale);
+  int shift = 0;
+  while (((NQB - 1) >> shift) >= 8192) ++shift;  // at most 8192 buckets of first query blocks
+  hipLaunchKernelGGL(bwd_order, dim3(BKV), dim3(1024), 0, st, pairs, items, nitems, order, L.pairs_per_bkv,
+                     L.items_per_bkv, shift);
+  hipLaunchKernelGGL((sparse_bwd_dkv<D>), dim3(BKV * ((L.items_per_bkv + 63) & ~63)), dim3(256), 0, st,
+                     (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const uint16_t *)a.dout,
+                     lse, drow, pairs, items, nitems, order, partial, a.Hq, a.Hkv, a.N, L.pairs_per_bkv,
+                     L.items_per_bkv, a.scale);
   hipLaunchKernelGGL((bwd_reduce<D>), dim3(BKV * NQB), dim3(256), 0, st, partial, meta, (uint16_t *)a.dk,
                      (uint16_t *)a.dv, a.N, NQB, L.items_per_bkv);
   return hipGetLastError();
