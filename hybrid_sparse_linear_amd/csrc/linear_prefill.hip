@@ -501,10 +501,13 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   auto qfrag = [&](int s) -> u32x4 {
     return lds_load<u32x4>(lds + Fz::QN, qq * Cf::ROWB + (((4 * s + g) ^ fkv(qq)) & (Cf::NCH - 1)) * 16u);
   };
-  // this lane's output row, gated by gv when given
+  // this lane's output row, gated by gv when given; 16-byte stores of eight
+  // consecutive d_v values (a row's four lanes cover 64 contiguous bytes per
+  // store instead of 32 with one 8-byte store per d_v tile)
   auto store_out = [&](int c0, int m, const f32x4 (&Oacc)[Cf::DVW], const u32x2 (&gv)[Cf::DVW], bool gated) {
     if (qq < m) {
       uint16_t *orow = ob + (size_t)(REV ? N - 1 - (c0 + qq) : c0 + qq) * D;
+      u32x2 ov[Cf::DVW];
 #pragma unroll
       for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
         f32x4 x = Oacc[dvi];
@@ -514,8 +517,22 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
           x[2] *= sigmoid_fast(bf16lo(gv[dvi][1]));
           x[3] *= sigmoid_fast(bf16hi(gv[dvi][1]));
         }
-        *reinterpret_cast<u32x2 *>(orow + 16 * (dvb + dvi) + 4 * g) =
-            u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        ov[dvi] = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      }
+      // lanes l and l ^ 16 (g and g ^ 1) swap halves so that each holds eight
+      // consecutive d_v values: g even tile dvi, g odd tile dvi + 1 (the two
+      // lanes share qq, so both take this branch or neither does)
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; dvi += 2) {
+        u32x2 a = ov[dvi], b = ov[dvi + 1];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(a[e], b[e], false, false);
+          a[e] = sw[0];
+          b[e] = sw[1];
+        }
+        const int tile = dvb + dvi + (g & 1);
+        *reinterpret_cast<u32x4 *>(orow + 16 * tile + 8 * (g >> 1)) = u32x4{a[0], a[1], b[0], b[1]};
       }
     }
   };
