@@ -13,9 +13,12 @@
 // so that B*H*segments workgroups fill the 256 CUs.
 //   pass 1  lin_seg_aggregate: each segment except the last computes its own
 //           decayed state contribution A_m = sum_{s in m} lam^(end-1-s) k_s v_s^T
-//           (fp32, written to the workspace).
-//   pass 2  lin_seg_scan: an element-wise scan over segments turns the A_m into
-//           the state entering every segment, S_in(m) = lam^len S_in(m-1) + A_{m-1}.
+//           (fp32, written to the workspace), in parts of at most 32 chunks
+//           spread over the CUs; parts whose keys cannot reach the segment's
+//           end are left out.
+//   pass 2  lin_seg_scan: an element-wise scan over segments sums each
+//           segment's parts into A_m and turns the A_m into the state entering
+//           every segment, S_in(m) = lam^len S_in(m-1) + A_{m-1}.
 //   pass 3  lin_seg_output: each segment walks its chunks.  Per chunk of C tokens:
 //             O^T  = lam^(i+1) (S^T Q^T)  +  V^T (decay-masked K Q^T)
 //             S    = lam^C S + (diag(lam^(C-1-j)) K)^T V
@@ -337,106 +340,188 @@ __device__ __forceinline__ int agg_first_row(float lam, int t_begin, int t_end, 
 }
 
 // F: k is normalised and rotated as it is staged (the fused form).
+// Part p of segment seg (parts of part_len tokens, whole chunks):
+// A_{seg,p} = sum over the part's keys of lam^(part end-1-s) k_s v_s^T, from the
+// first key that reaches the segment's end (agg_first_row over the whole
+// segment); a part wholly before it is left out (and skipped by the scan,
+// which applies the same test).  Persistent, one workgroup per CU: each
+// workgroup first lists the parts that are not left out (a prefix count per
+// (b, h, segment), b and h from the last, whose slow decay keeps the most
+// parts) and then takes every gridDim.x-th entry of that dense list, so the
+// work spreads evenly whichever parts the decays leave out.
+constexpr int AGG_MAX_PAIRS = 4096;  // (b, h, segment) pairs one list can hold
 template <int C, int D, bool F, bool REV>
 __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v,
                                                          const float *__restrict__ decay,
-                                                         float *__restrict__ seg_state, int H, int N,
-                                                         int seg_len, int nseg, NbK nb) {
+                                                         float *__restrict__ seg_state, int H, int N, int BH,
+                                                         int seg_len, int nseg, int part_len, int nparts, NbK nb) {
   using Cf = LinCfg<C, D>;
   using Fz = LinF<C, D>;
   __shared__ __attribute__((aligned(16))) char lds[F ? Fz::LDS : Cf::LDS];
+  __shared__ int pre[AGG_MAX_PAIRS + 1];  // pre[j]: parts kept by the pairs before j
+  __shared__ int wtot[8];
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int nagg = nseg - 1;
-  // (b, h) from the last: with slope decays the later heads decay slowest and
-  // keep the most chunks, so the longest workgroups are dispatched first.
-  const int bh = (int)(gridDim.x / nagg) - 1 - (int)(blockIdx.x / nagg), seg = blockIdx.x % nagg;
-  const int h = bh % H;
-  const float lam = decay ? decay[h] : 1.f;
-  const int t_end = min(N, (seg + 1) * seg_len), t_begin = agg_first_row(lam, seg * seg_len, t_end, C);
+  const int nsa = nseg - 1, npairs = BH * nsa;  // the host keeps npairs <= AGG_MAX_PAIRS
+  // pair j = (bh, seg): bh = BH - 1 - j / nsa, seg = j % nsa
+  auto first_part = [&](int j) {
+    const int bh = BH - 1 - j / nsa, seg = j % nsa;
+    const float lam = decay ? decay[bh % H] : 1.f;
+    const int first = agg_first_row(lam, seg * seg_len, (seg + 1) * seg_len, C);
+    return (first - seg * seg_len) / part_len;  // parts before it are left out
+  };
+  {
+    int cnt[8], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * tid + e;
+      cnt[e] = j < npairs ? nparts - first_part(j) : 0;
+      sum += cnt[e];
+    }
+    int incl = sum;  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (l >= o) incl += y;
+    }
+    if (l == 63) wtot[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int u = 0; u < w; ++u) run += wtot[u];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * tid + e;
+      if (j <= npairs) pre[j] = run;
+      run += cnt[e];
+    }
+    __syncthreads();
+  }
+  const int total = pre[npairs];
   float *pw = reinterpret_cast<float *>(lds + Cf::PW) + Cf::PWZ;  // pw[n] = lam^n, 0 for n < 0
   float *rw = reinterpret_cast<float *>(lds + Cf::RW);
-  for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);
-  const uint16_t *kb = k + (size_t)bh * N * D;
-  const uint16_t *vb = v + (size_t)bh * N * D;
   const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
   const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
-
-  f32x4 Sacc[Cf::SDV];
-#pragma unroll
-  for (int a = 0; a < Cf::SDV; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (F) {
-    nb_tables<C, D>(lds, tid, nb);
-    const bool norm = nb.gk != nullptr, rope = nb.rope_base > 0.f;
-    const int hc = tid % Fz::HC;
-    const auto kr = buf_rsrc(kb, (uint32_t)N * D * 2u), vr = buf_rsrc(vb, (uint32_t)N * D * 2u);
-    u32x4 xk[Fz::NSF][2], xv[Fz::NSF][2];
-    load_rows_f<C, D, REV>(kr, tid, t_begin, t_end, xk, N);
-    load_rows_f<C, D, REV>(vr, tid, t_begin, t_end, xv, N);
-    for (int c0 = t_begin; c0 < t_end; c0 += C) {
-      const int m = min(C, t_end - c0);
-      __syncthreads();
-      float bt[8], cs[8], sn[8];
-      if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
-#pragma unroll
-      for (int u = 0; u < Fz::NSF; ++u) {
-        const int row = tid / Fz::HC + Fz::RPF * u;
-        if (rope) rope_cs<C, D>(lds, hc, row, bt, cs, sn);
-        nb_row<C, D>(lds, hc, norm, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
-        __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
-      }
-      store_rows_f<C, D>(lds + Cf::KN, tid, m, xk);
-      store_rows_f<C, D>(lds + Cf::VN, tid, m, xv);
-      if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
-      __syncthreads();
-      if (c0 + C < t_end) {
-        load_rows_f<C, D, REV>(kr, tid, c0 + C, t_end, xk, N);
-        load_rows_f<C, D, REV>(vr, tid, c0 + C, t_end, xv, N);
-      }
-      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+  if constexpr (F) nb_tables<C, D>(lds, tid, nb);
+  int h_tab = -1;  // head whose lam^n is in pw
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = npairs - 1;  // the pair j with pre[j] <= item < pre[j + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= item) lo = mid;
+      else hi = mid - 1;
     }
-  } else {
-    u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
-    load_kv<C, D, REV>(kb, vb, tid, t_begin, t_end, N, xk, xv);
-    for (int c0 = t_begin; c0 < t_end; c0 += C) {
-      const int m = min(C, t_end - c0);
-      __syncthreads();
-      store_kv<C, D>(lds, tid, m, xk, xv);
-      if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
-      __syncthreads();
-      if (c0 + C < t_end) load_kv<C, D, REV>(kb, vb, tid, c0 + C, t_end, N, xk, xv);
-      state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+    const int j = lo;
+    const int bh = BH - 1 - j / nsa, seg = j % nsa;
+    const int part = nparts - (pre[j + 1] - pre[j]) + (item - pre[j]);
+    const int h = bh % H;
+    const float lam = decay ? decay[h] : 1.f;
+    const int seg_end = (seg + 1) * seg_len;
+    const int first = agg_first_row(lam, seg * seg_len, seg_end, C);
+    const int p_begin = seg * seg_len + part * part_len, t_end = min(seg_end, p_begin + part_len);
+    const int t_begin = max(p_begin, first);
+    __syncthreads();  // the previous part's readers of the tables and tiles are done
+    if (h != h_tab) {
+      for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);
+      h_tab = h;
     }
+    const uint16_t *kb = k + (size_t)bh * N * D;
+    const uint16_t *vb = v + (size_t)bh * N * D;
+    f32x4 Sacc[Cf::SDV];
+#pragma unroll
+    for (int a = 0; a < Cf::SDV; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (F) {
+      const bool norm = nb.gk != nullptr, rope = nb.rope_base > 0.f;
+      const int hc = tid % Fz::HC;
+      const auto kr = buf_rsrc(kb, (uint32_t)N * D * 2u), vr = buf_rsrc(vb, (uint32_t)N * D * 2u);
+      u32x4 xk[Fz::NSF][2], xv[Fz::NSF][2];
+      load_rows_f<C, D, REV>(kr, tid, t_begin, t_end, xk, N);
+      load_rows_f<C, D, REV>(vr, tid, t_begin, t_end, xv, N);
+      for (int c0 = t_begin; c0 < t_end; c0 += C) {
+        const int m = min(C, t_end - c0);
+        __syncthreads();
+        float bt[8], cs[8], sn[8];
+        if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
+#pragma unroll
+        for (int u = 0; u < Fz::NSF; ++u) {
+          const int row = tid / Fz::HC + Fz::RPF * u;
+          if (rope) rope_cs<C, D>(lds, hc, row, bt, cs, sn);
+          nb_row<C, D>(lds, hc, norm, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
+          __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
+        }
+        store_rows_f<C, D>(lds + Cf::KN, tid, m, xk);
+        store_rows_f<C, D>(lds + Cf::VN, tid, m, xv);
+        if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
+        __syncthreads();
+        if (c0 + C < t_end) {
+          load_rows_f<C, D, REV>(kr, tid, c0 + C, t_end, xk, N);
+          load_rows_f<C, D, REV>(vr, tid, c0 + C, t_end, xv, N);
+        }
+        state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+      }
+    } else {
+      u32x4 xk[Cf::NSTG], xv[Cf::NSTG];
+      load_kv<C, D, REV>(kb, vb, tid, t_begin, t_end, N, xk, xv);
+      for (int c0 = t_begin; c0 < t_end; c0 += C) {
+        const int m = min(C, t_end - c0);
+        __syncthreads();
+        store_kv<C, D>(lds, tid, m, xk, xv);
+        if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
+        __syncthreads();
+        if (c0 + C < t_end) load_kv<C, D, REV>(kb, vb, tid, c0 + C, t_end, N, xk, xv);
+        state_update<C, D>(lds, sdk, sdv0, g, lane_tr, xtr, pw[m], Sacc);
+      }
+    }
+    float *out = seg_state + (((size_t)bh * nseg + seg) * nparts + part) * D * D;
+#pragma unroll
+    for (int a = 0; a < Cf::SDV; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] = Sacc[a][i];
   }
-  float *out = seg_state + ((size_t)bh * nseg + seg) * D * D;
-#pragma unroll
-  for (int a = 0; a < Cf::SDV; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[(size_t)(16 * sdk + 4 * g + i) * D + 16 * (sdv0 + a) + lr] = Sacc[a][i];
 }
 
 // ---------------------------------------------------------------- pass 2
-// seg_state[bh][m] holds A_m for m < nseg-1 on entry, S_in(m) for every m on exit.
+// seg_state[bh][m][p] holds A_{m,p} for m < nseg-1 on entry (parts the
+// aggregate pass left out are not read), and seg_state[bh][m][0] holds
+// S_in(m) for every m on exit.  A_m = sum_p lam^(end of m - end of p) A_{m,p}.
 // dir.state_T: state_in is read transposed; dir.lag: the initial state's first
 // transition decays by lam^(seg_len-1) (it enters one step late).
+// C: the chunk the aggregate pass rounds its first key to (agg_first_row).
 __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_state,
                                                     const float *__restrict__ state_in,
                                                     const float *__restrict__ decay, int H, int D, int DD,
-                                                    int N, int seg_len, int nseg, LinDir dir) {
+                                                    int N, int seg_len, int nseg, int part_len, int nparts, int C,
+                                                    LinDir dir) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= DD) return;
   const int h = bh % H;
-  const double lam = decay ? (double)decay[h] : 1.0;
+  const float lam_f = decay ? decay[h] : 1.f;
+  const double lam = (double)lam_f;
   const float lam_seg = (float)pow(lam, (double)seg_len);
   const float lam_first = dir.lag ? (float)pow(lam, (double)(seg_len - 1)) : lam_seg;
   const int e_in = dir.state_T ? (e % D) * D + e / D : e;
   float s = state_in ? state_in[(size_t)bh * DD + e_in] : 0.f;
-  float *base = seg_state + (size_t)bh * nseg * DD + e;
+  float *base = seg_state + (size_t)bh * nseg * nparts * DD + e;
+  // every aggregated segment is whole (it ends before the last one), so its
+  // parts' weights are the same for every m: walking back from the segment
+  // end, lam^0 for the last part (len_last tokens), then lam^len_last,
+  // lam^(len_last + part_len), ...
+  const int len_last = seg_len - (nparts - 1) * part_len;
+  const double lam_last = pow(lam, (double)len_last), lam_part = pow(lam, (double)part_len);
   for (int m = 0; m < nseg; ++m) {
-    const float a = (m + 1 < nseg) ? base[(size_t)m * DD] : 0.f;
-    base[(size_t)m * DD] = s;
+    float a = 0.f;
+    if (m + 1 < nseg) {
+      const int seg_end = (m + 1) * seg_len, first = agg_first_row(lam_f, m * seg_len, seg_end, C);
+      double wgt = 1.0;
+      for (int p = nparts - 1; p >= 0; --p) {
+        const int p_end = m * seg_len + min(seg_len, (p + 1) * part_len);
+        if (first >= p_end) break;  // this part and all before it were left out by the aggregate pass
+        a = fmaf((float)wgt, base[((size_t)m * nparts + p) * DD], a);
+        wgt *= (p == nparts - 1) ? lam_last : lam_part;
+      }
+    }
+    base[(size_t)m * nparts * DD] = s;
     s = fmaf(m == 0 ? lam_first : lam_seg, s, a);
   }
 }
@@ -847,22 +932,60 @@ __global__ __launch_bounds__(256) void lin_f32_pass(const float *__restrict__ q,
   }
 }
 
-// Segments: about 4 workgroups per CU over all (b, h), whole chunks each, and
-// no segment shorter than min_chunks chunks.  Each output workgroup starts by
-// reading its d x d entry state, and each segment boundary costs an aggregate
-// of up to a segment of keys, so short segments cost more than the occupancy
-// they buy: at 32K tokens and 32 heads, 8 segments of 32 chunks per head ran
-// the bf16 layer in 0.37 ms against 0.43 ms with 32 segments of 8 chunks.
-// The fp32 path (VALU-bound, tiles of 32 tokens) keeps every tile parallel.
-void seg_plan(int BH, int N, int C, int min_chunks, int *seg_len, int *nseg) {
-  const int target = 1024;
+// Segment plans.  The output pass runs one workgroup per (b, h, segment) in
+// sequence over the segment's chunks, so its time is about
+//   rounds * chunks per segment,  rounds = ceil(B*H*segments / 256 CUs);
+// the bf16 plan takes, from enough segments to give every CU a workgroup, the
+// number that minimises that, the fewest among equals, with no segment
+// shorter than 32 chunks: each workgroup starts by reading its d x d entry
+// state, and every segment boundary needs an aggregate of the keys that reach
+// it (R28 keeps that short for fast-decaying heads and whole for slow ones),
+// so fewer boundaries mean less aggregate work.  At 32 heads that is 8
+// segments per head from 32K tokens up (one round).  The aggregates are
+// computed over parts of at most 32 chunks, which the aggregate pass deals
+// out evenly over the CUs.
+// The fp32 path (VALU-bound, tiles of 32 tokens) keeps about 4 workgroups per
+// CU and one part per segment.
+struct SegPlan {
+  int seg_len, nseg, part_len, nparts;
+};
+constexpr int NCU = 256;  // compute units of an MI355X
+SegPlan seg_plan_bf16(int BH, int N, int C) {
   const int nchunks = (N + C - 1) / C;
-  int want = (target + BH - 1) / BH;
-  if (want > nchunks / min_chunks) want = nchunks / min_chunks;
+  // at most AGG_MAX_PAIRS - 1 (b, h, segment) pairs with an aggregate
+  const int max_seg = max(1, min(min(nchunks / 32, 1024), (AGG_MAX_PAIRS - 1) / BH + 1));
+  const int min_seg = min(max_seg, max(1, NCU / BH));  // a workgroup for every CU where that is possible
+  int best = 1;
+  long long best_cost = -1;
+  for (int ns = min_seg; ns <= max_seg; ++ns) {
+    const long long rounds = ((long long)BH * ns + NCU - 1) / NCU;
+    const long long cost = rounds * ((nchunks + ns - 1) / ns);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ns;
+    }
+  }
+  SegPlan p;
+  const int cps = (nchunks + best - 1) / best;  // chunks per segment
+  p.seg_len = cps * C;
+  p.nseg = (N + p.seg_len - 1) / p.seg_len;
+  const int ppc = max(min(cps, 32), (cps + 63) / 64);  // chunks per aggregate part (at most 64 parts)
+  p.nparts = (cps + ppc - 1) / ppc;
+  p.part_len = ppc * C;
+  return p;
+}
+SegPlan seg_plan_f32(int BH, int N) {
+  const int nchunks = (N + FT - 1) / FT;
+  int want = (1024 + BH - 1) / BH;
+  if (want > nchunks) want = nchunks;
   if (want < 1) want = 1;
-  const int cps = (nchunks + want - 1) / want;  // chunks per segment
-  *seg_len = cps * C;
-  *nseg = (N + *seg_len - 1) / *seg_len;
+  SegPlan p;
+  const int cps = (nchunks + want - 1) / want;
+  p.seg_len = cps * FT;
+  p.nseg = (N + p.seg_len - 1) / p.seg_len;
+  p.part_len = p.seg_len;
+  p.nparts = 1;
+  return p;
 }
 
 template <int C, int D, bool REV>
@@ -874,26 +997,31 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
   const bool k_transformed = nb.gk != nullptr || nb.rope_base > 0.f;
   const int BH = a.B * a.H;
-  int seg_len, nseg;
-  seg_plan(BH, a.N, C, 32, &seg_len, &nseg);
+  const SegPlan pl = seg_plan_bf16(BH, a.N, C);
+  const int seg_len = pl.seg_len, nseg = pl.nseg;
   float *ws = static_cast<float *>(a.ws);
   const size_t DD = (size_t)D * D;
   const float *seg_state = a.state_in;  // nseg == 1: segment 0 starts from state_in
+  size_t seg_stride = DD;
   int sin_T = a.state_T;
   if (nseg > 1) {
+    const dim3 agrid(min(BH * (nseg - 1) * pl.nparts, NCU));
     if (k_transformed)
-      hipLaunchKernelGGL((lin_seg_aggregate<C, D, true, REV>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
-                         (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
+      hipLaunchKernelGGL((lin_seg_aggregate<C, D, true, REV>), agrid, dim3(512), 0, st, (const uint16_t *)a.k,
+                         (const uint16_t *)a.v, a.decay, ws, a.H, a.N, BH, seg_len, nseg, pl.part_len, pl.nparts,
+                         nb);
     else
-      hipLaunchKernelGGL((lin_seg_aggregate<C, D, false, REV>), dim3(BH * (nseg - 1)), dim3(512), 0, st,
-                         (const uint16_t *)a.k, (const uint16_t *)a.v, a.decay, ws, a.H, a.N, seg_len, nseg, nb);
+      hipLaunchKernelGGL((lin_seg_aggregate<C, D, false, REV>), agrid, dim3(512), 0, st, (const uint16_t *)a.k,
+                         (const uint16_t *)a.v, a.decay, ws, a.H, a.N, BH, seg_len, nseg, pl.part_len, pl.nparts,
+                         nb);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws,
-                       a.state_in, a.decay, a.H, D, (int)DD, a.N, seg_len, nseg, dir);
+                       a.state_in, a.decay, a.H, D, (int)DD, a.N, seg_len, nseg, pl.part_len, pl.nparts, C, dir);
     seg_state = ws;
+    seg_stride = DD * pl.nparts;  // S_in(m) sits in part slot 0 of segment m
     sin_T = 0;  // the scan wrote the segment states in the plain layout
   }
   hipLaunchKernelGGL((lin_seg_output<C, D, REV>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
-                     (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, DD,
+                     (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, seg_stride,
                      a.state_out, a.H, a.N, seg_len, nseg, nb, dir, sin_T);
   return hipGetLastError();
 }
@@ -907,8 +1035,8 @@ template <int D>
 hipError_t run_f32(const LinearPrefillArgs &a, hipStream_t st) {
   const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
   const int BH = a.B * a.H;
-  int seg_len, nseg;
-  seg_plan(BH, a.N, FT, 1, &seg_len, &nseg);
+  const SegPlan pl = seg_plan_f32(BH, a.N);
+  const int seg_len = pl.seg_len, nseg = pl.nseg;
   float *ws = static_cast<float *>(a.ws);
   const size_t DD = (size_t)D * D;
   const float *q = static_cast<const float *>(a.q), *k = static_cast<const float *>(a.k),
@@ -917,7 +1045,7 @@ hipError_t run_f32(const LinearPrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((lin_f32_pass<D, false>), dim3(BH * (nseg - 1)), dim3(256), 0, st, q, k, v, nullptr, a.decay,
                        ws, nullptr, nullptr, a.H, a.N, seg_len, nseg, dir, 0);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws, a.state_in,
-                       a.decay, a.H, D, (int)DD, a.N, seg_len, nseg, dir);
+                       a.decay, a.H, D, (int)DD, a.N, seg_len, nseg, pl.part_len, pl.nparts, FT, dir);
   }
   // one segment: the pass reads the caller's initial state itself (transposed if asked)
   hipLaunchKernelGGL((lin_f32_pass<D, true>), dim3(BH * nseg), dim3(256), 0, st, q, k, v, static_cast<float *>(a.o),
@@ -928,11 +1056,9 @@ hipError_t run_f32(const LinearPrefillArgs &a, hipStream_t st) {
 }  // namespace
 
 size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk) {
-  int seg_len, nseg;
-  if (dtype == 1) seg_plan(B * H, N, chunk, 32, &seg_len, &nseg);
-  else seg_plan(B * H, N, FT, 1, &seg_len, &nseg);  // the fp32 path tiles by FT tokens
-  if (nseg <= 1) return 0;
-  return (size_t)B * H * nseg * d * d * sizeof(float);
+  const SegPlan pl = dtype == 1 ? seg_plan_bf16(B * H, N, chunk) : seg_plan_f32(B * H, N);
+  if (pl.nseg <= 1) return 0;
+  return (size_t)B * H * pl.nseg * pl.nparts * d * d * sizeof(float);
 }
 
 hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st) {
