@@ -36,11 +36,18 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 # Packed fp32 VALU ops stay disabled in all device code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source flags.  The sparse gradient kernels run one wave per SIMD per
+# workgroup; there the compiler would keep the dK / dV accumulators in AGPRs
+# and copy all 64 of them to VGPRs and back on every step (262 v_accvgpr moves
+# in the loop); the VGPR form of the MFMAs keeps them in place.
+PER_SOURCE = {"sparse_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, verbose, build_dir, extra):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + extra + (DEVICE if src.endswith(".hip") else []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    own = PER_SOURCE.get(os.path.basename(src), [])
+    cmd = ([HIPCC] + COMMON + extra + (DEVICE if src.endswith(".hip") else []) + own +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -71,7 +71,10 @@ template <int D, int NT>
 __device__ __forceinline__ void load_tile(const uint16_t *base, int valid_rows, char *dst, int tid) {
   using Cf = BwCfg<D>;
   constexpr int PER = Cf::TB / 16 / NT;
-  const auto r = buf_rsrc(base, (uint32_t)min(max(valid_rows, 0), BB) * D * 2u);
+  // the row count through readfirstlane: a clamp the compiler puts on the VALU
+  // would make the resource look divergent (a waterfall loop around every load)
+  const uint32_t rows = (uint32_t)__builtin_amdgcn_readfirstlane(min(max(valid_rows, 0), BB));
+  const auto r = buf_rsrc(base, rows * D * 2u);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
     load_tile<D, 256>(q + rb * D, valid, qd, tid);
     load_tile<D, 256>(dout + rb * D, valid, od, tid);
     if (w == 0) {
-      const uint32_t nb = (uint32_t)max(0, min(BB, valid)) * 4u;
+      const uint32_t nb = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(BB, valid))) * 4u;  // uniform (see load_tile)
       bload16_lds(buf_rsrc(lse2 + rb, nb), sd[0], 16u * l);
       bload16_lds(buf_rsrc(drow + rb, nb), sd[1], 16u * l);
     }
