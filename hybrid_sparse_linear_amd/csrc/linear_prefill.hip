@@ -411,9 +411,9 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
       if (pre[mid] <= item) lo = mid;
       else hi = mid - 1;
     }
-    const int j = lo;
+    const int j = __builtin_amdgcn_readfirstlane(lo);  // uniform: read from LDS, the same in every lane
     const int bh = BH - 1 - j / nsa, seg = j % nsa;
-    const int part = nparts - (pre[j + 1] - pre[j]) + (item - pre[j]);
+    const int part = __builtin_amdgcn_readfirstlane(nparts - (pre[j + 1] - pre[j]) + (item - pre[j]));
     const int h = bh % H;
     const float lam = decay ? decay[h] : 1.f;
     const int seg_end = (seg + 1) * seg_len;
