@@ -31,7 +31,7 @@ def dev(x):
 
 LIN_BWD_CASES = [
     # B, H, N, d, chunk, dtype, with_state, with_dstate
-    (2, 3, 1000, 128, 128, I.BF16, True, True),     # 8 segments, ragged tail
+    (2, 3, 1000, 128, 128, I.BF16, True, True),     # ragged tail (one segment: see test_linear_backward_segments)
     (1, 2, 777, 128, 64, I.BF16, True, False),      # chunk 64
     (1, 2, 600, 64, 128, I.BF16, False, True),      # d 64
     (1, 3, 333, 64, 64, I.BF16, False, False),
@@ -65,6 +65,30 @@ def test_linear_prefill_backward(case):
     assert_close(dsi, r[3], torch.float32 if dt == I.F32 else I.BF16, "dstate_in")
 
 
+def test_linear_backward_segments():
+    """Gradients over 8525 tokens (two segments of 34 chunks, each aggregated in
+    parts of 32 + 2 chunks) with lam 0.99 (part 0 weighted 0.99^256 in the scan)
+    and 0.9 (part 0 left out), an initial state and a state gradient: every
+    element against the oracle's chunked backward."""
+    B, H, N, d, C = 1, 2, 8525, 128, 128
+    say("linear_prefill_backward segments", B, H, N, d, C)
+    std = 1.0 / math.sqrt(d)
+    x = I.linear_inputs(B, H, N, d, I.BF16, 116, 5, std)
+    do = I.normal((B, H, N, d), 117, std, I.BF16)
+    decay = torch.tensor([0.99, 0.9], dtype=torch.float32)
+    s0 = I.normal((B, H, d, d), 118, 1.0 / d)
+    ds = I.normal((B, H, d, d), 119, 1.0 / d)
+    dq, dk, dv, dsi = sala.linear_prefill_backward(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(do), dev(decay),
+                                                   dev(s0), dev(ds), chunk=C)
+    torch.cuda.synchronize()
+    r = BW.linear_prefill_backward(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(do),
+                                   decay.double().numpy(), host64(s0), host64(ds), form="chunked", chunk=C)
+    assert_close(dq, r[0], I.BF16, "dq")
+    assert_close(dk, r[1], I.BF16, "dk")
+    assert_close(dv, r[2], I.BF16, "dv")
+    assert_close(dsi, r[3], I.BF16, "dstate_in")
+
+
 def test_linear_backward_full_size_heads():
     """The 32-head 32K linear workload (slope decays 0.43 .. 0.996): every row of
     three heads against the oracle's chunked backward (pinned equal to the
@@ -86,8 +110,9 @@ def test_linear_backward_full_size_heads():
 
 
 def test_linear_backward_256K_heads():
-    """The linear layer at the group's 262144 tokens (32 heads, 32 segments of
-    8192 tokens per head, the aggregate passes leaving out keys below 2^-126):
+    """The linear layer at the group's 262144 tokens (32 heads, 8 segments of
+    32768 tokens per head aggregated in parts of 4096, the aggregate passes
+    leaving out keys below 2^-126 and whole parts before them):
     every row of the fastest- and the slowest-decaying head against the
     oracle's chunked backward."""
     N = 262144

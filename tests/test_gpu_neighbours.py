@@ -33,7 +33,8 @@ DECAYS = [1.0, 0.9, 0.43, 0.99, 0.0, 0.97]
 
 NB_CASES = [
     # B, H, N, d, chunk, pos0, norm_q, norm_k, rope, gate, with_state
-    (1, 4, 293, 128, 128, 0, True, True, True, True, True),          # 3 segments, ragged tail
+    (1, 4, 293, 128, 128, 0, True, True, True, True, True),          # ragged tail
+    (1, 2, 4500, 128, 64, 4096, True, True, True, True, True),       # 2 segments of 36 chunks, aggregate parts of 32 + 4
     (2, 2, 1000, 128, 128, 123456789, True, True, True, True, False),  # large positions
     (1, 3, 517, 128, 64, 77, True, False, True, False, True),         # chunk 64, k not normalised
     (1, 2, 600, 64, 128, 0, False, True, False, True, False),         # d 64, no RoPE

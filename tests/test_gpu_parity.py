@@ -31,7 +31,7 @@ LIN_CASES = [
     # B, H, N, d, chunk, dtype, std, with_state.  bf16 cases use the workloads' input scale
     # (std 1/sqrt(d)): bf16 operand rounding errors scale with the summed terms, which at this
     # scale keeps the elementwise rule meaningful; the relative-norm check catches structure.
-    (2, 3, 1000, 128, 128, I.BF16, 1.0 / math.sqrt(128), True),   # 8 segments, ragged tail
+    (2, 3, 1000, 128, 128, I.BF16, 1.0 / math.sqrt(128), True),   # ragged tail (one segment: see LIN_SEG_CASES)
     (1, 2, 777, 128, 64, I.BF16, 1.0 / math.sqrt(128), True),     # chunk 64
     (1, 2, 600, 64, 128, I.BF16, 1.0 / 8.0, False),               # d 64
     (1, 3, 333, 64, 64, I.BF16, 1.0 / 8.0, True),
@@ -56,11 +56,41 @@ def test_linear_prefill(case):
     assert_close(st, rs, torch.float32 if dt == I.F32 else I.BF16, "state")
 
 
+# Sequences long enough for several segments (the bf16 plan keeps segments at
+# least 32 chunks long) and for more than one aggregate part per segment (parts
+# of at most 32 chunks, summed by the scan with weights lam^(segment end - part
+# end)); the plans noted are the library's for these shapes.
+LIN_SEG_CASES = [
+    # B, H, N, d, chunk, decays
+    # part 0's weight lam^(segment end - part end): 0.995^256 = 0.28 below; 0.95^64 = 0.04 and lam 1 next;
+    # 0.999^256 = 0.77 last.  lam 0.9 and 0.3 leave part 0 out.
+    (1, 2, 8525, 128, 128, (0.995, 0.9)),        # 2 segments of 34 chunks, parts of 32 + 2
+    (1, 3, 10340, 128, 64, (1.0, 0.95, 0.3)),    # 5 segments of 33 chunks, parts of 32 + 1
+    (2, 1, 4500, 64, 64, (0.999,)),              # d 64: 2 segments of 36 chunks, parts of 32 + 4
+]
+
+
+@pytest.mark.parametrize("case", LIN_SEG_CASES, ids=lambda c: f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}C{c[4]}")
+def test_linear_prefill_segments_and_parts(case):
+    B, H, N, d, C, decays = case
+    say("linear_prefill segments and parts", case)
+    x = I.linear_inputs(B, H, N, d, I.BF16, 96, N % 89, 1.0 / math.sqrt(d))
+    decay = torch.tensor(decays, dtype=torch.float32)
+    s0 = I.normal((B, H, d, d), 79, 1.0 / d)
+    o, st = sala.linear_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(decay), dev(s0), chunk=C)
+    torch.cuda.synchronize()
+    ro, rs = OL.linear_prefill(host64(x["q"]), host64(x["k"]), host64(x["v"]), decay.double().numpy(), host64(s0),
+                               form="chunked", chunk=C)
+    assert_close(o, ro, I.BF16, "o")
+    assert_close(st, rs, I.BF16, "state")
+
+
 def test_linear_prefill_fast_decay_segments():
-    """128 heads of 4133 tokens (chunk 64, 8 segments of 9 chunks) with decays from
-    0 to 1: the aggregate pass leaves out keys whose weight lam^n is below 2^-126
-    (all but the last chunk or so of each segment for lam <= 0.43, none for
-    lam >= 0.9), and every output row, head and final state must still match."""
+    """128 heads of 4133 tokens (chunk 64: two segments, the first in two
+    aggregate parts) with decays from 0 to 1: the aggregate pass leaves out keys
+    whose weight lam^n is below 2^-126 (and whole parts before them for lam <=
+    0.43, none for lam >= 0.9), and every output row, head and final state must
+    still match."""
     B, H, N, d, C = 4, 32, 4133, 128, 64
     say("linear_prefill fast decays", B, H, N, d, C)
     x = I.linear_inputs(B, H, N, d, I.BF16, 95, 3, 1.0 / math.sqrt(d))
