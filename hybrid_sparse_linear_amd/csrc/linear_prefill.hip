@@ -39,6 +39,9 @@
 // initial state dS^T / dS enters one decay step later (weight lam^r on
 // reversed row r instead of lam^(r+1)); dS_in is lam times the final state of
 // the (K, Q, dO) pass.  So every kernel below takes the switches of LinDir.
+// The (K, Q, dO) pass's segment states, sums of Q dO^T, are the transposes of
+// the (V, dO, Q) pass's sums of dO Q^T, so it reads those instead of running
+// its own aggregate and scan.
 
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
@@ -1004,7 +1007,11 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   const float *seg_state = a.state_in;  // nseg == 1: segment 0 starts from state_in
   size_t seg_stride = DD;
   int sin_T = a.state_T;
-  if (nseg > 1) {
+  if (nseg > 1 && a.reuse_states_T) {
+    seg_state = ws;
+    seg_stride = DD * pl.nparts;
+    sin_T = 1;
+  } else if (nseg > 1) {
     const dim3 agrid(min(BH * (nseg - 1) * pl.nparts, NCU));
     if (k_transformed)
       hipLaunchKernelGGL((lin_seg_aggregate<C, D, true, REV>), agrid, dim3(512), 0, st, (const uint16_t *)a.k,
@@ -1041,7 +1048,7 @@ hipError_t run_f32(const LinearPrefillArgs &a, hipStream_t st) {
   const size_t DD = (size_t)D * D;
   const float *q = static_cast<const float *>(a.q), *k = static_cast<const float *>(a.k),
               *v = static_cast<const float *>(a.v);
-  if (nseg > 1) {
+  if (nseg > 1 && !a.reuse_states_T) {
     hipLaunchKernelGGL((lin_f32_pass<D, false>), dim3(BH * (nseg - 1)), dim3(256), 0, st, q, k, v, nullptr, a.decay,
                        ws, nullptr, nullptr, a.H, a.N, seg_len, nseg, dir, 0);
     hipLaunchKernelGGL(lin_seg_scan, dim3((unsigned)((DD + 255) / 256), BH), dim3(256), 0, st, ws, a.state_in,
@@ -1049,7 +1056,8 @@ hipError_t run_f32(const LinearPrefillArgs &a, hipStream_t st) {
   }
   // one segment: the pass reads the caller's initial state itself (transposed if asked)
   hipLaunchKernelGGL((lin_f32_pass<D, true>), dim3(BH * nseg), dim3(256), 0, st, q, k, v, static_cast<float *>(a.o),
-                     a.decay, ws, a.state_in, a.state_out, a.H, a.N, seg_len, nseg, dir, nseg > 1 ? 0 : a.state_T);
+                     a.decay, ws, a.state_in, a.state_out, a.H, a.N, seg_len, nseg, dir,
+                     nseg > 1 ? a.reuse_states_T : a.state_T);
   return hipGetLastError();
 }
 
@@ -1092,6 +1100,9 @@ hipError_t launch_linear_prefill_backward(const LinearBackwardArgs &a, hipStream
   pv.rev = 1;
   pv.lag = 1;
   pv.scale_final = 1;
+  // its states are sum Q dO^T, the transposes of the dK pass's sum dO Q^T (same
+  // decays, same late start, initial dS against dS^T): read them transposed
+  pv.reuse_states_T = 1;
   return launch_linear_prefill(pv, st);
 }
 

@@ -33,6 +33,9 @@ struct LinearPrefillArgs {
   // reverse order; initial state entering one decay step late; initial state
   // read transposed; final state written times lam
   int rev = 0, lag = 0, state_T = 0, scale_final = 0;
+  // 1: the segment states a previous pass of the same plan left in ws are this
+  // pass's states transposed (the dV pass after the dK pass); no aggregate or scan
+  int reuse_states_T = 0;
 };
 size_t linear_prefill_workspace(int dtype, int B, int H, int N, int d, int chunk);
 hipError_t launch_linear_prefill(const LinearPrefillArgs &a, hipStream_t st);
