@@ -151,24 +151,64 @@ __device__ __forceinline__ void store_kv(char *lds, int tid, int m, const u32x4 
 //   S = lam^m S + (diag(lam^(m-1-j)) K)^T V
 // A = K^T fragments by transposed reads, scaled per token in fp32 and rounded
 // once to bf16; B = V fragments by transposed reads.
+// kn, vn: the K and V tiles; rw: lam^(m-1-j) for the chunk's rows.
 template <int C, int D>
-__device__ __forceinline__ void state_update(const char *lds, int sdk, int sdv0, int g, uint32_t lane_tr,
-                                             uint32_t xtr, float lam_m, f32x4 (&Sacc)[LinCfg<C, D>::SDV]) {
+__device__ __forceinline__ void state_update(const char *kn, const char *vn, const char *rw, int sdk, int sdv0,
+                                             int g, uint32_t lane_tr, uint32_t xtr, float lam_m,
+                                             f32x4 (&Sacc)[LinCfg<C, D>::SDV]) {
   using Cf = LinCfg<C, D>;
 #pragma unroll
   for (int a = 0; a < Cf::SDV; ++a) Sacc[a] *= lam_m;
 #pragma unroll
   for (int ks = 0; ks < Cf::NKS; ++ks) {
-    u32x4 A = tr_frag<C, D>(lds, Cf::KN + 32 * ks * Cf::ROWB, lane_tr, xtr, sdk);
-    const f32x4 w0 = lds_load<f32x4>(lds + Cf::RW, (32 * ks + 8 * g) * 4);
-    const f32x4 w1 = lds_load<f32x4>(lds + Cf::RW, (32 * ks + 8 * g + 4) * 4);
+    u32x4 A = tr_frag<C, D>(kn, 32 * ks * Cf::ROWB, lane_tr, xtr, sdk);
+    const f32x4 w0 = lds_load<f32x4>(rw, (32 * ks + 8 * g) * 4);
+    const f32x4 w1 = lds_load<f32x4>(rw, (32 * ks + 8 * g + 4) * 4);
     A[0] = pack_bf16x2(bf16lo(A[0]) * w0[0], bf16hi(A[0]) * w0[1]);
     A[1] = pack_bf16x2(bf16lo(A[1]) * w0[2], bf16hi(A[1]) * w0[3]);
     A[2] = pack_bf16x2(bf16lo(A[2]) * w1[0], bf16hi(A[2]) * w1[1]);
     A[3] = pack_bf16x2(bf16lo(A[3]) * w1[2], bf16hi(A[3]) * w1[3]);
 #pragma unroll
     for (int a = 0; a < Cf::SDV; ++a)
-      Sacc[a] = mfma16x16x32(A, tr_frag<C, D>(lds, Cf::VN + 32 * ks * Cf::ROWB, lane_tr, xtr, sdv0 + a), Sacc[a]);
+      Sacc[a] = mfma16x16x32(A, tr_frag<C, D>(vn, 32 * ks * Cf::ROWB, lane_tr, xtr, sdv0 + a), Sacc[a]);
+  }
+}
+template <int C, int D>
+__device__ __forceinline__ void state_update(const char *lds, int sdk, int sdv0, int g, uint32_t lane_tr,
+                                             uint32_t xtr, float lam_m, f32x4 (&Sacc)[LinCfg<C, D>::SDV]) {
+  using Cf = LinCfg<C, D>;
+  state_update<C, D>(lds + Cf::KN, lds + Cf::VN, lds + Cf::RW, sdk, sdv0, g, lane_tr, xtr, lam_m, Sacc);
+}
+// The same update on an NI x NJ block of tiles, d_k tiles sdk .. sdk+NI-1 and
+// d_v tiles sdv .. sdv+NJ-1 (Sacc[NJ * i + j]): per 32 tokens a wave reads
+// NI K^T and NJ V fragments, so a 2 x 4 block reads 6 where a 1 x 8 row of
+// tiles reads 9.
+template <int C, int D, int NI, int NJ>
+__device__ __forceinline__ void state_update_blk(const char *kn, const char *vn, const char *rw, int sdk, int sdv,
+                                                 int g, uint32_t lane_tr, uint32_t xtr, float lam_m,
+                                                 f32x4 (&Sacc)[NI * NJ]) {
+  using Cf = LinCfg<C, D>;
+#pragma unroll
+  for (int a = 0; a < NI * NJ; ++a) Sacc[a] *= lam_m;
+#pragma unroll
+  for (int ks = 0; ks < Cf::NKS; ++ks) {
+    const f32x4 w0 = lds_load<f32x4>(rw, (32 * ks + 8 * g) * 4);
+    const f32x4 w1 = lds_load<f32x4>(rw, (32 * ks + 8 * g + 4) * 4);
+    u32x4 A[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      A[i] = tr_frag<C, D>(kn, 32 * ks * Cf::ROWB, lane_tr, xtr, sdk + i);
+      A[i][0] = pack_bf16x2(bf16lo(A[i][0]) * w0[0], bf16hi(A[i][0]) * w0[1]);
+      A[i][1] = pack_bf16x2(bf16lo(A[i][1]) * w0[2], bf16hi(A[i][1]) * w0[3]);
+      A[i][2] = pack_bf16x2(bf16lo(A[i][2]) * w1[0], bf16hi(A[i][2]) * w1[1]);
+      A[i][3] = pack_bf16x2(bf16lo(A[i][3]) * w1[2], bf16hi(A[i][3]) * w1[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const u32x4 B = tr_frag<C, D>(vn, 32 * ks * Cf::ROWB, lane_tr, xtr, sdv + j);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) Sacc[NJ * i + j] = mfma16x16x32(A[i], B, Sacc[NJ * i + j]);
+    }
   }
 }
 
@@ -746,6 +786,295 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   }
 }
 
+// Pass 3 with direct loads (no q / k transform to apply): each chunk's k, v
+// and q rows go from HBM straight into LDS (buffer loads with an LDS
+// destination, 16 bytes per lane), into one of two buffers, so the next
+// chunk's rows are in flight while this one is computed and no registers or
+// LDS stores stage them.  The two buffers hold 3 C rows each (k | v | q), so
+// this form runs with C = 64 at d = 128 (128 KB of LDS with the bf16 S^T).
+// The arithmetic per chunk is that of lin_seg_output, except that each wave
+// updates a 2 x 4 block of state tiles (d = 128).  Rows past a chunk's valid
+// rows read as zero (the buffer resources cover the valid rows only).
+template <int C, int D>
+struct LinDma {
+  using Cf = LinCfg<C, D>;
+  static constexpr uint32_t TILE = C * Cf::ROWB;      // one [C][D] bf16 tile
+  static constexpr int SLOTS = C * Cf::NCH / Cf::NT;  // 16-byte slots per thread and tile
+  static constexpr int NST = Cf::DVW / 2;             // 16-byte output stores per thread and chunk
+  static_assert(SLOTS >= 1 && C * Cf::NCH % Cf::NT == 0, "unsupported chunk / head size");
+};
+// the two chunk buffers, S^T and the decay tables fit the 160 KB of LDS
+template <int C, int D>
+constexpr bool dma_fits() {
+  return 2 * 3 * C * D * 2 + D * D * 2 <= 156 * 1024;
+}
+
+// Workgroup barrier after this wave's LDS operations and all but its last VM
+// vector memory operations are done.  __syncthreads would also wait for every
+// direct load still in flight (its fence counts them as LDS writes); here the
+// caller names what must have landed.  The signal fences keep the compiler
+// from moving LDS accesses across.
+template <int VM>
+__device__ __forceinline__ void lds_barrier() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0070);  // vmcnt(VM) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// GATE: the output is gated (a compile-time switch: the gate loads' registers
+// would otherwise be waited on before every reuse in the ungated form).
+template <int C, int D, bool REV, bool GATE>
+__global__ __launch_bounds__(512) void lin_seg_output_dma(const uint16_t *__restrict__ q,
+                                                          const uint16_t *__restrict__ k,
+                                                          const uint16_t *__restrict__ v,
+                                                          uint16_t *__restrict__ o,
+                                                          const float *__restrict__ decay,
+                                                          const float *__restrict__ seg_state, size_t seg_stride,
+                                                          float *__restrict__ state_out, int H, int N, int seg_len,
+                                                          int nseg, const uint16_t *__restrict__ gate, LinDir dir,
+                                                          int sin_T) {
+  using Cf = LinCfg<C, D>;
+  using Dm = LinDma<C, D>;
+  // two chunk buffers (k | v | q) and the S^T copy: separate arrays, so the
+  // compiler sees that direct loads into one buffer do not touch the others
+  __shared__ __attribute__((aligned(16))) char buf0[3 * Dm::TILE], buf1[3 * Dm::TILE];
+  __shared__ __attribute__((aligned(16))) char stl[D * Cf::ROWB];
+  __shared__ __attribute__((aligned(16))) float tab[Cf::PWZ + C + 4 + C];
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const int h = bh % H;
+  const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
+  const float lam = decay ? decay[h] : 1.f;
+  float *pw = tab + Cf::PWZ;          // pw[n] = lam^n, 0 for n < 0
+  float *rw = tab + Cf::PWZ + C + 4;  // lam^(m-1-j) for the chunk's rows, 0 past m
+  for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);
+  const size_t head_off = (size_t)bh * N * D;
+  const uint16_t *qb = q + head_off, *kb = k + head_off, *vb = v + head_off;
+  uint16_t *ob = o + head_off;
+  int qt, part;
+  Cf::qrole(w, qt, part);
+  const int dvb = part * Cf::DVW;
+  const int qq = 16 * qt + lr;  // this lane's query row in the chunk
+  // state tiles: an NI x NJ block, d_k tiles sdk .. and d_v tiles sdv ..
+  constexpr int NI = Cf::ND == 8 ? 2 : 1, NJ = Cf::SDV / NI, BI = Cf::ND / NI;
+  const int sdk = NI * (w % BI), sdv = NJ * (w / BI);
+  const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
+
+  f32x4 Sacc[Cf::SDV];
+  const float *sin = seg_state ? seg_state + (size_t)bh * seg_stride * nseg + (size_t)seg * seg_stride : nullptr;
+#pragma unroll
+  for (int a = 0; a < Cf::SDV; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t r = 16 * (sdk + a / NJ) + 4 * g + i, c = 16 * (sdv + a % NJ) + lr;
+      Sacc[a][i] = sin ? sin[sin_T ? c * D + r : r * D + c] : 0.f;
+    }
+  bool lag_chunk = dir.lag && seg == 0;
+
+  // Direct loads: the LDS slot of lane l in wave w for slot step u is
+  // p = 512u + 64w + l of a tile (16 bytes each); it holds chunk row p / NCH at
+  // swizzled position p % NCH, i.e. the logical 16-byte piece
+  // (p % NCH) ^ f(row) of that row (the swizzles are involutions): f = fkv for
+  // k and v, fst for q, whose fragments are 16 consecutive rows at one piece.
+  uint32_t srow[Dm::SLOTS], spiece[Dm::SLOTS], spq[Dm::SLOTS];
+#pragma unroll
+  for (int u = 0; u < Dm::SLOTS; ++u) {
+    const uint32_t p = Cf::NT * u + tid, row = p / Cf::NCH;
+    srow[u] = row;
+    spiece[u] = (((p % Cf::NCH) ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
+    spq[u] = (((p % Cf::NCH) ^ fst(row)) & (Cf::NCH - 1)) * 16u;
+  }
+  // Chunk rows c0 .. c0 + m - 1 (m = 0 past the segment: every load reads
+  // zero).  REV: chunk row r is memory row N - 1 - (c0 + r); the resource
+  // starts at memory row N - c0 - m, so rows r >= m fall past its end.
+  auto chunk_rows = [&](int c0) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(max(0, min(C, t_end - c0)));  // uniform: the resources stay scalar
+  };
+  auto rows_rsrc = [&](const uint16_t *base, int c0, int m) __attribute__((always_inline)) {
+    return buf_rsrc(base + (REV ? (size_t)(N - c0 - m) : (size_t)c0) * D, (uint32_t)m * Cf::ROWB);
+  };
+  // k, v and q rows of chunk c0 into buffer dst (k | v | q)
+  auto load_chunk = [&](char *dst, int c0) __attribute__((always_inline)) {
+    const int m = chunk_rows(c0);
+    const auto kr = rows_rsrc(kb, c0, m), vr = rows_rsrc(vb, c0, m), qr = rows_rsrc(qb, c0, m);
+#pragma unroll
+    for (int u = 0; u < Dm::SLOTS; ++u) {
+      const uint32_t r = REV ? (uint32_t)(m - 1) - srow[u] : srow[u];
+      const uint32_t slot = (Cf::NT * u + 64 * w) * 16;
+      bload16_lds(kr, dst + slot, r * Cf::ROWB + spiece[u]);
+      bload16_lds(vr, dst + Dm::TILE + slot, r * Cf::ROWB + spiece[u]);
+      bload16_lds(qr, dst + 2 * Dm::TILE + slot, r * Cf::ROWB + spq[u]);
+    }
+  };
+  const auto gr = buf_rsrc(GATE ? gate + head_off : qb, (uint32_t)N * D * 2u);
+
+  // One chunk: cur holds its rows (landed by the barrier below); the rows of
+  // chunk c0 + C go to nxt.
+  auto step = [&](const char *cur, char *nxt, int c0) __attribute__((always_inline)) {
+    const int m = min(C, t_end - c0);
+    // this wave's direct loads of the chunk have landed (only the previous
+    // chunk's output stores, issued after them, may be outstanding); after
+    // the barrier every wave's rows are in and the previous chunk is done
+    // with nxt, S^T and rw
+    lds_barrier<Dm::NST>();
+    // gate values of this lane's outputs (a clamped row is never stored),
+    // loaded before the next chunk's rows so that waiting for them waits for
+    // nothing issued later
+    u32x2 gv[Cf::DVW] = {};
+    if constexpr (GATE) {
+      uint32_t t = min(c0 + qq, t_end - 1);
+      if constexpr (REV) t = (uint32_t)(N - 1) - t;
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) gv[dvi] = bload8(gr, (t * D + 16 * (dvb + dvi) + 4 * g) * 2u);
+    }
+    // bf16 S^T in 16-byte stores: of the tiles (sdk, j) and (sdk + 1, j), a
+    // lane holds four d_k values of one d_v column in each; lanes 16 apart
+    // swap halves so that each holds eight consecutive d_k values of one of
+    // them (g even: tile sdk, g odd: tile sdk + 1).  S^T and rw are written
+    // before the next chunk's loads are issued: a store that the compiler
+    // cannot tell apart from a direct load in flight waits for that load, and
+    // it loses that information when it pairs 8-byte stores.
+    if constexpr (NI == 2) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const f32x4 &sa = Sacc[j], &sb = Sacc[NJ + j];
+        uint32_t x[2] = {pack_bf16x2(sa[0], sa[1]), pack_bf16x2(sa[2], sa[3])};
+        uint32_t y[2] = {pack_bf16x2(sb[0], sb[1]), pack_bf16x2(sb[2], sb[3])};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(x[e], y[e], false, false);
+          x[e] = sw[0];
+          y[e] = sw[1];
+        }
+        const uint32_t row = 16 * (sdv + j) + lr;
+        const uint32_t ch = 2 * (sdk + (g & 1)) + (g >> 1);
+        lds_store(stl, row * Cf::ROWB + ((ch ^ fst(row)) & (Cf::NCH - 1)) * 16u, u32x4{x[0], x[1], y[0], y[1]});
+      }
+    } else {  // one d_k tile per wave: 8-byte stores
+#pragma unroll
+      for (int a = 0; a < Cf::SDV; ++a) {
+        const uint32_t row = 16 * (sdv + a % NJ) + lr;
+        const uint32_t off =
+            row * Cf::ROWB + (((2 * (sdk + a / NJ) + (g >> 1)) ^ fst(row)) & (Cf::NCH - 1)) * 16u + (g & 1) * 8;
+        lds_store(stl, off, u32x2{pack_bf16x2(Sacc[a][0], Sacc[a][1]), pack_bf16x2(Sacc[a][2], Sacc[a][3])});
+      }
+    }
+    if (tid < C) rw[tid] = (tid < m) ? pw[m - 1 - tid] : 0.f;
+    load_chunk(nxt, c0 + C);  // past the segment: zeros
+    lds_barrier<63>();  // S^T and rw written; the next chunk's loads stay in flight
+    const char *kc = cur, *vc = cur + Dm::TILE, *qn = cur + 2 * Dm::TILE;
+    u32x4 qf[Cf::NDS];
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s)
+      qf[s] = lds_load<u32x4>(qn, qq * Cf::ROWB + (((4 * s + g) ^ fst(qq)) & (Cf::NCH - 1)) * 16u);
+    // O^T = lam^(qq+1) S^T Q^T
+    f32x4 Oacc[Cf::DVW];
+#pragma unroll
+    for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s) {
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        const uint32_t row = 16 * (dvb + dvi) + lr;
+        const u32x4 A = lds_load<u32x4>(stl, row * Cf::ROWB + (((4 * s + g) ^ fst(row)) & (Cf::NCH - 1)) * 16u);
+        Oacc[dvi] = mfma16x16x32(A, qf[s], Oacc[dvi]);
+      }
+    }
+    {
+      const float f = pw[lag_chunk ? qq : qq + 1];
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) Oacc[dvi] *= f;
+    }
+    // P^T = decay-masked K Q^T over the causal key pairs; O^T += V^T P^T
+#pragma unroll
+    for (int p = 0; p < (Cf::NQT + 1) / 2; ++p) {
+      if (p > qt / 2) break;
+      f32x4 P[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < Cf::NDS; ++s) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t row = 32 * p + pair_key(t, lr);
+          const u32x4 A = lds_load<u32x4>(kc, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
+          P[t] = mfma16x16x32(A, qf[s], P[t]);
+        }
+      }
+      const int nb0 = qq - 32 * p - 8 * g;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P[t][i] *= pw[nb0 - 4 * t - i];
+      const u32x4 Bp = u32x4{pack_bf16x2(P[0][0], P[0][1]), pack_bf16x2(P[0][2], P[0][3]),
+                             pack_bf16x2(P[1][0], P[1][1]), pack_bf16x2(P[1][2], P[1][3])};
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        const u32x4 A = tr_frag<C, D>(vc, 32 * p * Cf::ROWB, lane_tr, xtr, dvb + dvi);
+        Oacc[dvi] = mfma16x16x32(A, Bp, Oacc[dvi]);
+      }
+    }
+    state_update_blk<C, D, NI, NJ>(kc, vc, reinterpret_cast<const char *>(rw), sdk, sdv, g, lane_tr, xtr,
+                                   pw[lag_chunk ? m - 1 : m], Sacc);
+    // output row qq: 16-byte stores of eight consecutive d_v values (lanes 16
+    // apart swap halves), as in lin_seg_output.  Buffer stores over the
+    // chunk's valid rows: rows past m are dropped by the range check, so
+    // every wave issues the same NST stores in every chunk, which the vmcnt
+    // of the barriers counts on.
+    {
+      const auto orr = rows_rsrc(ob, c0, chunk_rows(c0));
+      const uint32_t orow = (REV ? (uint32_t)(m - 1 - qq) : (uint32_t)qq) * Cf::ROWB;
+      u32x2 ov[Cf::DVW];
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        f32x4 x = Oacc[dvi];
+        if constexpr (GATE) {
+          x[0] *= sigmoid_fast(bf16lo(gv[dvi][0]));
+          x[1] *= sigmoid_fast(bf16hi(gv[dvi][0]));
+          x[2] *= sigmoid_fast(bf16lo(gv[dvi][1]));
+          x[3] *= sigmoid_fast(bf16hi(gv[dvi][1]));
+        }
+        ov[dvi] = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      }
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; dvi += 2) {
+        u32x2 a = ov[dvi], b = ov[dvi + 1];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(a[e], b[e], false, false);
+          a[e] = sw[0];
+          b[e] = sw[1];
+        }
+        const int tile = dvb + dvi + (g & 1);
+        bstore16(orr, orow + (16 * tile + 8 * (g >> 1)) * 2u, u32x4{a[0], a[1], b[0], b[1]});
+      }
+    }
+    lag_chunk = false;
+  };
+
+  load_chunk(buf0, t_begin);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the entry state and the first chunk are in
+  for (int c0 = t_begin; c0 < t_end; c0 += 2 * C) {
+    step(buf0, buf1, c0);
+    if (c0 + C >= t_end) break;
+    step(buf1, buf0, c0 + C);
+  }
+  // the last step's loads of an empty successor write zeros into LDS: let
+  // them land before the workgroup's LDS can be handed on
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  if (state_out && seg == nseg - 1) {
+    float *so = state_out + (size_t)bh * D * D;
+    const float f = dir.scale ? lam : 1.f;
+#pragma unroll
+    for (int a = 0; a < Cf::SDV; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        so[(size_t)(16 * (sdk + a / NJ) + 4 * g + i) * D + 16 * (sdv + a % NJ) + lr] = Sacc[a][i] * f;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 // The bf16 path's segment plan in fp32 on the VALU, with tiles of FT tokens:
 // lin_f32_pass<D, false> forms the aggregate of every segment but the last,
@@ -1026,6 +1355,15 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
     seg_state = ws;
     seg_stride = DD * pl.nparts;  // S_in(m) sits in part slot 0 of segment m
     sin_T = 0;  // the scan wrote the segment states in the plain layout
+  }
+  if constexpr (dma_fits<C, D>()) {
+    if (!k_transformed && nb.gq == nullptr) {  // nothing to apply to q or k as they are staged
+      auto kern = nb.gate ? lin_seg_output_dma<C, D, REV, true> : lin_seg_output_dma<C, D, REV, false>;
+      hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                         (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, seg_stride, a.state_out, a.H,
+                         a.N, seg_len, nseg, nb.gate, dir, sin_T);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((lin_seg_output<C, D, REV>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, seg_stride,

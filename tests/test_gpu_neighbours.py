@@ -41,6 +41,8 @@ NB_CASES = [
     (1, 2, 333, 64, 64, 4096, True, True, True, True, True),
     (1, 2, 130, 128, 128, 0, False, False, True, False, False),       # RoPE only, one segment
     (1, 2, 700, 128, 128, 0, False, False, False, True, True),        # gate only
+    (1, 3, 1500, 128, 64, 0, False, False, False, True, True),        # gate only, chunk 64 (direct-load output pass)
+    (1, 2, 900, 64, 128, 0, False, False, False, True, False),        # gate only, d 64 (direct-load output pass)
 ]
 
 
