@@ -49,6 +49,12 @@
 namespace sala {
 namespace {
 
+// 16-byte store at buffer offset off (dropped past the resource's end).
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4 &v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                         off, 0, 0);
+}
+
 template <int C, int D>
 struct LinCfg {
   static constexpr int NT = 512;               // 8 waves, two per SIMD

@@ -120,11 +120,6 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
-// 16-byte store at buffer offset off (dropped past the resource's end).
-__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4 &v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
-                                         off, 0, 0);
-}
 // 16 bytes per lane from buffer offset off straight into LDS: lane l's bytes
 // land at lds + 16 l (lds wave-uniform).
 __device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
