@@ -47,8 +47,10 @@ struct Elem<float> {
 };
 
 // Mean of `nrows` rows of length d; row r lives at src(r).  256 threads.
-// Writes the fp32 mean to dst[0..d).
-template <typename T, typename RowPtr>
+// Writes the fp32 mean to dst[0..d).  NT: the rows are read with the
+// non-temporal hint (query rows, read once here; key rows are left in the
+// caches for the attention kernel's gathers).
+template <typename T, bool NT, typename RowPtr>
 __device__ void mean_rows(RowPtr src, int nrows, int d, float *dst, float *red /* 256*8 floats */) {
   constexpr int E = Elem<T>::PER16;
   const int cpr = d / E;  // 16-byte chunks per row
@@ -59,7 +61,8 @@ __device__ void mean_rows(RowPtr src, int nrows, int d, float *dst, float *red /
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int r = r0; r < nrows; r += slots) {
     float f[E];
-    Elem<T>::unpack(gload16(src(r) + c * E), f);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(src(r) + c * E);
+    Elem<T>::unpack(NT ? __builtin_nontemporal_load(p) : *p, f);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += f[e];
   }
@@ -87,15 +90,16 @@ __global__ __launch_bounds__(256) void pool_rows(const T *__restrict__ q, const 
     const int bh = bid / NBp, j = kb0 + bid % NBp;
     const int cnt = min(block, L - j * block);
     const T *base = k + ((size_t)bh * Lc + (size_t)j * block) * d;
-    mean_rows<T>([&](int r) { return base + (size_t)r * d; }, cnt, d, kbar + ((size_t)bh * NBs + j) * d, red);
+    mean_rows<T, false>([&](int r) { return base + (size_t)r * d; }, cnt, d, kbar + ((size_t)bh * NBs + j) * d,
+                        red);
   } else {
     const int id = bid - n_kblocks_total;
     const int bh = id / NQB, i = id % NQB;  // bh = b*Hkv + h
     const int b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv;
     const int cnt = min(block, Nq - i * block);
     const T *base = q + ((size_t)(b * Hq + h * G) * Nq + (size_t)i * block) * d;
-    mean_rows<T>([&](int r) { return base + ((size_t)(r / cnt) * Nq + (r % cnt)) * d; }, G * cnt, d,
-                 qbar + ((size_t)bh * NQB + i) * d, red);
+    mean_rows<T, true>([&](int r) { return base + ((size_t)(r / cnt) * Nq + (r % cnt)) * d; }, G * cnt, d,
+                       qbar + ((size_t)bh * NQB + i) * d, red);
   }
 }
 
@@ -118,8 +122,8 @@ __global__ __launch_bounds__(256) void kv_append(const T *__restrict__ k_new, co
   else if (tid < 2 * cpr) gstore16(vrow + (tid - cpr) * E, gload16(vn + (tid - cpr) * E));
   const int j = pos / block, first = j * block, cnt = pos - first + 1;
   const T *base = kc + ((size_t)bh * Lc + first) * d;
-  mean_rows<T>([&](int r) { return r == cnt - 1 ? kn : base + (size_t)r * d; }, cnt, d,
-               kbar + ((size_t)bh * NBs + j) * d, red);
+  mean_rows<T, false>([&](int r) { return r == cnt - 1 ? kn : base + (size_t)r * d; }, cnt, d,
+                      kbar + ((size_t)bh * NBs + j) * d, red);
 }
 
 // scores[bh][i][j] = (qbar_i . kbar_j) * inv_sqrt_d for the 64x64 tiles of
