@@ -1099,6 +1099,279 @@ __global__ __launch_bounds__(512) void lin_seg_output_dma(const uint16_t *__rest
   }
 }
 
+// The dK and dV passes of the gradients in one reversed pass (direct loads).
+// Both are decayed causal linear attention on the time-reversed sequence (see
+// the header): dK with query v, key dO and value q, dV with query k, key q
+// and value dO, and their states are transposes of each other,
+//   S = sum_t (decay) dO_t q_t^T  for dK,   S^T  for dV,
+// so one fp32 state S[d_v][d_k] serves both.  Per chunk of C reversed rows:
+//   dK^T += lam^(r+1) S^T V^T + Q^T (decay-masked dO V^T)
+//   dV^T += lam^(r+1) S   K^T + dO^T (decay-masked Q K^T)
+//   S     = lam^C S + (diag(lam^(C-1-j)) dO)^T Q
+// (r + 1 -> r and C -> C - 1 in the first chunk of the first segment: the
+// initial state enters one step late).  The bf16 copy of S^T in LDS is read
+// plainly for dK and transposed for dV.  k, v, q and dO rows go from HBM
+// straight into LDS by direct loads, double-buffered (2 x 64 KB at C = 64,
+// d = 128, with S^T the whole 160 KB), so the decay powers come from exp2 on
+// the VALU rather than LDS tables:
+//   lam^n = exp2(n * l2),  l2 = max(log2 lam, -16384)  (lam = 0: 0^0 = 1, 0^n = 0).
+// seg_state / sin_T: the segments' entry states of the dK pass (its
+// aggregate and scan); state_out receives dS_in = lam S_dV = lam S^T.
+template <int C, int D>
+constexpr bool gradkv_fits() {
+  return 2 * 4 * C * D * 2 + D * D * 2 <= 160 * 1024 && LinCfg<C, D>::ND == 8;
+}
+template <int C, int D>
+__global__ __launch_bounds__(512) void lin_seg_grad_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                       const uint16_t *__restrict__ v,
+                                                       const uint16_t *__restrict__ dout, uint16_t *__restrict__ dk,
+                                                       uint16_t *__restrict__ dv, const float *__restrict__ decay,
+                                                       const float *__restrict__ seg_state, size_t seg_stride,
+                                                       float *__restrict__ state_out, int H, int N, int seg_len,
+                                                       int nseg, int lag, int sin_T) {
+  using Cf = LinCfg<C, D>;
+  constexpr uint32_t TILE = C * Cf::ROWB;            // one [C][D] bf16 tile
+  constexpr int SLOTS = C * Cf::NCH / Cf::NT;        // 16-byte slots per thread and tile
+  constexpr int NST = Cf::DVW;                       // output stores per thread and chunk (dK and dV)
+  static_assert(SLOTS >= 1 && C * Cf::NCH % Cf::NT == 0 && gradkv_fits<C, D>(), "unsupported chunk / head size");
+  // tiles of a buffer: v (query of dK) | k (query of dV) | dO | q
+  constexpr uint32_t TV = 0, TK = TILE, TO = 2 * TILE, TQ = 3 * TILE;
+  __shared__ __attribute__((aligned(16))) char buf0[4 * TILE], buf1[4 * TILE];
+  __shared__ __attribute__((aligned(16))) char stl[D * Cf::ROWB];  // bf16 S^T, fkv-swizzled
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const int h = bh % H;
+  const int t_begin = seg * seg_len, t_end = min(N, t_begin + seg_len);
+  const float lam = decay ? decay[h] : 1.f;
+  const float l2 = fmaxf(log2f(lam), -16384.f);
+  auto lpow = [&](int n) __attribute__((always_inline)) { return __builtin_amdgcn_exp2f((float)n * l2); };
+  const size_t head_off = (size_t)bh * N * D;
+  int qt, part;
+  Cf::qrole(w, qt, part);
+  const int dvb = part * Cf::DVW;
+  const int qq = 16 * qt + lr;  // this lane's row in the chunk
+  constexpr int NI = 2, NJ = Cf::SDV / 2;
+  const int sdk = NI * (w % 4), sdv = NJ * (w / 4);  // state tiles: d_v (dO) tiles sdk.., d_k (q) tiles sdv..
+  const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
+
+  f32x4 Sacc[Cf::SDV];
+  const float *sin = seg_state ? seg_state + (size_t)bh * seg_stride * nseg + (size_t)seg * seg_stride : nullptr;
+#pragma unroll
+  for (int a = 0; a < Cf::SDV; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t r = 16 * (sdk + a / NJ) + 4 * g + i, c = 16 * (sdv + a % NJ) + lr;
+      Sacc[a][i] = sin ? sin[sin_T ? c * D + r : r * D + c] : 0.f;
+    }
+  bool lag_chunk = lag && seg == 0;
+
+  // direct-load slots (as in lin_seg_output_dma): fst for the query tiles (16
+  // consecutive rows at one piece), fkv for dO and q (read by key pairs and
+  // transposed)
+  uint32_t srow[SLOTS], spk[SLOTS], spq[SLOTS];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const uint32_t p = Cf::NT * u + tid, row = p / Cf::NCH;
+    srow[u] = row;
+    spk[u] = (((p % Cf::NCH) ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
+    spq[u] = (((p % Cf::NCH) ^ fst(row)) & (Cf::NCH - 1)) * 16u;
+  }
+  // reversed rows: chunk row r is memory row N - 1 - (c0 + r); the resources
+  // start at memory row N - c0 - m, so rows r >= m fall past their end
+  auto chunk_rows = [&](int c0) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(max(0, min(C, t_end - c0)));
+  };
+  auto rows_rsrc = [&](const uint16_t *base, int c0, int m) __attribute__((always_inline)) {
+    return buf_rsrc(base + head_off + (size_t)(N - c0 - m) * D, (uint32_t)m * Cf::ROWB);
+  };
+  auto load_chunk = [&](char *dst, int c0) __attribute__((always_inline)) {
+    const int m = chunk_rows(c0);
+    const auto vr = rows_rsrc(v, c0, m), kr = rows_rsrc(k, c0, m), orr = rows_rsrc(dout, c0, m),
+               qr = rows_rsrc(q, c0, m);
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      const uint32_t rb = ((uint32_t)(m - 1) - srow[u]) * Cf::ROWB;
+      const uint32_t slot = (Cf::NT * u + 64 * w) * 16;
+      bload16_lds_nt(vr, dst + TV + slot, rb + spq[u]);
+      bload16_lds_nt(kr, dst + TK + slot, rb + spq[u]);
+      bload16_lds_nt(orr, dst + TO + slot, rb + spk[u]);
+      bload16_lds_nt(qr, dst + TQ + slot, rb + spk[u]);
+    }
+  };
+  // 16-byte stores of eight consecutive values of output row qq (lanes 16
+  // apart swap halves); buffer stores over the chunk's valid rows, issued by
+  // every lane in every chunk
+  auto store_rows = [&](uint16_t *dst, int c0, int m, const f32x4 (&acc)[Cf::DVW]) __attribute__((always_inline)) {
+    const auto orr = rows_rsrc(dst, c0, chunk_rows(c0));
+    const uint32_t orow = (uint32_t)(m - 1 - qq) * Cf::ROWB;
+    u32x2 ov[Cf::DVW];
+#pragma unroll
+    for (int dvi = 0; dvi < Cf::DVW; ++dvi)
+      ov[dvi] = u32x2{pack_bf16x2(acc[dvi][0], acc[dvi][1]), pack_bf16x2(acc[dvi][2], acc[dvi][3])};
+#pragma unroll
+    for (int dvi = 0; dvi < Cf::DVW; dvi += 2) {
+      u32x2 a = ov[dvi], b = ov[dvi + 1];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(a[e], b[e], false, false);
+        a[e] = sw[0];
+        b[e] = sw[1];
+      }
+      const int tile = dvb + dvi + (g & 1);
+      bstore16_nt(orr, orow + (16 * tile + 8 * (g >> 1)) * 2u, u32x4{a[0], a[1], b[0], b[1]});
+    }
+  };
+
+  auto step = [&](const char *cur, char *nxt, int c0) __attribute__((always_inline)) {
+    const int m = min(C, t_end - c0);
+    // this wave's direct loads of the chunk have landed (only the previous
+    // chunk's output stores may be outstanding); the previous chunk is done
+    // with nxt and S^T
+    lds_barrier<NST>();
+    // bf16 S^T (rows d_k, fkv-swizzled) in 16-byte stores: lanes 16 apart swap
+    // halves of the tiles (sdk, j) and (sdk + 1, j), so each holds eight
+    // consecutive d_v values of one of them; written before the next chunk's
+    // loads are issued (see lin_seg_output_dma)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const f32x4 &sa = Sacc[j], &sb = Sacc[NJ + j];
+      uint32_t x[2] = {pack_bf16x2(sa[0], sa[1]), pack_bf16x2(sa[2], sa[3])};
+      uint32_t y[2] = {pack_bf16x2(sb[0], sb[1]), pack_bf16x2(sb[2], sb[3])};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(x[e], y[e], false, false);
+        x[e] = sw[0];
+        y[e] = sw[1];
+      }
+      const uint32_t row = 16 * (sdv + j) + lr;
+      const uint32_t ch = 2 * (sdk + (g & 1)) + (g >> 1);
+      lds_store(stl, row * Cf::ROWB + ((ch ^ fkv(row)) & (Cf::NCH - 1)) * 16u, u32x4{x[0], x[1], y[0], y[1]});
+    }
+    load_chunk(nxt, c0 + C);  // past the segment: zeros
+    lds_barrier<63>();  // S^T written; the next chunk's loads stay in flight
+    const char *tv = cur + TV, *tk = cur + TK, *to = cur + TO, *tq = cur + TQ;
+    u32x4 fv[Cf::NDS], fk[Cf::NDS];  // query fragments of this lane's row: v (dK), k (dV)
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s) {
+      const uint32_t off = qq * Cf::ROWB + (((4 * s + g) ^ fst(qq)) & (Cf::NCH - 1)) * 16u;
+      fv[s] = lds_load<u32x4>(tv, off);
+      fk[s] = lds_load<u32x4>(tk, off);
+    }
+    // dK^T = lam^(r+1) S^T V^T (S^T read plainly), dV^T = lam^(r+1) S K^T (S^T read transposed)
+    f32x4 OK[Cf::DVW], OV[Cf::DVW];
+#pragma unroll
+    for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+      OK[dvi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      OV[dvi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < Cf::NDS; ++s) {
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        const uint32_t row = 16 * (dvb + dvi) + lr;
+        const u32x4 A = lds_load<u32x4>(stl, row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u);
+        OK[dvi] = mfma16x16x32(A, fv[s], OK[dvi]);
+        OV[dvi] = mfma16x16x32(tr_frag<C, D>(stl, 32 * s * Cf::ROWB, lane_tr, xtr, dvb + dvi), fk[s], OV[dvi]);
+      }
+    }
+    {
+      const float f = lpow(lag_chunk ? qq : qq + 1);
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        OK[dvi] *= f;
+        OV[dvi] *= f;
+      }
+    }
+    // decay-masked scores over the causal key pairs: P_K^T = dO V^T, P_V^T = Q K^T;
+    // dK^T += Q^T P_K^T, dV^T += dO^T P_V^T
+#pragma unroll
+    for (int p = 0; p < (Cf::NQT + 1) / 2; ++p) {
+      if (p > qt / 2) break;
+      f32x4 PK[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 PV[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < Cf::NDS; ++s) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t row = 32 * p + pair_key(t, lr);
+          const uint32_t off = row * Cf::ROWB + (((4 * s + g) ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
+          PK[t] = mfma16x16x32(lds_load<u32x4>(to, off), fv[s], PK[t]);
+          PV[t] = mfma16x16x32(lds_load<u32x4>(tq, off), fk[s], PV[t]);
+        }
+      }
+      // lam^(qq-j) for key j = 32p + 8g + 4t + i, zero for j > qq
+      const int nb0 = qq - 32 * p - 8 * g;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = nb0 - 4 * t - i;
+          const float f = n < 0 ? 0.f : lpow(n);
+          PK[t][i] *= f;
+          PV[t][i] *= f;
+        }
+      const u32x4 BK = u32x4{pack_bf16x2(PK[0][0], PK[0][1]), pack_bf16x2(PK[0][2], PK[0][3]),
+                             pack_bf16x2(PK[1][0], PK[1][1]), pack_bf16x2(PK[1][2], PK[1][3])};
+      const u32x4 BV = u32x4{pack_bf16x2(PV[0][0], PV[0][1]), pack_bf16x2(PV[0][2], PV[0][3]),
+                             pack_bf16x2(PV[1][0], PV[1][1]), pack_bf16x2(PV[1][2], PV[1][3])};
+#pragma unroll
+      for (int dvi = 0; dvi < Cf::DVW; ++dvi) {
+        OK[dvi] = mfma16x16x32(tr_frag<C, D>(tq, 32 * p * Cf::ROWB, lane_tr, xtr, dvb + dvi), BK, OK[dvi]);
+        OV[dvi] = mfma16x16x32(tr_frag<C, D>(to, 32 * p * Cf::ROWB, lane_tr, xtr, dvb + dvi), BV, OV[dvi]);
+      }
+    }
+    // S = lam^m S + (diag(lam^(m-1-j)) dO)^T Q on this wave's 2 x NJ tiles
+    // (rows past m are zero, so their clamped weight does not matter)
+    {
+      const float f = lpow(lag_chunk ? m - 1 : m);
+#pragma unroll
+      for (int a = 0; a < Cf::SDV; ++a) Sacc[a] *= f;
+#pragma unroll
+      for (int ks = 0; ks < Cf::NKS; ++ks) {
+        float wt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wt[e] = lpow(max(m - 1 - (32 * ks + 8 * g + e), 0));
+        u32x4 A[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          A[i] = tr_frag<C, D>(to, 32 * ks * Cf::ROWB, lane_tr, xtr, sdk + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            A[i][e] = pack_bf16x2(bf16lo(A[i][e]) * wt[2 * e], bf16hi(A[i][e]) * wt[2 * e + 1]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const u32x4 B = tr_frag<C, D>(tq, 32 * ks * Cf::ROWB, lane_tr, xtr, sdv + j);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) Sacc[NJ * i + j] = mfma16x16x32(A[i], B, Sacc[NJ * i + j]);
+        }
+      }
+    }
+    store_rows(dk, c0, m, OK);
+    store_rows(dv, c0, m, OV);
+    lag_chunk = false;
+  };
+
+  load_chunk(buf0, t_begin);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the entry state and the first chunk are in
+  for (int c0 = t_begin; c0 < t_end; c0 += 2 * C) {
+    step(buf0, buf1, c0);
+    if (c0 + C >= t_end) break;
+    step(buf1, buf0, c0 + C);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the empty successor's loads have landed
+
+  if (state_out && seg == nseg - 1) {  // dS_in = lam S^T
+    float *so = state_out + (size_t)bh * D * D;
+#pragma unroll
+    for (int a = 0; a < Cf::SDV; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        so[(size_t)(16 * (sdv + a % NJ) + lr) * D + 16 * (sdk + a / NJ) + 4 * g + i] = Sacc[a][i] * lam;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 // The bf16 path's segment plan in fp32 on the VALU, with tiles of FT tokens:
 // lin_f32_pass<D, false> forms the aggregate of every segment but the last,
@@ -1344,12 +1617,25 @@ SegPlan seg_plan_f32(int BH, int N) {
   return p;
 }
 
-template <int C, int D, bool REV>
-hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+// The segments' entry states of the bf16 path: with one segment the caller's
+// initial state; otherwise the aggregate pass and the scan (or, with
+// reuse_states_T, the states a previous pass left in the workspace).
+struct SegStates {
+  SegPlan pl;
+  const float *seg_state;
+  size_t seg_stride;
+  int sin_T;
+};
+NbK nb_args(const LinearPrefillArgs &a) {
   NbK nb{nullptr, nullptr, 0.f, 0.f, 0, nullptr};
   if (a.nb)
     nb = NbK{a.nb->gamma_q, a.nb->gamma_k, a.nb->eps, a.nb->rope_base, a.nb->pos0,
              static_cast<const uint16_t *>(a.nb->gate)};
+  return nb;
+}
+template <int C, int D, bool REV>
+SegStates seg_states_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+  const NbK nb = nb_args(a);
   const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
   const bool k_transformed = nb.gk != nullptr || nb.rope_base > 0.f;
   const int BH = a.B * a.H;
@@ -1380,6 +1666,20 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
     seg_stride = DD * pl.nparts;  // S_in(m) sits in part slot 0 of segment m
     sin_T = 0;  // the scan wrote the segment states in the plain layout
   }
+  return SegStates{pl, seg_state, seg_stride, sin_T};
+}
+
+template <int C, int D, bool REV>
+hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
+  const NbK nb = nb_args(a);
+  const LinDir dir{a.rev, a.lag, a.state_T, a.scale_final};
+  const bool k_transformed = nb.gk != nullptr || nb.rope_base > 0.f;
+  const int BH = a.B * a.H;
+  const SegStates ss = seg_states_bf16<C, D, REV>(a, st);
+  const int seg_len = ss.pl.seg_len, nseg = ss.pl.nseg;
+  const float *seg_state = ss.seg_state;
+  const size_t seg_stride = ss.seg_stride;
+  const int sin_T = ss.sin_T;
   if constexpr (dma_fits<C, D>()) {
     if (!k_transformed && nb.gq == nullptr) {  // nothing to apply to q or k as they are staged
       auto kern = nb.gate ? lin_seg_output_dma<C, D, REV, true> : lin_seg_output_dma<C, D, REV, false>;
@@ -1455,6 +1755,16 @@ hipError_t launch_linear_prefill_backward(const LinearBackwardArgs &a, hipStream
   pk.rev = 1;
   pk.lag = 1;
   pk.state_T = 1;
+  if (a.dtype == 1 && a.chunk == 64 && a.d == 128) {
+    // dK and dV in one reversed pass from the dK pass's segment states
+    using Cf = LinCfg<64, 128>;
+    const SegStates ss = seg_states_bf16<64, 128, true>(pk, st);
+    hipLaunchKernelGGL((lin_seg_grad_kv<64, 128>), dim3(a.B * a.H * ss.pl.nseg), dim3(Cf::NT), 0, st,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (const uint16_t *)a.dout, (uint16_t *)a.dk, (uint16_t *)a.dv, a.decay, ss.seg_state,
+                       ss.seg_stride, a.dstate_in, a.H, a.N, ss.pl.seg_len, ss.pl.nseg, 1, ss.sin_T);
+    return hipGetLastError();
+  }
   e = launch_linear_prefill(pk, st);
   if (e != hipSuccess) return e;
   LinearPrefillArgs pv{a.dtype, a.B, a.H, a.N, a.d, a.chunk, a.k, a.q, a.dout, a.dv, a.decay, a.dstate_out,

@@ -36,6 +36,8 @@ LIN_BWD_CASES = [
     (1, 2, 600, 64, 128, I.BF16, False, True),      # d 64
     (1, 3, 333, 64, 64, I.BF16, False, False),
     (2, 2, 100, 128, 128, I.BF16, True, True),      # one segment, one partial chunk
+    (2, 3, 1000, 128, 64, I.BF16, True, True),      # chunk 64, d 128: dK and dV in one pass, ragged tail
+    (2, 2, 100, 128, 64, I.BF16, True, True),       # the same pass over one partial chunk
     (1, 4, 2048, 64, 64, I.F32, True, True),        # the tiny workload's linear shape
     (1, 2, 517, 128, 128, I.F32, False, True),
 ]
@@ -65,12 +67,15 @@ def test_linear_prefill_backward(case):
     assert_close(dsi, r[3], torch.float32 if dt == I.F32 else I.BF16, "dstate_in")
 
 
-def test_linear_backward_segments():
-    """Gradients over 8525 tokens (two segments of 34 chunks, each aggregated in
-    parts of 32 + 2 chunks) with lam 0.99 (part 0 weighted 0.99^256 in the scan)
-    and 0.9 (part 0 left out), an initial state and a state gradient: every
-    element against the oracle's chunked backward."""
-    B, H, N, d, C = 1, 2, 8525, 128, 128
+@pytest.mark.parametrize("C", [128, 64])
+def test_linear_backward_segments(C):
+    """Gradients over 8525 tokens (chunk 128: two segments of 34 chunks, each
+    aggregated in parts of 32 + 2 chunks; chunk 64, where dK and dV come from
+    one pass: four segments of 34 chunks) with lam 0.99 (part 0 weighted
+    0.99^256 in the scan at chunk 128) and 0.9 (part 0 left out), an initial
+    state and a state gradient: every element against the oracle's chunked
+    backward."""
+    B, H, N, d = 1, 2, 8525, 128
     say("linear_prefill_backward segments", B, H, N, d, C)
     std = 1.0 / math.sqrt(d)
     x = I.linear_inputs(B, H, N, d, I.BF16, 116, 5, std)
@@ -109,18 +114,19 @@ def test_linear_backward_full_size_heads():
         assert_close(dsi[0, h], r[3], I.BF16, f"dstate_in head {h}")
 
 
-def test_linear_backward_256K_heads():
+@pytest.mark.parametrize("C", [128, 64])
+def test_linear_backward_256K_heads(C):
     """The linear layer at the group's 262144 tokens (32 heads, 8 segments of
-    32768 tokens per head aggregated in parts of 4096, the aggregate passes
-    leaving out keys below 2^-126 and whole parts before them):
-    every row of the fastest- and the slowest-decaying head against the
-    oracle's chunked backward."""
+    32768 tokens per head aggregated in parts, the aggregate passes leaving out
+    keys below 2^-126 and whole parts before them; at chunk 64 dK and dV come
+    from one pass): every row of the fastest- and the slowest-decaying head
+    against the oracle's chunked backward."""
     N = 262144
-    say("linear_prefill_backward 256K")
+    say("linear_prefill_backward 256K chunk", C)
     x = I.workload2_linear(0, "cuda", N=N)
     do = I.normal((1, 32, N, 128), 115, 1.0 / math.sqrt(128), I.BF16, "cuda")
     dec = x["decay"]
-    dq, dk, dv, dsi = sala.linear_prefill_backward(x["q"], x["k"], x["v"], do, dec.cuda())
+    dq, dk, dv, dsi = sala.linear_prefill_backward(x["q"], x["k"], x["v"], do, dec.cuda(), chunk=C)
     torch.cuda.synchronize()
     for h in (0, 31):
         r = BW.linear_attention_backward_chunked(host64(x["q"][0, h]), host64(x["k"][0, h]), host64(x["v"][0, h]),
