@@ -535,7 +535,14 @@ def bench_backward(torch, sala, I, x, sp, idx, reps=3):
                                                dv=grads[2], want_dstate=False, workspace=ws)
     lin()
     ms_lin = events_ms(torch, lin, reps)
-    del grads, ws
+    # the same gradients in 64-token chunks, where dK and dV come from one pass
+    ws64 = torch.empty(max(1, sala.workspace_bytes("linear_prefill", dtype=1, B=B, H=H, N=N, d=d, chunk=64)),
+                       dtype=torch.uint8, device="cuda")
+    lin64 = lambda: sala.linear_prefill_backward(q, k, v, do, x["decay"], dq=grads[0], dk=grads[1],  # noqa: E731
+                                                 dv=grads[2], want_dstate=False, workspace=ws64, chunk=64)
+    lin64()
+    ms_lin64 = events_ms(torch, lin64, reps)
+    del grads, ws, ws64
     sq, sk, sv = sp["q"], sp["k"], sp["v"]
     Hq, Hkv = sq.shape[1], sk.shape[1]
     sdo = I.normal(sq.shape, 5000, 1.0 / math.sqrt(d), I.BF16, "cuda")
@@ -550,13 +557,16 @@ def bench_backward(torch, sala, I, x, sp, idx, reps=3):
     sp_flops = sparse_flops(idx, N, d, Hq // Hkv) * 10.0 / 4.0  # forward's 4 d per pair -> 10 d
     del sdo, sdq, sdk, sdv, sws, do
     torch.cuda.empty_cache()
-    return {"workload": "gradients at the group shapes, N=%d: one linear layer (H=32, d=128, slope decay) and the "
-                        "sparse layer at its forward selection (Hq=32, Hkv=2, 67 blocks)" % N,
+    return {"workload": "gradients at the group shapes, N=%d: one linear layer (H=32, d=128, slope decay; chunk 128 as "
+                        "in the forward, and chunk 64, where dK and dV come from one pass) and the sparse layer at "
+                        "its forward selection (Hq=32, Hkv=2, 67 blocks)" % N,
             "linear_layer_ms": round(ms_lin, 3),
             "linear_roofline": {"bound": "hbm", "achieved": round(lin_bytes / (ms_lin * 1e-3) / 1e9, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(lin_bytes / (ms_lin * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
                                 "algorithmic_bytes": lin_bytes},
+            "linear_layer_chunk64_ms": round(ms_lin64, 3),
+            "linear_chunk64_hbm_frac": round(lin_bytes / (ms_lin64 * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
             "sparse_layer_ms": round(ms_sp, 3),
             "sparse_roofline": {"bound": "mfma", "achieved": round(sp_flops / (ms_sp * 1e-3) / 1e12, 1),
                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -41,7 +41,9 @@
 // the (K, Q, dO) pass.  So every kernel below takes the switches of LinDir.
 // The (K, Q, dO) pass's segment states, sums of Q dO^T, are the transposes of
 // the (V, dO, Q) pass's sums of dO Q^T, so it reads those instead of running
-// its own aggregate and scan.
+// its own aggregate and scan.  Where four double-buffered tiles fit the LDS
+// (chunk 64, d = 128), lin_seg_grad_kv computes dK and dV in one reversed
+// pass from that one state.
 
 #include "sala_common.hpp"
 #include "sala_launch.hpp"
