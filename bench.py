@@ -532,7 +532,7 @@ def bench_backward(torch, sala, I, x, sp, idx, reps=3):
     ws = torch.empty(max(1, sala.workspace_bytes("linear_prefill", dtype=1, B=B, H=H, N=N, d=d, chunk=128)),
                      dtype=torch.uint8, device="cuda")
     lin = lambda: sala.linear_prefill_backward(q, k, v, do, x["decay"], dq=grads[0], dk=grads[1],  # noqa: E731
-                                               dv=grads[2], want_dstate=False, workspace=ws)
+                                               dv=grads[2], want_dstate=False, workspace=ws, chunk=128)
     lin()
     ms_lin = events_ms(torch, lin, reps)
     # the same gradients in 64-token chunks, where dK and dV come from one pass

@@ -187,14 +187,16 @@ def linear_prefill(q, k, v, decay=None, state=None, *, chunk=None, out=None, sta
 def linear_prefill_backward(q, k, v, dout, decay=None, state=None, dstate_out=None, *, chunk=None, dq=None, dk=None,
                             dv=None, want_dstate=True, workspace=None):
     """Gradients of linear_prefill(q, k, v, decay, state) for dL/do = dout [B, H, N, d] and
-    dL/dS_out = dstate_out ([B, H, d, d] fp32 or None).  Returns (dq, dk, dv, dstate_in or None)."""
+    dL/dS_out = dstate_out ([B, H, d, d] fp32 or None).  Returns (dq, dk, dv, dstate_in or None).
+    chunk: the tile of the chunked form (64 or 128; the gradients do not depend on it beyond
+    rounding); 64 by default, where dK and dV come from one pass at d = 128."""
     B, H, N, d = _check_linear(q, k, v, decay, state, None, None)
     _want(dout, "dout", q.shape, q.dtype)
     _want(dstate_out, "dstate_out", (B, H, d, d), torch.float32)
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _want(t, name, q.shape, q.dtype)
     _dev(q, k, v, dout, decay, state, dstate_out, dq, dk, dv, workspace)
-    chunk = chunk or (64 if d == 64 else 128)
+    chunk = chunk or 64
     dt = _code(q)
     dq = _empty_like(q) if dq is None else dq
     dk = _empty_like(q) if dk is None else dk
