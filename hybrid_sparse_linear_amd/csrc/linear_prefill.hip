@@ -269,6 +269,9 @@ struct LinF {
   static constexpr uint32_t TRV = GAM + 2 * D * 4;
   static constexpr uint32_t TRF = TRV + (D / 2) * 8;
   static constexpr uint32_t LDS = TRF + (D / 2) * 4;
+  // the tables (gamma_q | gamma_k, theta_i / 2pi in fp64 and fp32) as one
+  // block of TAB bytes; the helpers below take a pointer to its start
+  static constexpr uint32_t TAB = LDS - GAM, TRV_R = TRV - GAM, TRF_R = TRF - GAM;
 };
 
 // xr: buffer resource over one head's [N, D] rows (REV: row N-1-t holds token t)
@@ -311,22 +314,22 @@ __device__ __forceinline__ void store_rows_f(char *dst, int tid, int m, const u3
 }
 // theta_i / 2pi for i < D/2 (fp64 and fp32) and the norm weights into LDS.
 template <int C, int D>
-__device__ __forceinline__ void nb_tables(char *lds, int tid, const NbK &nb) {
+__device__ __forceinline__ void nb_tables(char *tab, int tid, const NbK &nb) {
   using F = LinF<C, D>;
-  float *gam = reinterpret_cast<float *>(lds + F::GAM);
+  float *gam = reinterpret_cast<float *>(tab);
   if (tid < D) gam[tid] = nb.gq ? nb.gq[tid] : 1.f;
   else if (tid < 2 * D) gam[tid] = nb.gk ? nb.gk[tid - D] : 1.f;
   if (tid < D / 2 && nb.rope_base > 0.f) {
     const double t = pow((double)nb.rope_base, -2.0 * tid / D) * 0.15915494309189535;  // / 2pi
-    reinterpret_cast<double *>(lds + F::TRV)[tid] = t;
-    reinterpret_cast<float *>(lds + F::TRF)[tid] = (float)t;
+    reinterpret_cast<double *>(tab + F::TRV_R)[tid] = t;
+    reinterpret_cast<float *>(tab + F::TRF_R)[tid] = (float)t;
   }
 }
 // Fraction of a turn of p0 * theta_i / 2pi for this thread's features (fp64).
 template <int C, int D>
-__device__ __forceinline__ void rope_base_turns(const char *lds, int hc, long long p0, float (&b)[8]) {
+__device__ __forceinline__ void rope_base_turns(const char *tab, int hc, long long p0, float (&b)[8]) {
   using F = LinF<C, D>;
-  const double *trv = reinterpret_cast<const double *>(lds + F::TRV);
+  const double *trv = reinterpret_cast<const double *>(tab + F::TRV_R);
   const double p = (double)p0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -338,9 +341,9 @@ __device__ __forceinline__ void rope_base_turns(const char *lds, int hc, long lo
 // cos / sin of the angles of this thread's features at chunk row `row`:
 // turns = base turns of the chunk (fp64-reduced) + row * theta_i / 2pi.
 template <int C, int D>
-__device__ __forceinline__ void rope_cs(const char *lds, int hc, int row, const float (&b)[8], float (&c)[8],
+__device__ __forceinline__ void rope_cs(const char *tab, int hc, int row, const float (&b)[8], float (&c)[8],
                                         float (&sn)[8]) {
-  const float *trf = reinterpret_cast<const float *>(lds + LinF<C, D>::TRF);
+  const float *trf = reinterpret_cast<const float *>(tab + LinF<C, D>::TRF_R);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float turns = fmaf((float)row, trf[8 * hc + e], b[e]);
@@ -349,7 +352,7 @@ __device__ __forceinline__ void rope_cs(const char *lds, int hc, int row, const 
   }
 }
 template <int C, int D>
-__device__ __forceinline__ void nb_row(const char *lds, int hc, bool norm, int which, float eps, bool rope,
+__device__ __forceinline__ void nb_row(const char *tab, int hc, bool norm, int which, float eps, bool rope,
                                        const float (&c)[8], const float (&sn)[8], u32x4 &lo, u32x4 &hi) {
   using F = LinF<C, D>;
   if (!norm && !rope) return;  // rows pass through unchanged
@@ -367,7 +370,7 @@ __device__ __forceinline__ void nb_row(const char *lds, int hc, bool norm, int w
     for (int e = 0; e < 8; ++e) ss = fmaf(z[e], z[e], fmaf(a[e], a[e], ss));
     ss = lane_group_sum<F::HC>(ss);
     const float r = rsqrtf(fmaf(ss, 1.f / D, eps));
-    const char *gam = lds + F::GAM + which * D * 4;
+    const char *gam = tab + which * D * 4;
     const f32x4 ga0 = lds_load<f32x4>(gam, 32u * hc), ga1 = lds_load<f32x4>(gam, 32u * hc + 16u);
     const f32x4 gz0 = lds_load<f32x4>(gam, (D / 2 + 8u * hc) * 4u), gz1 = lds_load<f32x4>(gam, (D / 2 + 8u * hc) * 4u + 16u);
 #pragma unroll
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
   float *rw = reinterpret_cast<float *>(lds + Cf::RW);
   const int sdk = (w * Cf::SDV) / Cf::ND, sdv0 = (w * Cf::SDV) % Cf::ND;
   const uint32_t lane_tr = tr_lane_off(l, Cf::ROWB), xtr = tr_lane_xor(l);
-  if constexpr (F) nb_tables<C, D>(lds, tid, nb);
+  if constexpr (F) nb_tables<C, D>(lds + Fz::GAM, tid, nb);
   int h_tab = -1;  // head whose lam^n is in pw
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     int lo = 0, hi = npairs - 1;  // the pair j with pre[j] <= item < pre[j + 1]
@@ -510,12 +513,12 @@ __global__ __launch_bounds__(512) void lin_seg_aggregate(const uint16_t *__restr
         const int m = min(C, t_end - c0);
         __syncthreads();
         float bt[8], cs[8], sn[8];
-        if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
+        if (rope) rope_base_turns<C, D>(lds + Fz::GAM, hc, nb.pos0 + c0, bt);
 #pragma unroll
         for (int u = 0; u < Fz::NSF; ++u) {
           const int row = tid / Fz::HC + Fz::RPF * u;
-          if (rope) rope_cs<C, D>(lds, hc, row, bt, cs, sn);
-          nb_row<C, D>(lds, hc, norm, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
+          if (rope) rope_cs<C, D>(lds + Fz::GAM, hc, row, bt, cs, sn);
+          nb_row<C, D>(lds + Fz::GAM, hc, norm, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
           __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
         }
         store_rows_f<C, D>(lds + Cf::KN, tid, m, xk);
@@ -697,7 +700,7 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto qr = buf_rsrc(qb, head_bytes), kr = buf_rsrc(kb, head_bytes), vr = buf_rsrc(vb, head_bytes);
   const auto gr = buf_rsrc(nb.gate ? nb.gate + head_off : qb, head_bytes);
-  nb_tables<C, D>(lds, tid, nb);
+  nb_tables<C, D>(lds + Fz::GAM, tid, nb);
   const bool norm_q = nb.gq != nullptr, norm_k = nb.gk != nullptr, rope = nb.rope_base > 0.f;
   load_rows_f<C, D, REV>(kr, tid, t_begin, t_end, xk, N);
   load_rows_f<C, D, REV>(vr, tid, t_begin, t_end, xv, N);
@@ -708,13 +711,13 @@ __global__ __launch_bounds__(512) void lin_seg_output(const uint16_t *__restrict
     __syncthreads();
     {
       float bt[8], cs[8], sn[8];
-      if (rope) rope_base_turns<C, D>(lds, hc, nb.pos0 + c0, bt);
+      if (rope) rope_base_turns<C, D>(lds + Fz::GAM, hc, nb.pos0 + c0, bt);
 #pragma unroll
       for (int u = 0; u < Fz::NSF; ++u) {
         const int row = tid / Fz::HC + Fz::RPF * u;
-        if (rope) rope_cs<C, D>(lds, hc, row, bt, cs, sn);
-        nb_row<C, D>(lds, hc, norm_q, 0, nb.eps, rope, cs, sn, xq[u][0], xq[u][1]);
-        nb_row<C, D>(lds, hc, norm_k, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
+        if (rope) rope_cs<C, D>(lds + Fz::GAM, hc, row, bt, cs, sn);
+        nb_row<C, D>(lds + Fz::GAM, hc, norm_q, 0, nb.eps, rope, cs, sn, xq[u][0], xq[u][1]);
+        nb_row<C, D>(lds + Fz::GAM, hc, norm_k, 1, nb.eps, rope, cs, sn, xk[u][0], xk[u][1]);
         __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
       }
       store_rows_f<C, D>(lds + Fz::QN, tid, m, xq);
@@ -851,7 +854,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 // GATE: the output is gated (a compile-time switch: the gate loads' registers
 // would otherwise be waited on before every reuse in the ungated form).
-template <int C, int D, bool REV, bool GATE>
+// NBT: q and k are normalised and rotated (NbK) once their rows have landed,
+// in place in LDS, each thread taking the two 16-byte pieces of a row that
+// hold rotate-half partners (as the staged form does in registers).
+template <int C, int D, bool REV, bool GATE, bool NBT>
 __global__ __launch_bounds__(512) void lin_seg_output_dma(const uint16_t *__restrict__ q,
                                                           const uint16_t *__restrict__ k,
                                                           const uint16_t *__restrict__ v,
@@ -859,15 +865,17 @@ __global__ __launch_bounds__(512) void lin_seg_output_dma(const uint16_t *__rest
                                                           const float *__restrict__ decay,
                                                           const float *__restrict__ seg_state, size_t seg_stride,
                                                           float *__restrict__ state_out, int H, int N, int seg_len,
-                                                          int nseg, const uint16_t *__restrict__ gate, LinDir dir,
-                                                          int sin_T) {
+                                                          int nseg, NbK nb, LinDir dir, int sin_T) {
   using Cf = LinCfg<C, D>;
   using Dm = LinDma<C, D>;
+  using Fz = LinF<C, D>;
+  const uint16_t *gate = nb.gate;
   // two chunk buffers (k | v | q) and the S^T copy: separate arrays, so the
   // compiler sees that direct loads into one buffer do not touch the others
   __shared__ __attribute__((aligned(16))) char buf0[3 * Dm::TILE], buf1[3 * Dm::TILE];
   __shared__ __attribute__((aligned(16))) char stl[D * Cf::ROWB];
   __shared__ __attribute__((aligned(16))) float tab[Cf::PWZ + C + 4 + C];
+  __shared__ __attribute__((aligned(16))) char nbt[NBT ? Fz::TAB : 16];  // norm weights, RoPE frequencies
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
@@ -877,6 +885,7 @@ __global__ __launch_bounds__(512) void lin_seg_output_dma(const uint16_t *__rest
   float *pw = tab + Cf::PWZ;          // pw[n] = lam^n, 0 for n < 0
   float *rw = tab + Cf::PWZ + C + 4;  // lam^(m-1-j) for the chunk's rows, 0 past m
   for (int n = tid - Cf::PWZ; n <= C; n += Cf::NT) pw[n] = n < 0 ? 0.f : (float)pow((double)lam, (double)n);
+  if constexpr (NBT) nb_tables<C, D>(nbt, tid, nb);  // read after the first chunk barrier
   const size_t head_off = (size_t)bh * N * D;
   const uint16_t *qb = q + head_off, *kb = k + head_off, *vb = v + head_off;
   uint16_t *ob = o + head_off;
@@ -939,13 +948,39 @@ __global__ __launch_bounds__(512) void lin_seg_output_dma(const uint16_t *__rest
 
   // One chunk: cur holds its rows (landed by the barrier below); the rows of
   // chunk c0 + C go to nxt.
-  auto step = [&](const char *cur, char *nxt, int c0) __attribute__((always_inline)) {
+  auto step = [&](char *cur, char *nxt, int c0) __attribute__((always_inline)) {
     const int m = min(C, t_end - c0);
     // this wave's direct loads of the chunk have landed (only the previous
     // chunk's output stores, issued after them, may be outstanding); after
     // the barrier every wave's rows are in and the previous chunk is done
     // with nxt, S^T and rw
     lds_barrier<Dm::NST>();
+    if constexpr (NBT) {
+      // q and k rows of the chunk, normalised and rotated in place (rows past
+      // the segment's end are zero and stay zero)
+      const bool norm_q = nb.gq != nullptr, norm_k = nb.gk != nullptr, rope = nb.rope_base > 0.f;
+      const int hc = tid % Fz::HC;
+      float bt[8], cs[8], sn[8];
+      if (rope) rope_base_turns<C, D>(nbt, hc, nb.pos0 + c0, bt);
+#pragma unroll
+      for (int u = 0; u < Fz::NSF; ++u) {
+        const int row = tid / Fz::HC + Fz::RPF * u;
+        if (Fz::RPF * Fz::NSF > C && row >= C) continue;
+        if (rope) rope_cs<C, D>(nbt, hc, row, bt, cs, sn);
+        char *qrow = cur + 2 * Dm::TILE + row * Cf::ROWB;
+        char *krow = cur + row * Cf::ROWB;
+        const uint32_t q0 = ((hc ^ fst(row)) & (Cf::NCH - 1)) * 16u, q1 = (((hc + Fz::HC) ^ fst(row)) & (Cf::NCH - 1)) * 16u;
+        const uint32_t k0 = ((hc ^ fkv(row)) & (Cf::NCH - 1)) * 16u, k1 = (((hc + Fz::HC) ^ fkv(row)) & (Cf::NCH - 1)) * 16u;
+        u32x4 ql = lds_load<u32x4>(qrow, q0), qh = lds_load<u32x4>(qrow, q1);
+        u32x4 kl = lds_load<u32x4>(krow, k0), kh = lds_load<u32x4>(krow, k1);
+        nb_row<C, D>(nbt, hc, norm_q, 0, nb.eps, rope, cs, sn, ql, qh);
+        nb_row<C, D>(nbt, hc, norm_k, 1, nb.eps, rope, cs, sn, kl, kh);
+        lds_store(qrow, q0, ql);
+        lds_store(qrow, q1, qh);
+        lds_store(krow, k0, kl);
+        lds_store(krow, k1, kh);
+      }
+    }
     // gate values of this lane's outputs (a clamped row is never stored),
     // loaded before the next chunk's rows so that waiting for them waits for
     // nothing issued later
@@ -1683,13 +1718,13 @@ hipError_t run_bf16(const LinearPrefillArgs &a, hipStream_t st) {
   const size_t seg_stride = ss.seg_stride;
   const int sin_T = ss.sin_T;
   if constexpr (dma_fits<C, D>()) {
-    if (!k_transformed && nb.gq == nullptr) {  // nothing to apply to q or k as they are staged
-      auto kern = nb.gate ? lin_seg_output_dma<C, D, REV, true> : lin_seg_output_dma<C, D, REV, false>;
-      hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q, (const uint16_t *)a.k,
-                         (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, seg_stride, a.state_out, a.H,
-                         a.N, seg_len, nseg, nb.gate, dir, sin_T);
-      return hipGetLastError();
-    }
+    const bool nbt = k_transformed || nb.gq != nullptr;  // q or k normalised or rotated
+    auto kern = nb.gate ? (nbt ? lin_seg_output_dma<C, D, REV, true, true> : lin_seg_output_dma<C, D, REV, true, false>)
+                        : (nbt ? lin_seg_output_dma<C, D, REV, false, true> : lin_seg_output_dma<C, D, REV, false, false>);
+    hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                       (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, seg_stride, a.state_out, a.H, a.N,
+                       seg_len, nseg, nb, dir, sin_T);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((lin_seg_output<C, D, REV>), dim3(BH * nseg), dim3(512), 0, st, (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.decay, seg_state, seg_stride,

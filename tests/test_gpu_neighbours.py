@@ -144,16 +144,16 @@ def test_fused_linear_decode(dt, d):
     assert_close(state, rs, dt, "state")
 
 
-@pytest.mark.parametrize("N", [32768, 262144], ids=["32K", "256K"])
-def test_fused_linear_full_size_rows(N):
-    say("linear_prefill_fused full", N)
+@pytest.mark.parametrize("N,chunk", [(32768, 128), (262144, 128), (32768, 64)], ids=["32K", "256K", "32K-c64"])
+def test_fused_linear_full_size_rows(N, chunk):
+    say("linear_prefill_fused full", N, chunk)
     x = I.workload2_linear(0, "cuda", N=N, workload=2 if N == 32768 else 4)
     nb = I.neighbour_inputs(1, 32, N, 128, 2 if N == 32768 else 4, 0, "cuda")
-    ws = torch.empty(max(1, sala.workspace_bytes("linear_prefill", dtype=1, B=1, H=32, N=N, d=128, chunk=128)),
+    ws = torch.empty(max(1, sala.workspace_bytes("linear_prefill", dtype=1, B=1, H=32, N=N, d=128, chunk=chunk)),
                      dtype=torch.uint8, device="cuda")
     o, st = sala.linear_prefill_fused(x["q"], x["k"], x["v"], x["decay"].cuda(), gamma_q=nb["gamma_q"],
                                       gamma_k=nb["gamma_k"], eps=1e-6, rope_base=10000.0, gate=nb["gate"],
-                                      workspace=ws)
+                                      workspace=ws, chunk=chunk)
     torch.cuda.synchronize()
     rows = sorted({0, 1, 127, 128, 1000, N // 2, N - 129, N - 1})
     dec = x["decay"].double().numpy()
