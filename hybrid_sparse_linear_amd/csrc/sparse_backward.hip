@@ -29,7 +29,7 @@
 //                    query block i) pairs, then per key block the list of the
 //                    query blocks that selected it in increasing order, cut
 //                    into work items of at most ITEM_QB query blocks.
-//   sparse_bwd_dkv   one workgroup per work item (4 waves, one 16-key tile of
+//   sparse_bwd_dkv   one workgroup per work item (2 waves, two 16-key tiles of
 //                    block j each, K and V rows held as MFMA operands): for
 //                    every (query block, head) of the item, Q and dO rows are
 //                    staged in LDS and S = Q K^T, dP = dO V^T, dV^T += dO^T P,
@@ -490,16 +490,25 @@ __global__ __launch_bounds__(1024) void bwd_order(const int *__restrict__ pairs,
 }
 
 // ------------------------------------------------------------------ dk / dv pass
+// Two waves, each holding two 16-key tiles of block j (keys 32w .. 32w + 31)
+// as MFMA operands, so that every Q or dO fragment read from LDS (plain for S
+// and dP, transposed for dK and dV) feeds two MFMAs: with one tile per wave
+// the staged tiles were read twice as fast as the matrix cores consume them.
+// Two workgroups share a CU (one wave per SIMD), each with its own staged
+// tiles.
+constexpr int DKV_KT = 2;                   // 16-key tiles per wave
+constexpr int DKV_NW = BB / (16 * DKV_KT);  // waves per workgroup
+constexpr int DKV_NT = 64 * DKV_NW;         // threads per workgroup
+
 template <int D>
-__global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                      const uint16_t *__restrict__ v,
-                                                      const uint16_t *__restrict__ dout,
-                                                      const float *__restrict__ lse2, const float *__restrict__ drow,
-                                                      const int *__restrict__ pairs, const int4 *__restrict__ items,
-                                                      const int *__restrict__ nitems, const int *__restrict__ order,
-                                                      float *__restrict__ partial, int Hq, int Hkv, int N,
-                                                      int pairs_per_bkv, int items_per_bkv, float scale) {
+__global__ __launch_bounds__(DKV_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_bwd_dkv(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ dout, const float *__restrict__ lse2, const float *__restrict__ drow,
+    const int *__restrict__ pairs, const int4 *__restrict__ items, const int *__restrict__ nitems,
+    const int *__restrict__ order, float *__restrict__ partial, int Hq, int Hkv, int N, int pairs_per_bkv,
+    int items_per_bkv, float scale) {
   using Cf = BwCfg<D>;
+  constexpr int KT = DKV_KT;
   __shared__ __attribute__((aligned(16))) char qb0[Cf::TB], qb1[Cf::TB];
   __shared__ __attribute__((aligned(16))) char ob0[Cf::TB], ob1[Cf::TB];
   __shared__ __attribute__((aligned(16))) float st0[2][256], st1[2][256];  // lse2, D of the 64 rows (+ pad)
@@ -520,21 +529,26 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
   const int b = bkv / Hkv, kvh = bkv % Hkv, G = Hq / Hkv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const float scale_log2 = scale * 1.4426950408889634f;
-  const int key = BB * j + 16 * w + lr;  // this lane's key (column of S)
+  int key[KT];  // this lane's key (column of S) in each of the wave's tiles
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) key[kt] = BB * j + 16 * (KT * w + kt) + lr;
 
-  // K and V rows of this wave's 16 keys as B operands
-  u32x4 kf[Cf::NDS], vf[Cf::NDS];
-  {
-    const size_t off = ((size_t)bkv * N + key) * D;
+  // K and V rows of this wave's keys as B operands
+  u32x4 kf[KT][Cf::NDS], vf[KT][Cf::NDS];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const size_t off = ((size_t)bkv * N + key[kt]) * D;
 #pragma unroll
     for (int s = 0; s < Cf::NDS; ++s) {
-      kf[s] = key < N ? gload16(k + off + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
-      vf[s] = key < N ? gload16(v + off + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
+      kf[kt][s] = key[kt] < N ? gload16(k + off + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
+      vf[kt][s] = key[kt] < N ? gload16(v + off + 32 * s + 8 * lg) : u32x4{0, 0, 0, 0};
     }
   }
-  f32x4 dK[Cf::ND], dV[Cf::ND];
+  f32x4 dK[KT][Cf::ND], dV[KT][Cf::ND];
 #pragma unroll
-  for (int dt = 0; dt < Cf::ND; ++dt) dK[dt] = dV[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < Cf::ND; ++dt) dK[kt][dt] = dV[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int *plist = pairs + (size_t)bkv * pairs_per_bkv + start;
   const int steps = len * G;  // (query block, head) pairs, query block major
@@ -545,8 +559,8 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
     const int hq = kvh * G + n % G;
     const size_t rb = (size_t)(b * Hq + hq) * N + (size_t)i * BB;
     const int valid = N - i * BB;
-    load_tile<D, 256>(q + rb * D, valid, qd, tid);
-    load_tile<D, 256>(dout + rb * D, valid, od, tid);
+    load_tile<D, DKV_NT>(q + rb * D, valid, qd, tid);
+    load_tile<D, DKV_NT>(dout + rb * D, valid, od, tid);
     if (w == 0) {
       const uint32_t nb = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(BB, valid))) * 4u;  // uniform (see load_tile)
       bload16_lds(buf_rsrc(lse2 + rb, nb), sd[0], 16u * l);
@@ -569,50 +583,65 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
     const bool interior = i > j && (i + 1) * BB <= N && (j + 1) * BB <= N;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {  // query rows 32p .. 32p + 31
-      // S and dP tiles tt = 0, 1: lane holds queries 32p + 8lg + 4tt + e of key `key`
-      f32x4 S[2], dP[2];
+      // S and dP tiles [kt][tt]: lane holds queries 32p + 8lg + 4tt + e of key key[kt]
+      f32x4 S[KT][2], dP[KT][2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) S[tt] = dP[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) S[kt][tt] = dP[kt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < Cf::NDS; ++s)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const uint32_t off = tile_off<D>(32 * p + pair_key(tt, lr), 4 * s + lg);
-          S[tt] = mfma16x16x32(lds_load<u32x4>(qc, off), kf[s], S[tt]);
-          dP[tt] = mfma16x16x32(lds_load<u32x4>(oc, off), vf[s], dP[tt]);
+          const u32x4 qa = lds_load<u32x4>(qc, off), oa = lds_load<u32x4>(oc, off);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            S[kt][tt] = mfma16x16x32(qa, kf[kt][s], S[kt][tt]);
+            dP[kt][tt] = mfma16x16x32(oa, vf[kt][s], dP[kt][tt]);
+          }
         }
       const f32x4 ls0 = lds_load<f32x4>(sc[0], (32 * p + 8 * lg) * 4), ls1 = lds_load<f32x4>(sc[0], (32 * p + 8 * lg + 4) * 4);
       const f32x4 dr0 = lds_load<f32x4>(sc[1], (32 * p + 8 * lg) * 4), dr1 = lds_load<f32x4>(sc[1], (32 * p + 8 * lg + 4) * 4);
-      float pr[2][4], ds[2][4];
-      if (interior) {  // every (query, key) pair of the step is live: no masks
+      u32x4 Pf[KT], Sf[KT];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+      for (int kt = 0; kt < KT; ++kt) {
+        float pr[2][4], ds[2][4];
+        if (interior) {  // every (query, key) pair of the step is live: no masks
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
-            pr[tt][e] = __builtin_amdgcn_exp2f(S[tt][e] * scale_log2 - lsev);
-            ds[tt][e] = pr[tt][e] * (dP[tt][e] - drv) * scale;
-          }
-      } else {
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+            for (int e = 0; e < 4; ++e) {
+              const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
+              pr[tt][e] = __builtin_amdgcn_exp2f(S[kt][tt][e] * scale_log2 - lsev);
+              ds[tt][e] = pr[tt][e] * (dP[kt][tt][e] - drv) * scale;
+            }
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int qrow = BB * i + 32 * p + 8 * lg + 4 * tt + e;  // the query's token
-            const bool live = qrow < N && key < N && key <= qrow;
-            const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
-            pr[tt][e] = live ? __builtin_amdgcn_exp2f(S[tt][e] * scale_log2 - lsev) : 0.f;
-            ds[tt][e] = pr[tt][e] * (dP[tt][e] - drv) * scale;
-          }
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int qrow = BB * i + 32 * p + 8 * lg + 4 * tt + e;  // the query's token
+              const bool live = qrow < N && key[kt] < N && key[kt] <= qrow;
+              const float lsev = tt ? ls1[e] : ls0[e], drv = tt ? dr1[e] : dr0[e];
+              pr[tt][e] = live ? __builtin_amdgcn_exp2f(S[kt][tt][e] * scale_log2 - lsev) : 0.f;
+              ds[tt][e] = pr[tt][e] * (dP[kt][tt][e] - drv) * scale;
+            }
+        }
+        Pf[kt] = u32x4{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                       pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+        Sf[kt] = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
+                       pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
       }
-      const u32x4 Pf = u32x4{pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
-                             pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
-      const u32x4 Sf = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
-                             pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
 #pragma unroll
       for (int dt = 0; dt < Cf::ND; ++dt) {
-        dV[dt] = mfma16x16x32(tr_frag(oc, 32 * p * Cf::ROWB, tr_off, tr_xor, dt, Cf::NCH, Cf::ROWB), Pf, dV[dt]);
-        dK[dt] = mfma16x16x32(tr_frag(qc, 32 * p * Cf::ROWB, tr_off, tr_xor, dt, Cf::NCH, Cf::ROWB), Sf, dK[dt]);
+        const u32x4 ot = tr_frag(oc, 32 * p * Cf::ROWB, tr_off, tr_xor, dt, Cf::NCH, Cf::ROWB);
+        const u32x4 qt = tr_frag(qc, 32 * p * Cf::ROWB, tr_off, tr_xor, dt, Cf::NCH, Cf::ROWB);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          dV[kt][dt] = mfma16x16x32(ot, Pf[kt], dV[kt][dt]);
+          dK[kt][dt] = mfma16x16x32(qt, Sf[kt], dK[kt][dt]);
+        }
       }
     }
     __syncthreads();  // every wave is done with this step's buffers before they are reloaded
@@ -620,11 +649,14 @@ __global__ __launch_bounds__(256) void sparse_bwd_dkv(const uint16_t *__restrict
   // this item's sums: partial[item][0 = dK, 1 = dV][key row][feature]
   float *pk = partial + ((size_t)bkv * items_per_bkv + r) * 2 * BB * D;
   float *pv = pk + BB * D;
-  const int kr = 16 * w + lr;
 #pragma unroll
-  for (int dt = 0; dt < Cf::ND; ++dt) {
-    *reinterpret_cast<f32x4 *>(pk + (size_t)kr * D + 16 * dt + 4 * lg) = dK[dt];
-    *reinterpret_cast<f32x4 *>(pv + (size_t)kr * D + 16 * dt + 4 * lg) = dV[dt];
+  for (int kt = 0; kt < KT; ++kt) {
+    const int kr = 16 * (KT * w + kt) + lr;
+#pragma unroll
+    for (int dt = 0; dt < Cf::ND; ++dt) {
+      *reinterpret_cast<f32x4 *>(pk + (size_t)kr * D + 16 * dt + 4 * lg) = dK[kt][dt];
+      *reinterpret_cast<f32x4 *>(pv + (size_t)kr * D + 16 * dt + 4 * lg) = dV[kt][dt];
+    }
   }
 }
 
@@ -715,7 +747,7 @@ hipError_t run_bwd(const SparseBackwardArgs &a, hipStream_t st) {
   while (((NQB - 1) >> shift) >= 8192) ++shift;  // at most 8192 buckets of first query blocks
   hipLaunchKernelGGL(bwd_order, dim3(BKV), dim3(1024), 0, st, pairs, items, nitems, order, L.pairs_per_bkv,
                      L.items_per_bkv, shift);
-  hipLaunchKernelGGL((sparse_bwd_dkv<D>), dim3(BKV * ((L.items_per_bkv + 63) & ~63)), dim3(256), 0, st,
+  hipLaunchKernelGGL((sparse_bwd_dkv<D>), dim3(BKV * ((L.items_per_bkv + 63) & ~63)), dim3(DKV_NT), 0, st,
                      (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const uint16_t *)a.dout,
                      lse, drow, pairs, items, nitems, order, partial, a.Hq, a.Hkv, a.N, L.pairs_per_bkv,
                      L.items_per_bkv, a.scale);
