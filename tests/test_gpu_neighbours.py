@@ -43,6 +43,7 @@ NB_CASES = [
     (1, 2, 700, 128, 128, 0, False, False, False, True, True),        # gate only
     (1, 3, 1500, 128, 64, 0, False, False, False, True, True),        # gate only, chunk 64 (direct-load output pass)
     (1, 2, 900, 64, 128, 0, False, False, False, True, False),        # gate only, d 64 (direct-load output pass)
+    (1, 2, 700, 64, 128, 55, True, True, True, True, True),          # d 64, chunk 128, all (direct-load, norm + RoPE in LDS)
 ]
 
 
