@@ -88,7 +88,12 @@ __device__ __forceinline__ void load_tile(const uint16_t *base, int valid_rows, 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ------------------------------------------------------------------ dq pass
-template <int D>
+// FOLD (scale > 0): scores stay unscaled and scale * log2(e) is folded into the
+// fma that subtracts each reference, and the factor `scale` of dS into the
+// log-sum-exp (P scale = 2^(s - (lse - log2 scale))), two VALU operations
+// fewer per score in the second sweep and one in the first.  A scale of zero
+// or below keeps the scaled scores, whose masked entries are -inf.
+template <int D, bool FOLD>
 __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                      const uint16_t *__restrict__ v,
                                                      const uint16_t *__restrict__ dout,
@@ -174,9 +179,9 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
   const uint32_t tr_off = tr_lane_off(l, Cf::ROWB), tr_xor = tr_lane_xor(l);
 
   // S^T for keys 32p .. 32p+31 of one block: tile [tt][a] holds keys
-  // 32p + 8lg + 4tt + e (e = 0..3) of row r0 + 16a + lr, in log2 units; masked
-  // keys (after the row in the diagonal block, or at or past N) are -inf.
-  // Each K fragment feeds both row tiles.
+  // 32p + 8lg + 4tt + e (e = 0..3) of row r0 + 16a + lr, unscaled with FOLD,
+  // else in log2 units; masked keys (after the row in the diagonal block, or
+  // at or past N) are -inf.  Each K fragment feeds both row tiles.
   auto scores = [&](const char *kbuf, int j, bool diag, int p, f32x4 (&S)[2][2]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -190,12 +195,7 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
 #pragma unroll
         for (int a = 0; a < 2; ++a) S[tt][a] = mfma16x16x32(A, qf[a][s], S[tt][a]);
       }
-    if (!diag && (j + 1) * BB <= N) {  // no key of the block is masked
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) S[tt][a] *= scale_log2;
-    } else {
+    if (diag || (j + 1) * BB > N) {  // some key of the block is masked
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -204,8 +204,13 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
           for (int e = 0; e < 4; ++e) {
             const int key = 32 * p + 8 * lg + 4 * tt + e;
             const bool masked = (diag && key > r0 + 16 * a + lr) || (BB * j + key >= N);
-            S[tt][a][e] = masked ? -INFINITY : S[tt][a][e] * scale_log2;
+            S[tt][a][e] = masked ? -INFINITY : (FOLD ? S[tt][a][e] : S[tt][a][e] * scale_log2);
           }
+    } else if constexpr (!FOLD) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) S[tt][a] *= scale_log2;
     }
   };
 
@@ -266,7 +271,8 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
 #pragma unroll
           for (int ee = 0; ee < 4; ++ee) mx = fmaxf(mx, S[p][tt][a][ee]);
       mx = row4_max(mx);
-      const float mn = fmaxf(m[a], mx);
+      // FOLD: the scale is positive, so the max of the scaled scores is the scaled max
+      const float mn = fmaxf(m[a], FOLD ? mx * scale_log2 : mx);
       float ps = 0.f, pd = 0.f;
 #pragma unroll
       for (int p = 0; p < 2; ++p)
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int ee = 0; ee < 4; ++ee) {
-            const float pe = __builtin_amdgcn_exp2f(S[p][tt][a][ee] - mn);
+            const float pe = __builtin_amdgcn_exp2f(FOLD ? fmaf(S[p][tt][a][ee], scale_log2, -mn) : S[p][tt][a][ee] - mn);
             ps += pe;
             pd = fmaf(pe, dP[p][tt][a][ee], pd);
           }
@@ -294,6 +300,13 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
   }
 
   // sweep 2, per 32-key half p: dQ^T += K^T dS^T with dS = P (dP - D) scale
+  // (FOLD: P scale = 2^(s - (lse - log2 scale)) in one exponential)
+  float lse2s[2];
+  {
+    const float l2s = FOLD ? log2f(scale) : 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) lse2s[a] = lse2[a] - l2s;
+  }
   f32x4 dQ[2][Cf::ND];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -313,8 +326,13 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int ee = 0; ee < 4; ++ee) {
-            const float pr = __builtin_amdgcn_exp2f(S[tt][a][ee] - lse2[a]);
-            ds[tt][ee] = pr * (dP[tt][a][ee] - drow[a]) * scale;
+            if constexpr (FOLD) {
+              const float prs = __builtin_amdgcn_exp2f(fmaf(S[tt][a][ee], scale_log2, -lse2s[a]));
+              ds[tt][ee] = prs * (dP[tt][a][ee] - drow[a]);
+            } else {
+              const float pr = __builtin_amdgcn_exp2f(S[tt][a][ee] - lse2[a]);
+              ds[tt][ee] = pr * (dP[tt][a][ee] - drow[a]) * scale;
+            }
           }
         dS[a] = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
                       pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
@@ -732,7 +750,8 @@ hipError_t run_bwd(const SparseBackwardArgs &a, hipStream_t st) {
   const int HG = (G + 3) / 4;
   const int ntasks = BKV * NQB;
   const int grid_dq = ((ntasks + 7) / 8) * 8 * HG;
-  hipLaunchKernelGGL((sparse_bwd_dq<D>), dim3(grid_dq), dim3(512), 0, st, (const uint16_t *)a.q,
+  hipLaunchKernelGGL((a.scale > 0.f ? sparse_bwd_dq<D, true> : sparse_bwd_dq<D, false>), dim3(grid_dq), dim3(512), 0, st,
+                     (const uint16_t *)a.q,
                      (const uint16_t *)a.k, (const uint16_t *)a.v, (const uint16_t *)a.dout,
                      a.idx, (uint16_t *)a.dq, lse, drow, a.Hq, a.Hkv, a.N, NQB, a.n_sel, HG, ntasks, a.scale);
   const size_t nbits = (size_t)BKV * NQB * L.WPR;
