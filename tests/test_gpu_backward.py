@@ -175,6 +175,25 @@ def test_sparse_prefill_backward(case):
     assert_close(dv, r[2], I.BF16, "dv", absolute_floor=False)
 
 
+@pytest.mark.parametrize("scale", [-0.06, 0.0, 0.2], ids=["negative", "zero", "positive"])
+def test_sparse_backward_custom_scale(scale):
+    """A scale other than 1/sqrt(d): above zero the dQ pass folds the scale into
+    its exponent arguments; zero and below take the scaled form (masked scores
+    stay -inf); both against the oracle's gradients at that scale."""
+    case = (1, 8, 2, 64 * 6 + 21, 128, 3)
+    say("sparse_prefill_backward scale", scale, case)
+    x, do, ridx = _sparse_bwd_case(case, 123)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    idx = dev(torch.from_numpy(ridx).to(torch.int32))
+    dq, dk, dv = sala.sparse_prefill_backward(q, k, v, idx, dev(do), scale=scale)
+    torch.cuda.synchronize()
+    r = BW.sparse_attention_backward(host64(x["q"]), host64(x["k"]), host64(x["v"]), ridx, host64(do), 64,
+                                     scale=scale)
+    assert_close(dq, r[0], I.BF16, "dq")
+    assert_close(dk, r[1], I.BF16, "dk", absolute_floor=False)
+    assert_close(dv, r[2], I.BF16, "dv", absolute_floor=False)
+
+
 def test_sparse_backward_repeats_bit_for_bit():
     """Every sum of the backward runs in a fixed order: two calls give the same bits."""
     case = (1, 16, 2, 64 * 30 + 9, 128, 6)
