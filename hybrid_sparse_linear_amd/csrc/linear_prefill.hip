@@ -25,6 +25,11 @@
 //           with bf16 MFMA 16x16x32 and fp32 accumulation; the fp32 master S
 //           stays in registers, a bf16 copy of S^T in LDS feeds the Q S product.
 //           The last segment writes S_out.
+//           Where two chunk buffers of k | v | q fit the LDS (chunk 64 at
+//           d = 128, every chunk at d = 64), lin_seg_output_dma takes this
+//           pass: the rows go from HBM straight into LDS (direct loads, the
+//           next chunk in flight during the current one), and the fused
+//           form's q/k norm and RoPE are applied to them there, in place.
 // fp32 path: the same three passes on the VALU in fp32 over tiles of 32
 // tokens (lin_f32_pass, lin_seg_scan).
 //
