@@ -251,8 +251,11 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
     }
   };
 
-  // sweep 1, online over the blocks, per row tile a: the row max m, lsum =
-  // sum 2^(s - m) and dsum = sum 2^(s - m) dP_s, both rescaled when m moves
+  // sweep 1, online over the blocks, per row tile a: the reference m and this
+  // lane's parts of lsum = sum 2^(s - m) and dsum = sum 2^(s - m) dP_s.  As in
+  // the forward kernel, m moves (to the row max, rescaling the parts) only
+  // when a score of the wave lies more than 8 above its row's m, so a term is
+  // at most 2^8; the four lanes of a row are added once, after the sweep.
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, dsum[2] = {0.f, 0.f};
   sweep([&](const char *kcur, const char *vcur, int j, bool diag) {
     f32x4 S[2][2][2], dP[2][2][2];  // [p][tt][a]
@@ -270,26 +273,32 @@ __global__ __launch_bounds__(512) void sparse_bwd_dq(const uint16_t *__restrict_
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int ee = 0; ee < 4; ++ee) mx = fmaxf(mx, S[p][tt][a][ee]);
-      mx = row4_max(mx);
       // FOLD: the scale is positive, so the max of the scaled scores is the scaled max
-      const float mn = fmaxf(m[a], FOLD ? mx * scale_log2 : mx);
-      float ps = 0.f, pd = 0.f;
+      if (FOLD) mx *= scale_log2;
+      if (__any(mx > m[a] + 8.f)) {
+        const float mn = fmaxf(m[a], row4_max(mx));
+        const float alpha = mn == m[a] ? 1.f : __builtin_amdgcn_exp2f(m[a] - mn);
+        lsum[a] *= alpha;
+        dsum[a] *= alpha;
+        m[a] = mn;
+      }
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int ee = 0; ee < 4; ++ee) {
-            const float pe = __builtin_amdgcn_exp2f(FOLD ? fmaf(S[p][tt][a][ee], scale_log2, -mn) : S[p][tt][a][ee] - mn);
-            ps += pe;
-            pd = fmaf(pe, dP[p][tt][a][ee], pd);
+            const float pe = __builtin_amdgcn_exp2f(FOLD ? fmaf(S[p][tt][a][ee], scale_log2, -m[a]) : S[p][tt][a][ee] - m[a]);
+            lsum[a] += pe;
+            dsum[a] = fmaf(pe, dP[p][tt][a][ee], dsum[a]);
           }
-      const float alpha = __builtin_amdgcn_exp2f(m[a] - mn);
-      lsum[a] = lsum[a] * alpha + row4_sum(ps);
-      dsum[a] = dsum[a] * alpha + row4_sum(pd);
-      m[a] = mn;
     }
   });
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    lsum[a] = row4_sum(lsum[a]);
+    dsum[a] = row4_sum(dsum[a]);
+  }
   // log2 of the row's sum of 2^s, and D_t; a row with no key (a list without
   // its own block) gets +inf, so its P is 0 (the forward gives it a zero output)
   float lse2[2], drow[2];
