@@ -589,13 +589,22 @@ __global__ __launch_bounds__(256) void lin_seg_scan(float *__restrict__ seg_stat
   for (int m = 0; m < nseg; ++m) {
     float a = 0.f;
     if (m + 1 < nseg) {
+      // parts before p_first were left out by the aggregate pass (its test)
       const int seg_end = (m + 1) * seg_len, first = agg_first_row(lam_f, m * seg_len, seg_end, C);
+      const int p_first = (first - m * seg_len) / part_len;
       double wgt = 1.0;
-      for (int p = nparts - 1; p >= 0; --p) {
-        const int p_end = m * seg_len + min(seg_len, (p + 1) * part_len);
-        if (first >= p_end) break;  // this part and all before it were left out by the aggregate pass
-        a = fmaf((float)wgt, base[((size_t)m * nparts + p) * DD], a);
-        wgt *= (p == nparts - 1) ? lam_last : lam_part;
+      // eight parts' loads in flight at once, summed in the same order
+      for (int p0 = nparts - 1; p0 >= p_first; p0 -= 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p0 - u >= p_first ? base[((size_t)m * nparts + p0 - u) * DD] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = p0 - u;
+          if (p < p_first) break;
+          a = fmaf((float)wgt, v[u], a);
+          wgt *= (p == nparts - 1) ? lam_last : lam_part;
+        }
       }
     }
     base[(size_t)m * nparts * DD] = s;
